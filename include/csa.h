@@ -1,0 +1,211 @@
+/*
+ * csa.h -- C ABI of the CSA / HCA hybrid long-context attention library
+ * (libcsa.so, gfx950).
+ *
+ * The operators follow the DeepSeek-V4 pages:
+ *   - CSA: compress every m = 4 tokens' KV into one entry, score entries with
+ *     the Lightning Indexer, keep the top-k, attend to those (llm-tech
+ *     overview, "Compressed Sparse Attention"; kenelite analysis 5.1-5.3).
+ *   - HCA: compress every m' = 128 tokens, attend densely (llm-tech overview,
+ *     "Heavily Compressed Attention"; kenelite analysis section 6).
+ *   - both add a 128-token sliding window of raw tokens and a per-head
+ *     attention-sink logit (llm-tech overview, HCA section and "other
+ *     architecture details"; kenelite analysis section 7).
+ *   - KV rows keep RoPE dims in BF16 and the rest in FP8; the indexer runs in
+ *     FP8 or MXFP4 (llm-tech overview, "other architecture details" and
+ *     "FP4 Quantization-Aware Training"; kenelite analysis 8.2, 8.3).
+ * Where the pages leave an operator open the library fixes it as stated at
+ * each entry point.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless said otherwise; the caller owns all
+ *     memory.  The library allocates nothing, keeps no state between calls
+ *     and only enqueues work on `stream` (no synchronisation, no host copies).
+ *   - Arguments are validated on the host before anything is enqueued.  An
+ *     invalid call returns CSA_EINVAL / CSA_EUNSUPPORTED / CSA_EWORKSPACE and
+ *     writes nothing; a failed launch returns CSA_EHIP.  csa_last_error()
+ *     gives a message for the last failure on the calling thread.
+ *   - Results are deterministic: fixed reduction orders, no float atomics.
+ *   - Positions: a prefill query row t has position t.  A query at position
+ *     t sees compressed entry j iff (j+1)*m - 1 <= t, i.e. the first
+ *     n_t = min(n_entries, floor((t+1)/m)) entries, and the window positions
+ *     max(0, t-W+1) .. t.
+ */
+#ifndef CSA_H
+#define CSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  CSA_OK = 0,
+  CSA_EINVAL = 1,        /* bad argument (null, size, alignment, range)        */
+  CSA_EUNSUPPORTED = 2,  /* valid but not implemented (format / shape combo)   */
+  CSA_EWORKSPACE = 3,    /* workspace missing or too small                     */
+  CSA_EHIP = 4           /* a HIP call or kernel launch failed                 */
+} csa_status;
+
+typedef enum {
+  CSA_F32 = 0,           /* IEEE binary32                                     */
+  CSA_BF16 = 1,          /* bfloat16                                          */
+  CSA_FP8_E4M3 = 2,      /* OCP E4M3FN, per-row power-of-two fp32 scale        */
+  CSA_MXFP4 = 3          /* OCP MX: E2M1 elements, one E8M0 per 32 elements    */
+} csa_fmt;
+
+/*
+ * An entry store: rows of `dim` values for each of B batch elements.
+ * Row r of batch element b starts at rows + (b*cap + r) * row_bytes.
+ *   fmt CSA_F32      : dim float32; scales NULL; row_bytes = 4*dim.
+ *   fmt CSA_FP8_E4M3 : dims [0, dim-rope_dim) as E4M3 codes of x/s, then
+ *                      rope_dim BF16; s = scales[b*cap + r] (float32, a power
+ *                      of two, the smallest with max|x| <= 448 s);
+ *                      row_bytes = (dim - rope_dim) + 2*rope_dim.
+ *   fmt CSA_MXFP4    : dim/2 bytes, element 2i in the low nibble of byte i;
+ *                      scales = uint8 E8M0 [B][cap][dim/32]; rope_dim 0;
+ *                      row_bytes = dim/2.
+ * rows must be 16-byte aligned and row_bytes a multiple of 16 (4 for MXFP4
+ * rows of 32 values).
+ */
+typedef struct {
+  void* rows;
+  void* scales;
+  int64_t cap;
+  int32_t dim;
+  int32_t rope_dim;
+  int32_t fmt;
+  int32_t row_bytes;
+} csa_store;
+
+/* flags of the attention entry points */
+#define CSA_ATTN_PARTIAL 1  /* attend to the compressed entries only: no window,
+                               no sink; `out` is float32, normalised over those
+                               entries, lse = ln sum_e exp(l_e) (-inf if none)  */
+#define CSA_WIN_RING 2      /* the window store is a ring of W slots per batch
+                               element; position p lives in slot p mod W      */
+
+const char* csa_version(void);
+const char* csa_status_string(int status);
+const char* csa_last_error(void);   /* host string, per calling thread */
+
+/*
+ * csa_compress_kv -- learned block compression (kenelite analysis 5.2: each
+ * token's contribution weight is learned, not average pooling; section 6 for
+ * m' = 128), then quantisation into `out`.
+ *
+ * tok: [B] x [T][dim] token K/V (or indexer keys / queries), element type
+ *   tok_fmt (CSA_F32 or CSA_BF16), batch element b at tok + b*tok_bstride
+ *   elements, rows contiguous.
+ * For block j < floor(T/m) (an incomplete tail block is not compressed):
+ *   a_i = <x_{jm+i}, gate> + bias_i (i < m), alpha = softmax(a),
+ *   c_j = sum_i alpha_i x_{jm+i}  (float32),
+ * stored as row out_row0 + j of `out` in out.fmt.  m = 1 stores the tokens
+ * themselves (alpha = 1 exactly): the raw-token window store and the
+ * quantisation of indexer queries.
+ * gate: [dim] float32; bias: [m] float32.  1 <= m <= 1024; dim in
+ * {32, 64, 128, 256, 512}; MXFP4 output needs dim in {32, 64}.
+ * Writes floor(T/m) rows per batch element; out_row0 + floor(T/m) <= out.cap.
+ */
+csa_status csa_compress_kv(const void* tok, int tok_fmt, int B, int64_t T, int64_t tok_bstride,
+                           int m, const float* gate, const float* bias,
+                           csa_store out, int64_t out_row0, hipStream_t stream);
+
+/*
+ * csa_indexer_topk -- Lightning Indexer scores and top-k selection
+ * (llm-tech overview, CSA section: the indexer picks the top-k compressed
+ * entries; kenelite analysis 5.3: top-512 Flash, top-1024 Pro).
+ *
+ * For query row q of batch element b at position t (q_pos[b*Tq + q], or
+ * t = q when q_pos is NULL) and every visible entry j < n_t:
+ *   I(t, j) = sum_h w[b][q][h] * ReLU(<qI[b][q][h], K[b][j]>)   (float32)
+ * sel[b][q][0..k) receives the min(k, n_t) entries of largest I, ties to the
+ * smaller j, in ascending j, padded with -1.
+ *
+ * q_idx: store of indexer queries, row (q*H_I + h) of batch element b, dim
+ *   d_I, same format as `keys` (CSA_F32, CSA_FP8_E4M3 with rope_dim 0, or
+ *   CSA_MXFP4).  head_w: float32 [B][Tq][H_I].  keys: the compressed indexer
+ *   key store (dim d_I), first n_entries rows valid.
+ * Limits: d_I in {32, 64}; 1 <= H_I <= 16; 1 <= k <= 2048;
+ *   n_entries * k <= 32768 * 32768.
+ * ws: device workspace of at least csa_indexer_topk_workspace(...) bytes
+ *   (may be 0 bytes, then ws may be NULL).
+ */
+size_t csa_indexer_topk_workspace(int B, int Tq, int64_t n_entries, int k);
+csa_status csa_indexer_topk(csa_store q_idx, const float* head_w, csa_store keys,
+                            int64_t n_entries, const int64_t* q_pos, int B, int Tq, int H_I,
+                            int m, int k, int32_t* sel, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
+
+/*
+ * csa_sparse_attn_prefill -- CSA core attention for T prefill queries
+ * (kenelite analysis 5.1 "top-k compressed blocks -> core attention",
+ * section 7 sliding window; llm-tech overview, attention sink).
+ *
+ * q: [B][T][H][dim] in q_fmt (CSA_F32 or CSA_BF16).  For query t, head h:
+ *   entries E_t = {ckv[b][j] : j in sel[b][t][0..k), 0 <= j < n_entries}
+ *               + {win[b][u] : max(0, t-W+1) <= u <= t}   (win has >= T rows),
+ *   l_e = sm_scale * <q_{t,h}, e>,  M = max(sink_h, max_e l_e),
+ *   o = sum_e exp(l_e - M) e / (exp(sink_h - M) + sum_e exp(l_e - M)),
+ *   lse = M + ln(denominator).  K = V = the stored entry (all dim dims).
+ * sink: float32 [H] or NULL (= -inf).  out: [B][T][H][dim] in q_fmt (float32
+ * with CSA_ATTN_PARTIAL).  lse: float32 [B][T][H] or NULL.
+ * Indices outside [0, n_entries) in sel are skipped.
+ */
+csa_status csa_sparse_attn_prefill(const void* q, int q_fmt, int B, int T, int H,
+                                   csa_store ckv, int64_t n_entries, const int32_t* sel, int k,
+                                   csa_store win, int W, const float* sink, float sm_scale,
+                                   void* out, float* lse, int flags, hipStream_t stream);
+
+/* Workspace bytes of csa_sparse_attn_decode / hca_attn for these sizes. */
+size_t csa_attn_workspace(int B, int Tq, int H, int dim, int64_t max_list);
+
+/*
+ * csa_sparse_attn_decode -- CSA attention for one new token per sequence.
+ * q: [B][H][dim]; sel: [B][k]; ring: window ring of W slots (position p in
+ * slot p mod W) holding positions pos-W+1 .. pos; pos: int64 [B] (device).
+ * Same arithmetic as the prefill.  ws: optional; NULL runs each sequence in
+ * one workgroup per head group, otherwise >= csa_attn_workspace(B, 1, H,
+ * dim, k + W) bytes (CSA_EWORKSPACE if smaller) lets long lists be split
+ * across workgroups and merged in a fixed order.
+ */
+csa_status csa_sparse_attn_decode(const void* q, int q_fmt, int B, int H, csa_store ckv,
+                                  int64_t n_entries, const int32_t* sel, int k, csa_store ring,
+                                  const int64_t* pos, int W, const float* sink, float sm_scale,
+                                  void* out, float* lse, int flags, void* ws, size_t ws_bytes,
+                                  hipStream_t stream);
+
+/*
+ * hca_attn -- HCA dense attention (kenelite analysis section 6; model-card
+ * notes: heavier compression with dense attention) over every visible entry
+ * j < n_t = min(n_entries, floor((t+1)/m_prime)) plus the window and sink.
+ * q: [B][Tq][H][dim].  q_pos: int64 [B][Tq] or NULL (prefill, t = row).
+ * win: position-indexed raw rows, or a ring with CSA_WIN_RING.
+ * ws: optional, as for csa_sparse_attn_decode, sized by
+ * csa_attn_workspace(B, Tq, H, dim, n_entries + W) (0 for calls with enough
+ * queries to fill the GPU).
+ */
+csa_status hca_attn(const void* q, int q_fmt, int B, int Tq, int H, csa_store hkv, int m_prime,
+                    int64_t n_entries, const int64_t* q_pos, csa_store win, int W,
+                    const float* sink, float sm_scale, void* out, float* lse, int flags,
+                    void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * swa_merge -- sliding-window attention merged with a partial result
+ * (o_p, lse_p) of CSA_ATTN_PARTIAL, with the sink in the denominator:
+ *   o = (e^{lse_p} o_p + sum_w e^{l_w} v_w) / (e^{lse_p} + sum_w e^{l_w} + e^{sink}).
+ * part_out: float32 [B][Tq][H][dim]; part_lse: float32 [B][Tq][H].
+ * q_pos / win / flags as in hca_attn (CSA_WIN_RING only).  out: q_fmt.
+ */
+csa_status swa_merge(const void* q, int q_fmt, int B, int Tq, int H, csa_store win,
+                     const int64_t* q_pos, int W, int flags, const float* part_out,
+                     const float* part_lse, const float* sink, float sm_scale, void* out,
+                     hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA_H */

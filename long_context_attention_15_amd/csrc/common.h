@@ -1,0 +1,134 @@
+// Device-side helpers shared by the gfx950 kernels: storage codecs, row views
+// and wavefront reductions.  Formats: OCP E4M3FN (FP8), BF16, OCP MX E2M1 +
+// E8M0 (MXFP4); encoders round to nearest-even and saturate.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/csa.h"
+
+namespace csa {
+
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------ store view
+struct Store {
+  const uint8_t* rows;
+  const void* scales;
+  int64_t cap;
+  int dim, rope, fmt, row_bytes;
+};
+
+struct StoreW {
+  uint8_t* rows;
+  void* scales;
+  int64_t cap;
+  int dim, rope, fmt, row_bytes;
+};
+
+inline Store view(const csa_store& s) {
+  return Store{(const uint8_t*)s.rows, s.scales, s.cap, s.dim, s.rope_dim, s.fmt, s.row_bytes};
+}
+inline StoreW wview(const csa_store& s) {
+  return StoreW{(uint8_t*)s.rows, s.scales, s.cap, s.dim, s.rope_dim, s.fmt, s.row_bytes};
+}
+
+// ------------------------------------------------------------------ BF16
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// -------------------------------------------------------------- FP8 E4M3FN
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+  return (c & 0x80u) ? -v : v;
+}
+
+// Round-to-nearest-even E4M3FN code of x, saturating at 448; sign kept.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t s = (u >> 24) & 0x80u;
+  const uint32_t au = u & 0x7fffffffu;
+  if (au > 0x7f800000u) return 0x7fu;                    // NaN
+  const float a = __uint_as_float(au);
+  if (a >= 448.0f) return s | 0x7eu;
+  if (a < 0.015625f) {                                   // below 2^-6: spacing 2^-9
+    return s | (uint32_t)rintf(a * 512.0f);              // 8 -> code 0x08 = 2^-6
+  }
+  uint32_t r = (au + 0x7ffffu + ((au >> 20) & 1u)) >> 20;  // keep 3 mantissa bits, RNE
+  uint32_t code = r - (120u << 3);
+  return s | (code > 0x7eu ? 0x7eu : code);
+}
+
+// Smallest power of two s = 2^e with amax <= 448 s; e clamped to [-126, 127];
+// amax == 0 gives 1.
+__device__ __forceinline__ float fp8_row_scale(float amax) {
+  if (!(amax > 0.0f)) return 1.0f;
+  int a = ilogbf(amax);
+  int e = (amax <= ldexpf(448.0f, a - 8)) ? a - 8 : a - 7;
+  e = e < -126 ? -126 : (e > 127 ? 127 : e);
+  return ldexpf(1.0f, e);
+}
+
+// ---------------------------------------------------------------- E2M1
+__device__ __forceinline__ float e2m1_to_f32(uint32_t c) {
+  const uint32_t mag = c & 7u;
+  float v = mag < 4u ? 0.5f * (float)mag : (mag == 4u ? 2.0f : (mag == 5u ? 3.0f : (mag == 6u ? 4.0f : 6.0f)));
+  return (c & 8u) ? -v : v;
+}
+
+__device__ __forceinline__ uint32_t f32_to_e2m1(float x) {
+  const uint32_t s = (__float_as_uint(x) >> 28) & 8u;
+  const float a = fabsf(x);
+  float q2;  // twice the rounded magnitude
+  if (a < 2.0f) q2 = rintf(a * 2.0f);
+  else if (a < 4.0f) q2 = 2.0f * rintf(a);
+  else q2 = 4.0f * rintf(a * 0.5f);
+  q2 = fminf(q2, 12.0f);
+  uint32_t qi = (uint32_t)q2;
+  uint32_t mag = qi <= 4u ? qi : (qi == 6u ? 5u : (qi == 8u ? 6u : 7u));
+  return s | mag;
+}
+
+// OCP MX shared exponent of a block: floor(log2 amax) - 2, clamped to
+// [-127, 127]; an all-zero block gets -127.
+__device__ __forceinline__ int mx_block_exp(float amax) {
+  if (!(amax > 0.0f)) return -127;
+  int e = ilogbf(amax) - 2;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// ------------------------------------------------------- wave reductions
+template <int W = kWave>
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, W);
+  return v;
+}
+template <int W = kWave>
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = W / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, W));
+  return v;
+}
+
+// Order-preserving uint32 key of a float score; larger key = larger score.
+// -0 is folded into +0 first.  Every finite score maps to a key >= 0x00800000,
+// so 0 is free to mark "no entry".
+__device__ __forceinline__ uint32_t score_key(float s) {
+  if (s == 0.0f) s = 0.0f;
+  const uint32_t u = __float_as_uint(s);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_score(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+}  // namespace csa

@@ -1,0 +1,198 @@
+// Block compression + quantisation (csa_compress_kv).
+//
+// One wavefront per output entry.  Lane l owns VPL contiguous dims
+// [l*VPL, l*VPL + VPL), so a row of 512 bf16 is one 16-byte load per lane.
+// Pass 1 computes the m logits <x_i, gate> + bias_i (wave reductions), the
+// softmax weights are formed in LDS, pass 2 accumulates sum_i alpha_i x_i in
+// fixed order (the rows of pass 1 are still in L2), then the row is quantised
+// and written.  HBM traffic: the tokens once plus the stored rows.
+#include "common.h"
+#include "launch.h"
+
+namespace csa {
+
+constexpr int kCompressWaves = 4;
+constexpr int kMaxM = 1024;
+
+template <typename TIn, int VPL>
+__device__ __forceinline__ void load_vals(const TIn* p, float (&v)[VPL]);
+
+template <>
+__device__ __forceinline__ void load_vals<float, 1>(const float* p, float (&v)[1]) { v[0] = *p; }
+template <>
+__device__ __forceinline__ void load_vals<float, 2>(const float* p, float (&v)[2]) {
+  float2 t = *(const float2*)p; v[0] = t.x; v[1] = t.y;
+}
+template <>
+__device__ __forceinline__ void load_vals<float, 4>(const float* p, float (&v)[4]) {
+  float4 t = *(const float4*)p; v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+}
+template <>
+__device__ __forceinline__ void load_vals<float, 8>(const float* p, float (&v)[8]) {
+  float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+template <>
+__device__ __forceinline__ void load_vals<uint16_t, 1>(const uint16_t* p, float (&v)[1]) {
+  v[0] = bf16_to_f32(*p);
+}
+template <>
+__device__ __forceinline__ void load_vals<uint16_t, 2>(const uint16_t* p, float (&v)[2]) {
+  uint32_t t = *(const uint32_t*)p; v[0] = bf16_to_f32(t & 0xffffu); v[1] = bf16_to_f32(t >> 16);
+}
+template <>
+__device__ __forceinline__ void load_vals<uint16_t, 4>(const uint16_t* p, float (&v)[4]) {
+  uint2 t = *(const uint2*)p;
+  v[0] = bf16_to_f32(t.x & 0xffffu); v[1] = bf16_to_f32(t.x >> 16);
+  v[2] = bf16_to_f32(t.y & 0xffffu); v[3] = bf16_to_f32(t.y >> 16);
+}
+template <>
+__device__ __forceinline__ void load_vals<uint16_t, 8>(const uint16_t* p, float (&v)[8]) {
+  uint4 t = *(const uint4*)p;
+  const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { v[2 * i] = bf16_to_f32(w[i] & 0xffffu); v[2 * i + 1] = bf16_to_f32(w[i] >> 16); }
+}
+
+template <typename TIn, int VPL>
+__global__ __launch_bounds__(kWave * kCompressWaves) void compress_kernel(
+    const TIn* __restrict__ tok, int B, int64_t T, int64_t bstride, int m,
+    const float* __restrict__ gate, const float* __restrict__ bias, StoreW out, int64_t row0,
+    int64_t N) {
+  __shared__ float s_alpha[kCompressWaves][kMaxM];
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  int64_t e = (int64_t)blockIdx.x * kCompressWaves + wave;
+  // waves past the end idle through the block barriers below
+  const bool valid = e < (int64_t)B * N;
+  if (!valid) e = 0;
+  const int b = (int)(e / N);
+  const int64_t j = e % N;
+  const int D = out.dim;
+  const bool active = valid && lane * VPL < D;
+  const TIn* base = tok + (int64_t)b * bstride + j * m * (int64_t)D + lane * VPL;
+  float* alpha = s_alpha[wave];
+
+  float g[VPL];
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) g[v] = active ? gate[lane * VPL + v] : 0.0f;
+
+  // pass 1: logits
+  for (int i = 0; i < m; ++i) {
+    float x[VPL];
+    float p = 0.0f;
+    if (active) {
+      load_vals<TIn, VPL>(base + (int64_t)i * D, x);
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) p = fmaf(x[v], g[v], p);
+    }
+    p = wave_sum(p);
+    if (lane == 0) alpha[i] = p + bias[i];
+  }
+  __syncthreads();
+  float mx = -INFINITY;
+  for (int i = lane; i < m; i += kWave) mx = fmaxf(mx, alpha[i]);
+  mx = wave_max(mx);
+  float sum = 0.0f;
+  for (int i = lane; i < m; i += kWave) {
+    float ev = expf(alpha[i] - mx);
+    alpha[i] = ev;
+    sum += ev;
+  }
+  sum = wave_sum(sum);
+  __syncthreads();
+  for (int i = lane; i < m; i += kWave) alpha[i] = alpha[i] / sum;
+  __syncthreads();
+
+  // pass 2: weighted sum, fixed order over the block
+  float acc[VPL];
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) acc[v] = 0.0f;
+  if (active) {
+    // the sum starts from the first term (not from +0), so m = 1 stores x
+    // itself, signed zeros included
+    float x0[VPL];
+    load_vals<TIn, VPL>(base, x0);
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) acc[v] = alpha[0] * x0[v];
+    for (int i = 1; i < m; ++i) {
+      float x[VPL];
+      load_vals<TIn, VPL>(base + (int64_t)i * D, x);
+      const float a = alpha[i];
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) acc[v] = fmaf(a, x[v], acc[v]);
+    }
+  }
+
+  if (!valid) return;
+  // quantise + store
+  const int64_t row = (int64_t)b * out.cap + row0 + j;
+  uint8_t* dst = out.rows + row * out.row_bytes;
+  if (out.fmt == CSA_F32) {
+    if (active) {
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) ((float*)dst)[lane * VPL + v] = acc[v];
+    }
+  } else if (out.fmt == CSA_FP8_E4M3) {
+    const int nb = D - out.rope;          // bulk dims
+    const bool bulk = active && lane * VPL < nb;
+    float am = 0.0f;
+    if (bulk) {
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) am = fmaxf(am, fabsf(acc[v]));
+    }
+    am = wave_max(am);
+    const float s = fp8_row_scale(am);
+    const int es = ilogbf(s);
+    if (bulk) {
+      uint8_t c[VPL];
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) c[v] = (uint8_t)f32_to_e4m3(ldexpf(acc[v], -es));
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) dst[lane * VPL + v] = c[v];
+    } else if (active) {
+      uint16_t* r = (uint16_t*)(dst + nb);
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) r[lane * VPL + v - nb] = (uint16_t)f32_to_bf16(acc[v]);
+    }
+    if (lane == 0) ((float*)out.scales)[row] = s;
+  } else {  // CSA_MXFP4, VPL == 1, D in {32, 64}
+    float am = active ? fabsf(acc[0]) : 0.0f;
+    am = wave_max<32>(am);                // lanes 0-31 = block 0, 32-63 = block 1
+    const int E = mx_block_exp(am);
+    uint32_t c = active ? f32_to_e2m1(ldexpf(acc[0], -E)) : 0u;
+    uint32_t hi = __shfl_xor(c, 1);
+    if (active && (lane & 1) == 0) dst[lane >> 1] = (uint8_t)(c | (hi << 4));
+    if (active && (lane & 31) == 0)
+      ((uint8_t*)out.scales)[row * (D / 32) + (lane >> 5)] = (uint8_t)(E + 127);
+  }
+}
+
+template <typename TIn, int VPL>
+static hipError_t launch_compress_t(const void* tok, int B, int64_t T, int64_t bstride, int m,
+                                    const float* gate, const float* bias, const csa_store& out,
+                                    int64_t row0, hipStream_t st) {
+  const int64_t N = T / m;
+  const int64_t items = (int64_t)B * N;
+  if (items == 0) return hipSuccess;
+  const int64_t blocks = (items + kCompressWaves - 1) / kCompressWaves;
+  hipLaunchKernelGGL((compress_kernel<TIn, VPL>), dim3((unsigned)blocks), dim3(kWave * kCompressWaves),
+                     0, st, (const TIn*)tok, B, T, bstride, m, gate, bias, wview(out), row0, N);
+  return hipGetLastError();
+}
+
+hipError_t launch_compress(const void* tok, int tok_fmt, int B, int64_t T, int64_t bstride, int m,
+                           const float* gate, const float* bias, const csa_store& out, int64_t row0,
+                           hipStream_t st) {
+  const int vpl = out.dim >= 64 ? out.dim / 64 : 1;
+#define CSA_CMP(TT, V) return launch_compress_t<TT, V>(tok, B, T, bstride, m, gate, bias, out, row0, st)
+  if (tok_fmt == CSA_F32) {
+    switch (vpl) { case 1: CSA_CMP(float, 1); case 2: CSA_CMP(float, 2); case 4: CSA_CMP(float, 4); default: CSA_CMP(float, 8); }
+  } else {
+    switch (vpl) { case 1: CSA_CMP(uint16_t, 1); case 2: CSA_CMP(uint16_t, 2); case 4: CSA_CMP(uint16_t, 4); default: CSA_CMP(uint16_t, 8); }
+  }
+#undef CSA_CMP
+}
+
+int compress_max_m() { return kMaxM; }
+
+}  // namespace csa

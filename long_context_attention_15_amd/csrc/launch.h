@@ -1,0 +1,47 @@
+// Host-side launchers of the kernels, called by the C-ABI layer (api.hip)
+// after it has validated every argument.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/csa.h"
+
+namespace csa {
+
+hipError_t launch_compress(const void* tok, int tok_fmt, int B, int64_t T, int64_t bstride, int m,
+                           const float* gate, const float* bias, const csa_store& out, int64_t row0,
+                           hipStream_t st);
+int compress_max_m();
+
+// Indexer: chunk size and chunk count chosen for a call; workspace bytes.
+struct IdxPlan {
+  int chunk;      // entries scored per workgroup
+  int nchunk;     // chunks per query
+  size_t ws;      // workspace bytes (0 when nchunk == 1)
+  bool ok;
+};
+IdxPlan indexer_plan(int B, int Tq, int64_t n_entries, int k);
+hipError_t launch_indexer(const csa_store& qidx, const float* head_w, const csa_store& keys,
+                          int64_t n_entries, const int64_t* q_pos, int B, int Tq, int H_I, int m,
+                          int k, int32_t* sel, void* ws, const IdxPlan& plan, hipStream_t st);
+
+// Attention: one launcher for every attention entry point.
+struct AttnCall {
+  const void* q; int q_fmt; int B, Tq, H, D;
+  csa_store ckv; int64_t n_entries; int mode;   // 0: no compressed entries, 1: sel list, 2: range
+  const int32_t* sel; int k; int m;
+  csa_store win; int W; int ring;
+  const int64_t* q_pos;
+  const float* sink; float tau;
+  const float* prior_o; const float* prior_lse;  // swa_merge: partial to merge
+  void* out; float* lse; int partial;
+  void* ws; size_t ws_bytes;
+  int allow_split;                                 // split long lists over workgroups (needs ws)
+};
+enum { kModeNone = 0, kModeSel = 1, kModeRange = 2 };
+size_t attn_workspace(int B, int Tq, int H, int D, int64_t max_list);
+bool attn_supported(int H, int D);
+hipError_t launch_attn(const AttnCall& c, hipStream_t st);
+
+}  // namespace csa

@@ -1,0 +1,129 @@
+"""The C ABI on the CPU: the library loads, exports every symbol the header
+declares, and rejects invalid calls on the host before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import long_context_attention_15_amd as csa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa.h")
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_][a-z_0-9]*)\s*\(", src, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while")))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(csa.LIB_PATH):
+        pytest.skip("libcsa.so not built")
+    return csa.load()
+
+
+def test_header_declares_the_six_operators():
+    names = _declared_functions()
+    for op in ["csa_compress_kv", "csa_indexer_topk", "csa_sparse_attn_prefill", "csa_sparse_attn_decode",
+               "hca_attn", "swa_merge"]:
+        assert op in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    assert set(_declared_functions()) == set(csa.EXPORTS)
+
+
+def test_version_and_status_strings(lib):
+    assert "gfx950" in csa.version()
+    assert lib.csa_status_string(0).decode() == "CSA_OK"
+    assert "workspace" in lib.csa_status_string(3).decode()
+
+
+def _store(ptr=16, cap=8, dim=64, rope=0, fmt=csa.F32, scales=0):
+    return csa._CStore(ptr, scales, cap, dim, rope, fmt, csa.row_bytes(fmt, dim, rope))
+
+
+# Fake but aligned addresses: every call below must fail validation, so the
+# pointers are never dereferenced and no HIP call is made.
+P = 1 << 20
+
+
+def test_compress_rejects_bad_arguments(lib):
+    out = _store(P, 8, 64)
+    # m out of range
+    assert lib.csa_compress_kv(P, csa.F32, 1, 32, 32 * 64, 0, P, P, out, 0, None) == 1
+    assert lib.csa_compress_kv(P, csa.F32, 1, 32, 32 * 64, 4096, P, P, out, 0, None) == 1
+    assert "m = 4096" in lib.csa_last_error().decode()
+    # null gate, unaligned token pointer, unsupported token format
+    assert lib.csa_compress_kv(P, csa.F32, 1, 32, 32 * 64, 4, 0, P, out, 0, None) == 1
+    assert lib.csa_compress_kv(P + 4, csa.F32, 1, 32, 32 * 64, 4, P, P, out, 0, None) == 1
+    assert lib.csa_compress_kv(P, csa.FP8_E4M3, 1, 32, 32 * 64, 4, P, P, out, 0, None) == 2
+    # output rows beyond the store
+    assert lib.csa_compress_kv(P, csa.F32, 1, 64, 64 * 64, 4, P, P, out, 0, None) == 1
+    # bad store: wrong row_bytes, unsupported dim, FP8 without scales
+    bad = _store(P, 8, 64)
+    bad.row_bytes = 100
+    assert lib.csa_compress_kv(P, csa.F32, 1, 32, 32 * 64, 4, P, P, bad, 0, None) == 1
+    assert lib.csa_compress_kv(P, csa.F32, 1, 32, 32 * 48, 4, P, P, _store(P, 8, 48), 0, None) == 2
+    assert lib.csa_compress_kv(P, csa.F32, 1, 32, 32 * 64, 4, P, P, _store(P, 8, 64, 16, csa.FP8_E4M3), 0,
+                               None) == 1
+    # MXFP4 output of 512 dims
+    mx = _store(P, 8, 512, 0, csa.MXFP4, P)
+    assert lib.csa_compress_kv(P, csa.F32, 1, 32, 32 * 512, 4, P, P, mx, 0, None) == 2
+
+
+def test_indexer_rejects_bad_arguments(lib):
+    q = _store(P, 64, 64, 0, csa.FP8_E4M3, P)
+    k = _store(P, 1000, 64, 0, csa.FP8_E4M3, P)
+    ok = dict(n=1000, B=1, Tq=8, H=8, m=4, k=64)
+    call = lambda **kw: lib.csa_indexer_topk(kw.get("q", q), P, kw.get("keys", k), kw.get("n", 1000), 0,
+                                             kw.get("B", 1), kw.get("Tq", 8), kw.get("H", 8), kw.get("m", 4),
+                                             kw.get("k", 64), P, 0, 0, None)
+    assert call(k=0) == 2 and call(k=4096) == 2
+    assert call(H=17) == 2
+    assert call(n=1001) == 1                       # beyond keys.cap
+    assert call(Tq=9) == 1                         # q store too small for Tq * H_I rows
+    assert call(keys=_store(P, 1000, 64, 0, csa.MXFP4, P)) == 2   # mixed formats
+    assert call(m=0) == 1
+    # decode-sized call with many entries needs a workspace
+    big = _store(P, 1 << 18, 64, 0, csa.FP8_E4M3, P)
+    need = lib.csa_indexer_topk_workspace(4, 1, 1 << 18, 1024)
+    assert need > 0
+    assert lib.csa_indexer_topk(q, P, big, 1 << 18, P, 4, 1, 8, 4, 1024, P, 0, 0, None) == 3
+    assert "workspace" in lib.csa_last_error().decode()
+
+
+def test_attention_rejects_bad_arguments(lib):
+    kv = _store(P, 100, 512, 64, csa.FP8_E4M3, P)
+    win = _store(P, 300, 512, 64, csa.FP8_E4M3, P)
+    f32win = _store(P, 300, 512, 0, csa.F32)
+    pre = lambda **kw: lib.csa_sparse_attn_prefill(
+        kw.get("q", P), kw.get("qf", csa.BF16), 1, kw.get("T", 256), kw.get("H", 64), kv, kw.get("n", 100),
+        kw.get("sel", P), kw.get("k", 64), kw.get("win", win), 128, 0, 0.04, P, 0, kw.get("flags", 0), None)
+    assert pre(q=0) == 1
+    assert pre(sel=0) == 1
+    assert pre(qf=csa.FP8_E4M3) == 2
+    assert pre(H=0) == 1
+    assert pre(win=f32win) == 2                       # window and entries must share a format
+    assert pre(T=301) == 1                            # window store shorter than T
+    assert pre(n=101) == 1
+    assert pre(flags=csa.WIN_RING) == 1
+    assert pre(flags=8) == 1
+    # decode: workspace required for few queries
+    ring = _store(P, 128, 512, 64, csa.FP8_E4M3, P)
+    st = lib.csa_sparse_attn_decode(P, csa.BF16, 4, 128, kv, 100, P, 64, ring, P, 128, 0, 0.04, P, 0, 0, P, 16,
+                                    None)
+    assert st == 3                                    # a workspace was given but is too small
+    assert lib.csa_attn_workspace(4, 1, 128, 512, 64 + 128) > 0
+    # hca: ring without positions
+    assert lib.hca_attn(P, csa.BF16, 1, 8, 64, kv, 128, 100, 0, ring, 128, 0, 0.04, P, 0, csa.WIN_RING, 0, 0,
+                        None) == 1
+    # swa_merge: partial flag is not allowed, null partials rejected
+    assert lib.swa_merge(P, csa.BF16, 1, 8, 64, win, 0, 128, csa.ATTN_PARTIAL, P, P, 0, 0.04, P, None) == 1
+    assert lib.swa_merge(P, csa.BF16, 1, 8, 64, win, 0, 128, 0, 0, P, 0, 0.04, P, None) == 1

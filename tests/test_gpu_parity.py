@@ -1,0 +1,364 @@
+"""GPU parity: every entry point of libcsa.so against the oracle, element by
+element, on seeded inputs that span several tiles and ragged tails, plus the
+edge cases (no visible entries, empty window, k above the visible count,
+exact score ties)."""
+import math
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import codec
+from oracle import csa as O
+from tests import helpers as Hx
+
+pytestmark = pytest.mark.gpu
+
+
+def _sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+# ================================================================= compress
+COMPRESS_CASES = [
+    # name, tok fmt, store fmt, D, R, m, T, B
+    ("f32_to_f32_D64_m4", "f32", "f32", 64, 0, 4, 2051, 2),
+    ("bf16_to_fp8_D512_m4", "bf16", "fp8", 512, 64, 4, 1030, 2),
+    ("bf16_to_fp8_D512_m128", "bf16", "fp8", 512, 64, 128, 128 * 9 + 5, 1),
+    ("f32_to_fp8_D64_R16_m4", "f32", "fp8", 64, 16, 4, 999, 2),
+    ("bf16_to_fp8idx_D64_m4", "bf16", "fp8", 64, 0, 4, 4099, 1),
+    ("bf16_to_mxfp4_D64_m4", "bf16", "mxfp4", 64, 0, 4, 2050, 2),
+    ("f32_to_mxfp4_D32_m4", "f32", "mxfp4", 32, 0, 4, 1027, 1),
+    ("f32_to_f32_D32_m7", "f32", "f32", 32, 0, 7, 500, 1),
+]
+
+
+@pytest.mark.parametrize("name,tf,sf,D,R,m,T,B", COMPRESS_CASES)
+def test_compress_parity(lib, name, tf, sf, D, R, m, T, B):
+    x = synth.tensor(0, "kv", (B, T, D), rmsnorm=(tf == "bf16"))
+    g = synth.tensor(0, "gate", (D,), std=0.02)
+    b = synth.tensor(0, "bias", (m,), std=0.02)
+    xd, xv = Hx.act(x, tf)
+    N = T // m
+    out = lib.alloc_store(B, N + 3, D, sf, R, device=Hx.dev())
+    lib.compress_kv(xd, m, Hx.to_dev(g.astype(np.float32)), Hx.to_dev(b.astype(np.float32)), out, out_row0=2)
+    _sync()
+    g32 = g.astype(np.float32).astype(np.float64)
+    b32 = b.astype(np.float32).astype(np.float64)
+    for bi in range(B):
+        rows = out.rows[bi, 2: 2 + N].cpu().numpy()
+        sc = None if out.scales is None else out.scales[bi, 2: 2 + N].cpu().numpy()
+        c = O.compress(xv[bi], g32, b32, m)
+        eps = Hx.compress_error_bound(xv[bi], g32, b32, m)
+        frac = Hx.check_compress(rows, sc, sf, D, R, c, eps)
+        if sf != "f32":   # float32 stores differ in last bits by design; codes must not drift
+            assert frac <= 2e-3, f"{frac:.2e} of codes differ from the oracle's packing"
+
+
+@pytest.mark.parametrize("tf,sf,D,R", [("bf16", "fp8", 512, 64), ("f32", "fp8", 64, 16), ("bf16", "fp8", 64, 0),
+                                       ("bf16", "mxfp4", 64, 0), ("f32", "mxfp4", 32, 0), ("f32", "f32", 64, 0)])
+def test_compress_m1_quantisation_is_bit_exact(lib, tf, sf, D, R):
+    """m = 1 stores the token itself (alpha = 1 exactly), so the stored bytes
+    are the plain quantisation: identical to the oracle codec's."""
+    T = 777
+    x = synth.tensor(0, "kv", (1, T, D), rmsnorm=True) * 3.0
+    x[0, 5] = 0.0                       # an all-zero row
+    x[0, 6, ::3] = -0.0
+    xd, xv = Hx.act(x, tf)
+    out = lib.alloc_store(1, T, D, sf, R, device=Hx.dev())
+    one = Hx.to_dev(np.ones(1, np.float32))
+    lib.compress_kv(xd, 1, Hx.to_dev(np.zeros(D, np.float32)), one, out)
+    _sync()
+    rows, sc = Hx.download_store(out, T)
+    Hx.check_compress(rows[0], None if sc is None else sc[0], sf, D, R, xv[0], None, exact_codes=True)
+
+
+def test_compress_short_input_writes_nothing(lib):
+    import torch
+    x = torch.zeros((1, 3, 64), dtype=torch.bfloat16, device=Hx.dev())
+    out = lib.alloc_store(1, 4, 64, "fp8", 0, device=Hx.dev())
+    out.rows.fill_(0xAB)
+    lib.compress_kv(x, 4, Hx.to_dev(np.zeros(64, np.float32)), Hx.to_dev(np.zeros(4, np.float32)), out)
+    _sync()
+    assert bool((out.rows == 0xAB).all())
+
+
+# ================================================================== indexer
+def _indexer_inputs(B, Tq, N, H_I, d_I, fmt, seed_shift=0, positions=None):
+    keys = synth.tensor(0, "idx_k", (B, N, d_I), rmsnorm=True, layer=seed_shift)
+    q = synth.tensor(0, "idx_q", (B, Tq * H_I, d_I), rmsnorm=True, layer=seed_shift)
+    w = synth.tensor(0, "head_w", (B, Tq, H_I), std=0.02, layer=seed_shift).astype(np.float32)
+    kst, kdeq = Hx.upload_store(keys, fmt)
+    qst, qdeq = Hx.upload_store(q, fmt)
+    return kst, kdeq, qst, qdeq.reshape(B, Tq, H_I, d_I), w
+
+
+def _run_indexer(lib, kst, qst, w, N, q_pos, B, Tq, H_I, m, k):
+    import torch
+    sel = torch.full((B, Tq, k), -7, dtype=torch.int32, device=Hx.dev())
+    nws = lib.indexer_topk_workspace(B, Tq, N, k)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=Hx.dev()) if nws else None
+    qp = None if q_pos is None else Hx.to_dev(np.asarray(q_pos, np.int64))
+    lib.indexer_topk(qst, Hx.to_dev(w), kst, N, qp, B, Tq, H_I, m, k, sel, ws)
+    _sync()
+    return sel.cpu().numpy()
+
+
+def _check_indexer(sel, kdeq, qdeq, w, N, m, k, pos):
+    B, Tq = sel.shape[:2]
+    flips = 0
+    for b in range(B):
+        for i in range(Tq):
+            t = pos[b][i]
+            nt = int(O.n_visible(t, m, N))
+            s = O.indexer_scores(qdeq[b, i], w[b, i].astype(np.float64), kdeq[b, :nt])
+            err = Hx.score_error_bound(qdeq[b, i], w[b, i].astype(np.float64), kdeq[b, :nt])
+            flips += Hx.check_topk(sel[b, i], s, k, err)
+    return flips
+
+
+@pytest.mark.parametrize("fmt,H_I,d_I,T,m,k", [("f32", 2, 32, 2048, 4, 64), ("fp8", 8, 64, 4096, 4, 512),
+                                                ("mxfp4", 8, 64, 1500, 4, 128), ("fp8", 4, 32, 999, 3, 100)])
+def test_indexer_prefill_parity(lib, fmt, H_I, d_I, T, m, k):
+    N = T // m
+    kst, kdeq, qst, qdeq, w = _indexer_inputs(1, T, N, H_I, d_I, fmt)
+    sel = _run_indexer(lib, kst, qst, w, N, None, 1, T, H_I, m, k)
+    # check every 7th query plus the edges (t < m-1 sees nothing, first full set, last)
+    rows = sorted(set(list(range(0, T, 7)) + [0, m - 2, m - 1, m, k * m - 1, k * m, T - 1]) - {-1})
+    rows = [r for r in rows if 0 <= r < T]
+    flips = _check_indexer(sel[:, rows], kdeq, qdeq[:, rows], w[:, rows], N, m, k, [rows])
+    assert flips <= max(2, len(rows) * k // 2000)
+
+
+@pytest.mark.parametrize("fmt,B,N,k", [("fp8", 3, 20000, 1024), ("mxfp4", 2, 9001, 1024), ("fp8", 2, 700, 1024),
+                                       ("fp8", 1, 40000, 512)])
+def test_indexer_decode_parity(lib, fmt, B, N, k):
+    """One query per sequence over many entries: several chunks + the merge."""
+    H_I, d_I, m = 8, 64, 4
+    kst, kdeq, qst, qdeq, w = _indexer_inputs(B, 1, N, H_I, d_I, fmt, seed_shift=1)
+    pos = [[m * N + 3 - 5 * b] for b in range(B)]         # later sequences see a few entries less
+    sel = _run_indexer(lib, kst, qst, w, N, pos, B, 1, H_I, m, k)
+    flips = _check_indexer(sel, kdeq, qdeq, w, N, m, k, pos)
+    assert flips <= 2
+
+
+def test_indexer_exact_ties_go_to_the_smaller_index(lib):
+    """Integer-valued queries/keys with w = 1: every score is exact on both
+    sides, with many exact ties (and exact zeros from the ReLU), so the
+    selected sets must be identical to the oracle's tie rule."""
+    B, Tq, N, H_I, d_I, m, k = 1, 64, 3000, 2, 32, 4, 200
+    rng = np.random.default_rng(11)
+    keys = rng.integers(-2, 3, (B, N, d_I)).astype(np.float64)
+    keys[:, :, 0] = 2.0                        # every row has amax 2 -> scale 2^-7, codes exact
+    q = rng.integers(-1, 2, (B, Tq * H_I, d_I)).astype(np.float64)
+    q[:, :, 1] = 1.0
+    w = np.ones((B, Tq, H_I), np.float32)
+    kst, kdeq = Hx.upload_store(keys, "fp8")
+    qst, qdeq = Hx.upload_store(q, "fp8")
+    assert np.array_equal(kdeq, keys) and np.array_equal(qdeq, q)
+    pos = [[4 * N - 1 - 37 * i for i in range(Tq)]]
+    sel = _run_indexer(lib, kst, qst, w, N, pos, B, Tq, H_I, m, k)
+    qd = q.reshape(B, Tq, H_I, d_I)
+    for i in range(Tq):
+        nt = int(O.n_visible(pos[0][i], m, N))
+        want = O.topk_select(O.indexer_scores(qd[0, i], w[0, i], keys[0, :nt]), k)
+        assert np.array_equal(sel[0, i], want), f"query {i}"
+
+
+def test_indexer_no_visible_entries_and_k_above_count(lib):
+    B, T, N, H_I, d_I, m, k = 1, 40, 10, 2, 64, 4, 16
+    kst, kdeq, qst, qdeq, w = _indexer_inputs(B, T, N, H_I, d_I, "fp8", seed_shift=2)
+    sel = _run_indexer(lib, kst, qst, w, N, None, B, T, H_I, m, k)
+    assert np.all(sel[0, :3] == -1)                        # t < m - 1: nothing visible
+    for t in range(T):
+        nt = int(O.n_visible(t, m, N))
+        assert np.array_equal(sel[0, t, :nt], np.arange(nt)) and np.all(sel[0, t, nt:] == -1)
+
+
+# ================================================================ attention
+def _attn_inputs(B, Tq, H, D, R, fmt, qf, n_kv, n_win, layer=0):
+    q = synth.tensor(0, "q", (B, Tq, H, D), rmsnorm=True, layer=layer)
+    ckv = synth.tensor(0, "kv", (B, n_kv, D), rmsnorm=True, layer=layer)
+    win = synth.tensor(0, "kv", (B, n_win, D), rmsnorm=True, layer=layer + 7)
+    sink = synth.tensor(0, "sink", (H,), layer=layer).astype(np.float32)
+    qd, qv = Hx.act(q, qf)
+    cst, cdeq = Hx.upload_store(ckv, fmt, R)
+    wst, wdeq = Hx.upload_store(win, fmt, R)
+    return qd, qv, cst, cdeq, wst, wdeq, sink
+
+
+@pytest.mark.parametrize("fmt,qf,H,D,R,T,m,k,W", [("f32", "f32", 4, 64, 0, 2048, 4, 64, 128),
+                                                  ("fp8", "bf16", 64, 512, 64, 700, 4, 64, 128),
+                                                  ("fp8", "bf16", 32, 512, 64, 300, 4, 96, 40),
+                                                  ("fp8", "f32", 4, 64, 16, 500, 4, 32, 128)])
+def test_csa_prefill_parity(lib, fmt, qf, H, D, R, T, m, k, W):
+    import torch
+    N = T // m
+    qd, qv, cst, cdeq, wst, wdeq, sink = _attn_inputs(1, T, H, D, R, fmt, qf, N, T)
+    sel = Hx.random_selection(T, m, N, k, seed=3)
+    sel[5, 0] = N + 100                         # out-of-range slots are skipped
+    out = torch.empty(qd.shape, dtype=qd.dtype, device=Hx.dev())
+    lse = torch.empty((1, T, H), dtype=torch.float32, device=Hx.dev())
+    tau = 1.0 / math.sqrt(D)
+    lib.sparse_attn_prefill(qd, cst, N, Hx.to_dev(sel[None]), k, wst, W, Hx.to_dev(sink), tau, out, lse)
+    _sync()
+    sel_o = sel.copy()
+    sel_o[5, 0] = -1
+    want, want_lse = O.csa_prefill(qv[0], cdeq[0], sel_o, wdeq[0], W, sink.astype(np.float64), tau)
+    Hx.check_attn(out.float().cpu().numpy()[0], want, bf16=(qf == "bf16"))
+    np.testing.assert_allclose(lse.cpu().numpy()[0], want_lse, rtol=1e-4, atol=1e-4)
+
+
+@pytest.mark.parametrize("H,D,R,T,m,W", [(64, 512, 64, 1000, 128, 128), (4, 64, 16, 700, 16, 32),
+                                         (32, 512, 64, 200, 128, 0)])
+def test_hca_prefill_parity(lib, H, D, R, T, m, W):
+    import torch
+    N = T // m
+    qd, qv, cst, cdeq, wst, wdeq, sink = _attn_inputs(1, T, H, D, R, "fp8", "bf16", N, T, layer=1)
+    out = torch.empty(qd.shape, dtype=qd.dtype, device=Hx.dev())
+    tau = 1.0 / math.sqrt(D)
+    snk = None if W == 0 else Hx.to_dev(sink)
+    lib.hca_attn(qd, cst, m, N, None, wst, W, snk, tau, out)
+    _sync()
+    want, _ = O.hca_prefill(qv[0], cdeq[0], m, wdeq[0], W, None if W == 0 else sink.astype(np.float64), tau)
+    got = out.float().cpu().numpy()[0]
+    Hx.check_attn(got, want)
+    if W == 0:
+        assert np.all(got[: m - 1] == 0)                # no entries, no window, no sink
+
+
+def _decode_setup(B, H, D, R, N, W, layer):
+    q = synth.tensor(0, "q", (B, H, D), rmsnorm=True, layer=layer)
+    ckv = synth.tensor(0, "kv", (B, N, D), rmsnorm=True, layer=layer)
+    ring = synth.tensor(0, "kv", (B, W, D), rmsnorm=True, layer=layer + 7)
+    sink = synth.tensor(0, "sink", (H,), layer=layer).astype(np.float32)
+    qd, qv = Hx.act(q, "bf16")
+    cst, cdeq = Hx.upload_store(ckv, "fp8", R)
+    rst, rdeq = Hx.upload_store(ring, "fp8", R)
+    return qd, qv, cst, cdeq, rst, rdeq, sink
+
+
+def test_csa_decode_parity(lib):
+    import torch
+    B, H, D, R, N, k, W, m = 4, 128, 512, 64, 5000, 1024, 128, 4
+    qd, qv, cst, cdeq, rst, rdeq, sink = _decode_setup(B, H, D, R, N, W, 2)
+    pos = np.array([m * N + b for b in range(B)], np.int64)
+    pos[3] = 60                                   # a short sequence: partial window
+    rng = np.random.default_rng(5)
+    sel = np.full((B, k), -1, np.int32)
+    for b in range(B):
+        nt = int(O.n_visible(pos[b], m, N))
+        pick = np.sort(rng.permutation(nt)[:k])
+        sel[b, : len(pick)] = pick
+    ws_n = lib.attn_workspace(B, 1, H, D, k + W)
+    ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=Hx.dev())
+    out = torch.empty(qd.shape, dtype=torch.bfloat16, device=Hx.dev())
+    tau = 1.0 / math.sqrt(D)
+    lib.sparse_attn_decode(qd, cst, N, Hx.to_dev(sel), k, rst, Hx.to_dev(pos), W, Hx.to_dev(sink), tau, out,
+                           ws=ws)
+    _sync()
+    got = out.float().cpu().numpy()
+    for b in range(B):
+        want, _ = O.csa_decode(qv[b], cdeq[b], sel[b], rdeq[b], int(pos[b]), W, sink.astype(np.float64), tau)
+        Hx.check_attn(got[b], want)
+
+
+def test_hca_decode_parity(lib):
+    import torch
+    B, H, D, R, N, W, m = 3, 128, 512, 64, 300, 128, 128
+    qd, qv, cst, cdeq, rst, rdeq, sink = _decode_setup(B, H, D, R, N, W, 3)
+    pos = np.array([m * N + 5, m * 100 - 1, 20], np.int64)
+    ws_n = lib.attn_workspace(B, 1, H, D, N + W)
+    ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=Hx.dev())
+    out = torch.empty((B, 1, H, D), dtype=torch.bfloat16, device=Hx.dev())
+    tau = 1.0 / math.sqrt(D)
+    lib.hca_attn(qd[:, None], cst, m, N, Hx.to_dev(pos[:, None]), rst, W, Hx.to_dev(sink), tau, out,
+                 flags=lib.WIN_RING, ws=ws)
+    _sync()
+    got = out.float().cpu().numpy()[:, 0]
+    for b in range(B):
+        want, _ = O.hca_decode(qv[b], cdeq[b], m, N, rdeq[b], int(pos[b]), W, sink.astype(np.float64), tau)
+        Hx.check_attn(got[b], want)
+
+
+def test_partial_then_swa_merge_equals_fused(lib):
+    import torch
+    T, H, D, R, m, k, W = 400, 64, 512, 64, 4, 64, 128
+    N = T // m
+    qd, qv, cst, cdeq, wst, wdeq, sink = _attn_inputs(1, T, H, D, R, "fp8", "bf16", N, T, layer=4)
+    sel = Hx.random_selection(T, m, N, k, seed=9)
+    tau = 1.0 / math.sqrt(D)
+    part = torch.empty((1, T, H, D), dtype=torch.float32, device=Hx.dev())
+    plse = torch.empty((1, T, H), dtype=torch.float32, device=Hx.dev())
+    lib.sparse_attn_prefill(qd, cst, N, Hx.to_dev(sel[None]), k, wst, W, None, tau, part, plse,
+                            flags=lib.ATTN_PARTIAL)
+    out = torch.empty(qd.shape, dtype=torch.bfloat16, device=Hx.dev())
+    lib.swa_merge(qd, wst, None, W, 0, part, plse, Hx.to_dev(sink), tau, out)
+    _sync()
+    # the partial alone: attention over the selected entries, no window, no sink
+    pw, pl = O.csa_prefill(qv[0], cdeq[0], sel, wdeq[0], 0, None, tau)
+    got_p = part.cpu().numpy()[0]
+    assert np.abs(got_p - pw).max() <= 1e-3
+    finite = np.isfinite(pl)
+    assert np.array_equal(np.isfinite(plse.cpu().numpy()[0]), finite)
+    np.testing.assert_allclose(plse.cpu().numpy()[0][finite], pl[finite], rtol=1e-4, atol=1e-4)
+    want, _ = O.csa_prefill(qv[0], cdeq[0], sel, wdeq[0], W, sink.astype(np.float64), tau)
+    Hx.check_attn(out.float().cpu().numpy()[0], want)
+    want_merge = np.stack([O.swa_merge(qv[0, t], wdeq[0, O.window_positions(t, W)], pw[t], pl[t],
+                                       sink.astype(np.float64), tau) for t in range(T)])
+    Hx.check_attn(out.float().cpu().numpy()[0], want_merge)
+
+
+# ============================================================= end to end
+def test_tiny_csa_f32_end_to_end(lib):
+    """The tiny fp32 CSA workload in full: compress KV and indexer keys,
+    store the window, quantise nothing (fp32), indexer + top-k, attention."""
+    import torch
+    cfg = synth.get_config("tiny_csa_f32")
+    T, D, H, m, k, W, HI, dI = cfg.T, cfg.D, cfg.H, cfg.m, cfg.k, cfg.W, cfg.H_I, cfg.d_I
+    N = cfg.N
+    x = synth.tensor(0, "kv", (T, D)).astype(np.float32).astype(np.float64)
+    xi = synth.tensor(0, "idx_k", (T, dI)).astype(np.float32).astype(np.float64)
+    qi = synth.tensor(0, "idx_q", (T, HI, dI)).astype(np.float32).astype(np.float64)
+    w = synth.tensor(0, "head_w", (T, HI), std=0.02).astype(np.float32)
+    q = synth.tensor(0, "q", (T, H, D)).astype(np.float32).astype(np.float64)
+    g = synth.tensor(0, "gate", (D,), std=0.02).astype(np.float32)
+    bb = synth.tensor(0, "bias", (m,), std=0.02).astype(np.float32)
+    gi = synth.tensor(0, "idx_gate", (dI,), std=0.02).astype(np.float32)
+    bi = synth.tensor(0, "idx_bias", (m,), std=0.02).astype(np.float32)
+    sink = synth.tensor(0, "sink", (H,)).astype(np.float32)
+    tau = 1.0 / math.sqrt(D)
+    t = lambda a: Hx.to_dev(np.asarray(a, np.float32))
+    ckv = lib.alloc_store(1, N, D, "f32", device=Hx.dev())
+    win = lib.alloc_store(1, T, D, "f32", device=Hx.dev())
+    keys = lib.alloc_store(1, N, dI, "f32", device=Hx.dev())
+    qst = lib.alloc_store(1, T * HI, dI, "f32", device=Hx.dev())
+    one = t(np.ones(1))
+    lib.compress_kv(t(x)[None], m, t(g), t(bb), ckv)
+    lib.compress_kv(t(x)[None], 1, t(g), one, win)
+    lib.compress_kv(t(xi)[None], m, t(gi), t(bi), keys)
+    lib.compress_kv(t(qi.reshape(T * HI, dI))[None], 1, t(gi), one, qst)
+    sel = torch.empty((1, T, k), dtype=torch.int32, device=Hx.dev())
+    lib.indexer_topk(qst, t(w)[None], keys, N, None, 1, T, HI, m, k, sel)
+    out = torch.empty((1, T, H, D), dtype=torch.float32, device=Hx.dev())
+    lib.sparse_attn_prefill(t(q)[None], ckv, N, sel, k, win, W, t(sink), tau, out)
+    _sync()
+    ent = O.compress(x, g.astype(np.float64), bb.astype(np.float64), m)
+    keys_o = O.compress(xi, gi.astype(np.float64), bi.astype(np.float64), m)
+    sel_g = sel.cpu().numpy()[0]
+    flips = 0
+    for i in range(T):
+        nt = int(O.n_visible(i, m, N))
+        s = O.indexer_scores(qi[i], w[i].astype(np.float64), keys_o[:nt])
+        # keys went through the float32 compressor: widen the bound by its error
+        err = Hx.score_error_bound(qi[i], w[i].astype(np.float64), keys_o[:nt]) * 4 + 1e-6 * np.abs(s)
+        flips += Hx.check_topk(sel_g[i], s, k, err)
+    assert flips <= 5
+    sel_o = np.stack([O.topk_select(O.indexer_scores(qi[i], w[i].astype(np.float64),
+                                                     keys_o[: int(O.n_visible(i, m, N))]), k) for i in range(T)])
+    want, _ = O.csa_prefill(q, ent, sel_o, x, W, sink.astype(np.float64), tau)
+    same = np.array([np.array_equal(a, b) for a, b in zip(sel_g, sel_o)])
+    err = np.abs(out.cpu().numpy()[0] - want)
+    assert err[same].max() <= 1e-4
+    assert err.max() <= 2e-2 and err.mean() <= 2e-3
