@@ -254,7 +254,7 @@ static int attn_nsplit(int B, int Tq, int H, int D, int64_t max_list, int& split
   if (wgs >= 1024 || max_list <= 128) return 1;
   int64_t want = (1024 + wgs - 1) / wgs;                 // splits per query for ~1024 workgroups
   int64_t len = (max_list + want - 1) / want;
-  len = ((len + kTile - 1) / kTile) * kTile;
+  len = ((len + 31) / 32) * 32;                          // whole 32-entry tiles
   if (len < 64) len = 64;
   split_len = (int)len;
   return (int)((max_list + len - 1) / len);
@@ -283,6 +283,12 @@ hipError_t launch_attn(const AttnCall& c, hipStream_t st) {
   a.split_len = len;
   a.ws = (float*)c.ws;
   if ((int64_t)c.B * c.Tq == 0) return hipSuccess;
+  if (attn_mfma_eligible(c.q_fmt, c.H, c.D, c.ckv.rows ? c.ckv : c.win, c.prior_o != nullptr)) {
+    hipError_t e = launch_attn_mfma(c, a.nsplit, a.split_len, st);
+    if (e != hipSuccess || a.nsplit == 1) return e;
+    hipLaunchKernelGGL(attn_split_merge_kernel, dim3((unsigned)((int64_t)c.B * c.Tq), c.H), dim3(64), 0, st, a);
+    return hipGetLastError();
+  }
   const AttnShape s = attn_shape(c.H, c.D);
   const dim3 grid((unsigned)((int64_t)c.B * c.Tq), c.H / s.hg, a.nsplit);
   const dim3 block(s.hg * s.tph);

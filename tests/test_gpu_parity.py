@@ -299,7 +299,7 @@ def test_partial_then_swa_merge_equals_fused(lib):
     # the partial alone: attention over the selected entries, no window, no sink
     pw, pl = O.csa_prefill(qv[0], cdeq[0], sel, wdeq[0], 0, None, tau)
     got_p = part.cpu().numpy()[0]
-    assert np.abs(got_p - pw).max() <= 1e-3
+    Hx.check_attn(got_p, pw)                    # bf16 MFMA arithmetic, float32 storage
     finite = np.isfinite(pl)
     assert np.array_equal(np.isfinite(plse.cpu().numpy()[0]), finite)
     np.testing.assert_allclose(plse.cpu().numpy()[0][finite], pl[finite], rtol=1e-4, atol=1e-4)
