@@ -49,17 +49,21 @@ __device__ __forceinline__ int64_t m_visible(int64_t t, int m, int64_t n) {
   return v < n ? v : n;
 }
 
-// Row of list slot i; src 0 = empty, 1 = compressed store, 2 = window store.
-__device__ __forceinline__ int m_list_row(const MfmaArgs& a, int64_t bq, int b, int64_t t, int64_t Lc,
-                                          int64_t i, int64_t i1, int64_t& row) {
+// Index of list slot i that has to come from memory (the sel entry of a
+// top-k slot); other slots need no load.
+__device__ __forceinline__ int m_slot_sel(const MfmaArgs& a, int64_t bq, int64_t Lc, int64_t i, int64_t i1) {
+  return (a.mode == kModeSel && i < Lc && i < i1) ? a.sel[bq * a.k + i] : 0;
+}
+
+// Row of list slot i (jsel = its sel entry for top-k slots); src 0 = empty,
+// 1 = compressed store, 2 = window store.
+__device__ __forceinline__ int m_slot_row(const MfmaArgs& a, int b, int64_t t, int64_t Lc, int64_t i, int64_t i1,
+                                          int jsel, int64_t& row) {
   row = 0;
   if (i >= i1) return 0;
   if (i < Lc) {
-    int64_t j = i;
-    if (a.mode == kModeSel) {
-      j = a.sel[bq * a.k + i];
-      if (j < 0 || j >= a.n_entries) return 0;
-    }
+    const int64_t j = a.mode == kModeSel ? (int64_t)jsel : i;
+    if (j < 0 || j >= a.n_entries) return 0;
     row = (int64_t)b * a.ckv.cap + j;
     return 1;
   }
@@ -78,15 +82,27 @@ __device__ __forceinline__ u32x4 cvt8_fp8(u32x2 w, float s) {
   return r;
 }
 
-// One staging unit: dims [8g, 8g+8) of the entry pair (2p, 2p+1).
-struct StageUnit {
-  u32x4 a, b;   // raw bytes: fp8 in .x/.y (bulk) or 8 bf16 (rope)
-};
+// A row of zeros that empty slots gather from (device globals start zeroed).
+__device__ __attribute__((aligned(16))) uint8_t g_zero_row[1024];
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) void lds_void;
+
+constexpr int kRawRow = 576;                      // 448 FP8 + 64 BF16
+constexpr int kRawTile = kMT * kRawRow;           // 18432 B = 18 wave-wide 1 KiB loads
+constexpr int kRawLoads = kRawTile / 1024;
+constexpr int kKsTile = kMT * kKsPitch;           // bf16 elements per converted tile
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+#define CSA_WAIT_VMCNT0() __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8))
 
 __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kMT * kKsPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[kMD * kVtPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kKsTile];
+  __shared__ __attribute__((aligned(16))) uint8_t Raw[2][kRawTile];
   __shared__ __attribute__((aligned(16))) float Sx[4][16][64];
+  __shared__ const uint8_t* Tptr[4][kMT];         // per tile slot: row address (zero row if empty)
+  __shared__ float Tscl[4][kMT];                  // row scale, 0 if empty
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -100,16 +116,68 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
   const int64_t L = Lc + a.W;
   const int64_t i0 = (int64_t)blockIdx.z * a.split_len;
   const int64_t i1 = a.nsplit == 1 ? L : (i0 + a.split_len < L ? i0 + a.split_len : L);
-  const int nbulk = a.ckv.dim - a.ckv.rope;                // 448
-  const int gbulk = nbulk / 8;                              // dim groups in FP8
+  const int ntiles = i1 > i0 ? (int)((i1 - i0 + kMT - 1) / kMT) : 0;
 
-  // Q^T operand: 16 K-steps of 16 dims over this wave's 256 dims
+  // slot table of tile `tile` (threads < 32 own one slot each)
+  auto write_table = [&](int tile, int jsel) {
+    int64_t row;
+    const int64_t slot = i0 + (int64_t)tile * kMT + tid;
+    const int src = m_slot_row(a, b, t, Lc, slot, i1, jsel, row);
+    const Store& stv = src == 2 ? a.win : a.ckv;
+    Tptr[tile & 3][tid] = src ? stv.rows + row * stv.row_bytes : g_zero_row;
+    Tscl[tile & 3][tid] = src ? ((const float*)stv.scales)[row] : 0.0f;
+  };
+  auto sel_of = [&](int tile) -> int {
+    return m_slot_sel(a, bq, Lc, i0 + (int64_t)tile * kMT + tid, i1);
+  };
+  // DMA the raw rows of `tile` into Raw[tile & 1]: 18 wave-wide loads of
+  // 1 KiB, load q covering raw bytes [1024 q, 1024 q + 1024).
+  auto dma_tile = [&](int tile) {
+    uint8_t* dst = Raw[tile & 1];
+    for (int qd = wave; qd < kRawLoads; qd += 4) {
+      const int ci = qd * 64 + lane;                   // 16-byte chunk of the tile
+      const int slot = ci / 36, ch = ci - slot * 36;
+      const uint8_t* src = Tptr[tile & 3][slot] + 16 * ch;
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(dst + 1024 * qd), 16, 0, 0);
+    }
+  };
+  // Raw[tile & 1] -> Ks[tile & 1]: FP8 * row scale -> BF16 (exact), RoPE dims copied.
+  auto convert_tile = [&](int tile) {
+    const uint8_t* raw = Raw[tile & 1];
+    uint16_t* ks = Ks[tile & 1];
+    const int row = tid >> 3, sub = tid & 7;
+    const float sc = Tscl[tile & 3][row];
+    const uint8_t* rr = raw + row * kRawRow;
+    uint16_t* kr = ks + row * kKsPitch;
+#pragma unroll
+    for (int mm = 0; mm < 7; ++mm) {
+      const int u = sub + 8 * mm;                       // 8-byte unit of the 448 FP8 bytes
+      const u32x2 w = *(const u32x2*)(rr + 8 * u);
+      *(u32x4*)(kr + 8 * u) = cvt8_fp8(w, sc);
+    }
+    *(u32x4*)(kr + 448 + 8 * sub) = *(const u32x4*)(rr + 448 + 16 * sub);
+  };
+
+  // ---- prologue
+  int selreg = 0;
+  if (tid < kMT) {
+    for (int tl = 0; tl < 3; ++tl) write_table(tl, sel_of(tl));
+    selreg = sel_of(3);
+  }
+  __syncthreads();
+  if (ntiles > 0) dma_tile(0);
+  if (ntiles > 1) dma_tile(1);
   bf16x8 qf[16];
   {
     const uint16_t* qp = a.q + (bq * a.H + h) * (int64_t)kMD + dh * 256 + g32 * 8;
 #pragma unroll
     for (int s = 0; s < 16; ++s) qf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qp + 16 * s));
   }
+  CSA_WAIT_VMCNT0();
+  __syncthreads();
+  if (ntiles > 0) convert_tile(0);
+  __syncthreads();
+
   f32x16 acc[8];
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt)
@@ -118,86 +186,20 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
   float mrun = -INFINITY, lrun = 0.0f;
   const float sc2 = a.tau * kLog2e;
 
-  // staging assignment: entry pair p, dim groups g = gq + 16 j
-  const int sp = tid & 15, gq = tid >> 4;
+  // transposed-read addressing of V^T (see the ds_read_b64_tr_b16 lane map):
+  // lane j of a 16-lane group points at entry row 4*g + (j>>2) (+8 for the
+  // second half of a K-step), dims D0 + 16*half + 4*(j&3).
+  const int trj = lane & 15, trhalf = (lane >> 4) & 1;
+  const int tr_row = 4 * g32 + (trj >> 2);
+  const int tr_col = dh * 256 + 16 * trhalf + 4 * (trj & 3);
 
-  auto load_tile = [&](int64_t base, StageUnit (&u)[4], float& sa, float& sb, int& va, int& vb) {
-    int64_t ra, rb;
-    const int srca = m_list_row(a, bq, b, t, Lc, base + 2 * sp, i1, ra);
-    const int srcb = m_list_row(a, bq, b, t, Lc, base + 2 * sp + 1, i1, rb);
-    const Store& sta = srca == 2 ? a.win : a.ckv;
-    const Store& stb = srcb == 2 ? a.win : a.ckv;
-    va = srca; vb = srcb;
-    sa = srca ? ((const float*)sta.scales)[ra] : 0.0f;
-    sb = srcb ? ((const float*)stb.scales)[rb] : 0.0f;
-    const uint8_t* pa = sta.rows + ra * sta.row_bytes;
-    const uint8_t* pb = stb.rows + rb * stb.row_bytes;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int g = gq + 16 * j;
-      u32x4 za = {0u, 0u, 0u, 0u}, zb = {0u, 0u, 0u, 0u};
-      if (g < gbulk) {
-        if (srca) { u32x2 w = *(const u32x2*)(pa + 8 * g); za.x = w.x; za.y = w.y; }
-        if (srcb) { u32x2 w = *(const u32x2*)(pb + 8 * g); zb.x = w.x; zb.y = w.y; }
-      } else {
-        const int off = nbulk + 16 * (g - gbulk);
-        if (srca) za = *(const u32x4*)(pa + off);
-        if (srcb) zb = *(const u32x4*)(pb + off);
-      }
-      u[j].a = za;
-      u[j].b = zb;
-    }
-  };
-  auto store_tile = [&](const StageUnit (&u)[4], float sa, float sb, int va, int vb) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int g = gq + 16 * j;
-      u32x4 ca, cb;
-      if (g < gbulk) {
-        u32x2 wa = {u[j].a.x, u[j].a.y}, wb = {u[j].b.x, u[j].b.y};
-        ca = cvt8_fp8(wa, sa);
-        cb = cvt8_fp8(wb, sb);
-        if (!va) ca = u32x4{0u, 0u, 0u, 0u};
-        if (!vb) cb = u32x4{0u, 0u, 0u, 0u};
-      } else {
-        ca = u[j].a;
-        cb = u[j].b;
-      }
-      *(u32x4*)(Ks + (2 * sp) * kKsPitch + 8 * g) = ca;
-      *(u32x4*)(Ks + (2 * sp + 1) * kKsPitch + 8 * g) = cb;
-      const unsigned int A4[4] = {ca.x, ca.y, ca.z, ca.w};
-      const unsigned int B4[4] = {cb.x, cb.y, cb.z, cb.w};
-#pragma unroll
-      for (int q2 = 0; q2 < 4; ++q2) {
-        *(unsigned int*)(Vt + (8 * g + 2 * q2) * kVtPitch + 2 * sp) = __builtin_amdgcn_perm(B4[q2], A4[q2], 0x05040100u);
-        *(unsigned int*)(Vt + (8 * g + 2 * q2 + 1) * kVtPitch + 2 * sp) = __builtin_amdgcn_perm(B4[q2], A4[q2], 0x07060302u);
-      }
-    }
-  };
-
-  StageUnit u[4];
-  float su_a, su_b;
-  int sv_a, sv_b;
-  if (i0 < i1) {
-    load_tile(i0, u, su_a, su_b, sv_a, sv_b);
-    store_tile(u, su_a, su_b, sv_a, sv_b);
-  }
-  __syncthreads();
-
-  for (int64_t base = i0; base < i1; base += kMT) {
-    const bool more = base + kMT < i1;
-    if (more) load_tile(base + kMT, u, su_a, su_b, sv_a, sv_b);   // prefetch the next tile
-
-    // validity of this tile's 32 slots
-    int64_t rdummy;
-    const bool vslot = lane < 32 && m_list_row(a, bq, b, t, Lc, base + lane, i1, rdummy) != 0;
-    const unsigned int vmask = (unsigned int)__ballot(vslot);
-
+  for (int it = 0; it < ntiles; ++it) {
+    const uint16_t* ks = Ks[it & 1];
     // S^T partial over this wave's dims: two accumulators for independent chains
     f32x16 s0, s1;
 #pragma unroll
     for (int r = 0; r < 16; ++r) { s0[r] = 0.0f; s1[r] = 0.0f; }
-    const uint16_t* kp = Ks + l32 * kKsPitch + dh * 256 + g32 * 8;
+    const uint16_t* kp = ks + l32 * kKsPitch + dh * 256 + g32 * 8;
 #pragma unroll
     for (int s = 0; s < 16; s += 2) {
       const bf16x8 ka = __builtin_bit_cast(bf16x8, *(const u32x4*)(kp + 16 * s));
@@ -210,7 +212,18 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
       s0[r] += s1[r];
       Sx[wave][r][lane] = s0[r];
     }
-    __syncthreads();
+    CSA_WAIT_VMCNT0();                      // raw rows of tile it+1 and the next sel are in
+    if (tid < kMT && it + 3 < ntiles) write_table(it + 3, selreg);
+    __syncthreads();                        // B1
+    if (it + 2 < ntiles) dma_tile(it + 2);  // into Raw[it & 1], converted last iteration
+    if (tid < kMT && it + 4 < ntiles) selreg = sel_of(it + 4);
+
+    // softmax on this tile's logits
+    unsigned int vmask = 0;
+    {
+      const float sv = Tscl[it & 3][l32];
+      vmask = (unsigned int)__ballot(lane < 32 && sv > 0.0f);
+    }
     float p[16];
     float mt = -INFINITY;
 #pragma unroll
@@ -221,52 +234,54 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
       mt = fmaxf(mt, p[r]);
     }
     mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float mnew = fmaxf(mrun, mt);
-    float corr = 1.0f, psum = 0.0f;
-    if (mnew > -INFINITY) {
-      corr = mrun > -INFINITY ? exp2f(mrun - mnew) : 0.0f;
+    // Lazy rescaling: the accumulator keeps its reference max mrun until a
+    // tile's max exceeds it by more than 8 (factor 256); probabilities are
+    // then at most 2^8, which float32 and bf16 hold exactly enough.  This
+    // keeps the O^T accumulators out of VALU code on almost every tile.
+    if (__ballot(mt > mrun + 8.0f)) {
+      const float mnew = fmaxf(mrun, mt);
+      const float corr = mrun > -INFINITY ? exp2f(mrun - mnew) : 0.0f;
+      if (mrun > -INFINITY) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        p[r] = exp2f(p[r] - mnew);
-        psum += p[r];
+        for (int mt8 = 0; mt8 < 8; ++mt8)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[mt8][r] *= corr;
       }
+      lrun *= corr;
       mrun = mnew;
-    } else {
+    }
+    float psum = 0.0f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) p[r] = 0.0f;
+    for (int r = 0; r < 16; ++r) {
+      p[r] = mrun > -INFINITY ? exp2f(p[r] - mrun) : 0.0f;
+      psum += p[r];
     }
     psum += __shfl_xor(psum, 32);
-    lrun = lrun * corr + psum;
-    // P^T as the B operand of two K-steps (regs 0..7, 8..15)
+    lrun += psum;
     bf16x8 pb0, pb1;
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       pb0[r] = (__bf16)p[r];
       pb1[r] = (__bf16)p[r + 8];
     }
-#pragma unroll
-    for (int mt8 = 0; mt8 < 8; ++mt8)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mt8][r] *= corr;
-    // O^T += V^T P^T
+    if (it + 1 < ntiles) convert_tile(it + 1);   // Ks[(it+1)&1] was released at the last B2
+
+    // O^T += V^T P^T, V^T read transposed from Ks
 #pragma unroll
     for (int mt8 = 0; mt8 < 8; ++mt8) {
-      const uint16_t* vp = Vt + (dh * 256 + mt8 * 32 + l32) * kVtPitch + g32 * 4;
-      u32x4 v0, v1;
-      const u32x2 a0 = *(const u32x2*)(vp);
-      const u32x2 a1 = *(const u32x2*)(vp + 8);
-      const u32x2 b0 = *(const u32x2*)(vp + 16);
-      const u32x2 b1 = *(const u32x2*)(vp + 24);
-      v0 = u32x4{a0.x, a0.y, a1.x, a1.y};
-      v1 = u32x4{b0.x, b0.y, b1.x, b1.y};
+      const uint16_t* vb = ks + tr_row * kKsPitch + tr_col + 32 * mt8;
+      const v4i16 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vb));
+      const v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vb + 8 * kKsPitch));
+      const v4i16 y0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vb + 16 * kKsPitch));
+      const v4i16 y1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vb + 24 * kKsPitch));
+      const u32x2 ux0 = __builtin_bit_cast(u32x2, x0), ux1 = __builtin_bit_cast(u32x2, x1);
+      const u32x2 uy0 = __builtin_bit_cast(u32x2, y0), uy1 = __builtin_bit_cast(u32x2, y1);
+      const u32x4 v0 = u32x4{ux0.x, ux0.y, ux1.x, ux1.y};
+      const u32x4 v1 = u32x4{uy0.x, uy0.y, uy1.x, uy1.y};
       acc[mt8] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v0), pb0, acc[mt8], 0, 0, 0);
       acc[mt8] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v1), pb1, acc[mt8], 0, 0, 0);
     }
-    __syncthreads();                         // every wave is done with Ks / Vt / Sx
-    if (more) {
-      store_tile(u, su_a, su_b, sv_a, sv_b);
-      __syncthreads();
-    }
+    __syncthreads();                        // B2
   }
 
   // ---- epilogue
@@ -278,9 +293,10 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
 #pragma unroll
     for (int mt8 = 0; mt8 < 8; ++mt8)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int d = dh * 256 + mt8 * 32 + (r >> 2) * 8 + g32 * 4 + (r & 3);
-        wo[d] = acc[mt8][r];
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d = dh * 256 + mt8 * 32 + r4 * 8 + g32 * 4;
+        *(float4*)(wo + d) = make_float4(acc[mt8][r4 * 4], acc[mt8][r4 * 4 + 1], acc[mt8][r4 * 4 + 2],
+                                         acc[mt8][r4 * 4 + 3]);
       }
     if (dh == 0 && g32 == 0) {
       wml[0] = mrun > -INFINITY ? mrun * kLn2 : -INFINITY;
@@ -319,7 +335,7 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
 
 bool attn_mfma_eligible(int q_fmt, int H, int D, const csa_store& kv, bool has_prior) {
   return !has_prior && q_fmt == CSA_BF16 && D == kMD && H % 64 == 0 && kv.fmt == CSA_FP8_E4M3 &&
-         (kv.dim - kv.rope_dim) % 8 == 0;
+         kv.row_bytes == kRawRow;
 }
 
 hipError_t launch_attn_mfma(const AttnCall& c, int nsplit, int split_len, hipStream_t st) {

@@ -21,97 +21,109 @@ constexpr int kMaxHI = 16;
 constexpr int kMaxDI = 64;
 
 struct SelShared {
-  uint32_t hist[256];
+  uint32_t hist[2048];
   uint32_t misc[4];
   uint32_t wtot[2][kIdxWaves];
 };
 
-// Exact radix select on keys[0, n): returns the k-th largest key `thr` and how
-// many keys equal to thr are to be taken (the first ones by position).
+// Exact radix select on keys[0, n): returns the kk-th largest key `thr` and
+// how many keys equal to thr are to be taken (the first ones by position).
+// Three passes over 11/11/10-bit digits, most significant first; each pass
+// histograms the keys that match the digits found so far and one wavefront
+// locates the digit holding the kk-th key with a suffix scan.
 // Needs 1 <= kk <= #nonzero keys.  Called by all kIdxThreads threads.
 __device__ void radix_select(const uint32_t* keys, int n, int kk, SelShared& sh, uint32_t& thr,
                              int& need_eq) {
   const int tid = threadIdx.x, lane = tid % kWave;
   uint32_t prefix = 0, mask = 0;
   int remaining = kk;
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int i = tid; i < 256; i += kIdxThreads) sh.hist[i] = 0;
+  const int shifts[3] = {21, 10, 0};
+  const int widths[3] = {11, 11, 10};
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = shifts[pass];
+    const int nb = 1 << widths[pass];
+    const uint32_t dmask = (uint32_t)nb - 1u;
+    for (int i = tid; i < nb; i += kIdxThreads) sh.hist[i] = 0;
     __syncthreads();
     for (int i = tid; i < n; i += kIdxThreads) {
       const uint32_t key = keys[i];
-      if (key != 0u && (key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
+      if (key != 0u && (key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & dmask], 1u);
     }
     __syncthreads();
     if (tid < kWave) {
-      uint32_t c[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) c[i] = sh.hist[4 * lane + i];
-      uint32_t local = c[0] + c[1] + c[2] + c[3];
-      uint32_t suf = local;               // inclusive suffix sum over lanes >= lane
+      const int per = nb / kWave;            // 32 or 16 bins per lane
+      uint32_t local = 0;
+      for (int i = 0; i < per; ++i) local += sh.hist[per * lane + i];
+      uint32_t suf = local;                  // inclusive suffix sum over lanes >= lane
 #pragma unroll
       for (int o = 1; o < kWave; o <<= 1) {
         uint32_t t = __shfl_down(suf, o);
         if (lane + o < kWave) suf += t;
       }
-      uint32_t above = suf - local;       // keys in bins of higher lanes
-#pragma unroll
-      for (int i = 3; i >= 0; --i) {
-        if (above < (uint32_t)remaining && above + c[i] >= (uint32_t)remaining) {
-          sh.misc[0] = 4 * lane + i;
-          sh.misc[1] = above;
+      uint32_t above = suf - local;          // keys in bins of higher lanes
+      if (above < (uint32_t)remaining && suf >= (uint32_t)remaining) {
+        for (int i = per - 1; i >= 0; --i) {
+          const uint32_t c = sh.hist[per * lane + i];
+          if (above + c >= (uint32_t)remaining) {
+            sh.misc[0] = per * lane + i;
+            sh.misc[1] = above;
+            break;
+          }
+          above += c;
         }
-        above += c[i];
       }
     }
     __syncthreads();
     const uint32_t d = sh.misc[0];
     remaining -= (int)sh.misc[1];
     prefix |= d << shift;
-    mask |= 255u << shift;
+    mask |= dmask << shift;
     __syncthreads();
   }
   thr = prefix;
   need_eq = remaining;
 }
 
-// Walk positions 0..n-1 in order and call emit(pos, rank) for each selected
-// position; rank is its index in the ascending output.  Returns nothing; all
-// threads participate.
+// Call emit(pos, rank) for each selected position, rank = its index in the
+// ascending output.  Wave w walks its own contiguous range of positions in
+// 64-wide rounds; a first pass counts keys above / equal to thr per wave,
+// one barrier publishes the counts, the second pass emits with ballot
+// prefixes (no further barriers).
 template <typename Emit>
 __device__ void emit_selected(const uint32_t* keys, int n, uint32_t thr, int need_eq, SelShared& sh,
                               Emit emit) {
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int per = ((n + kIdxWaves * kWave - 1) / (kIdxWaves * kWave)) * kWave;
+  const int p0 = wave * per;
+  const int p1 = p0 + per < n ? p0 + per : n;
+  uint32_t ngt = 0, neq = 0;
+  for (int r0 = p0; r0 < p1; r0 += kWave) {
+    const int pos = r0 + lane;
+    const uint32_t key = pos < p1 ? keys[pos] : 0u;
+    ngt += (uint32_t)__popcll(__ballot(key != 0u && key > thr));
+    neq += (uint32_t)__popcll(__ballot(key != 0u && key == thr));
+  }
+  if (lane == 0) { sh.wtot[0][wave] = ngt; sh.wtot[1][wave] = neq; }
+  __syncthreads();
   int eq_base = 0, sel_base = 0;
-  for (int r0 = 0; r0 < n; r0 += kIdxThreads) {
-    const int pos = r0 + tid;
-    const uint32_t key = pos < n ? keys[pos] : 0u;
+  for (int w = 0; w < wave; ++w) {
+    const int gt = (int)sh.wtot[0][w], eq = (int)sh.wtot[1][w];
+    int take_eq = need_eq - eq_base;
+    take_eq = take_eq < 0 ? 0 : (take_eq > eq ? eq : take_eq);
+    sel_base += gt + take_eq;
+    eq_base += eq;
+  }
+  for (int r0 = p0; r0 < p1; r0 += kWave) {
+    const int pos = r0 + lane;
+    const uint32_t key = pos < p1 ? keys[pos] : 0u;
     const bool eq = key != 0u && key == thr;
     const uint64_t beq = __ballot(eq);
-    if (lane == 0) sh.wtot[0][wave] = (uint32_t)__popcll(beq);
-    __syncthreads();
-    int woff = 0, tot_eq = 0;
-    for (int w = 0; w < kIdxWaves; ++w) {
-      const int v = (int)sh.wtot[0][w];
-      woff += w < wave ? v : 0;
-      tot_eq += v;
-    }
-    const int eq_rank = eq_base + woff + __popcll(beq & lt);
-    const bool take = (key != 0u && key > thr) || (eq && eq_rank < need_eq);
+    const bool take = (key != 0u && key > thr) || (eq && eq_base + __popcll(beq & lt) < need_eq);
     const uint64_t bs = __ballot(take);
-    if (lane == 0) sh.wtot[1][wave] = (uint32_t)__popcll(bs);
-    __syncthreads();
-    int soff = 0, tot_s = 0;
-    for (int w = 0; w < kIdxWaves; ++w) {
-      const int v = (int)sh.wtot[1][w];
-      soff += w < wave ? v : 0;
-      tot_s += v;
-    }
-    if (take) emit(pos, sel_base + soff + __popcll(bs & lt));
-    eq_base += tot_eq;
-    sel_base += tot_s;
-    __syncthreads();
+    if (take) emit(pos, sel_base + __popcll(bs & lt));
+    eq_base += __popcll(beq);
+    sel_base += __popcll(bs);
   }
 }
 
@@ -168,6 +180,133 @@ struct IdxArgs {
   int32_t* ws_idx;
 };
 
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+
+// Scores of entries [c0, c0 + cn) for one query on MFMA, written to s_keys.
+// Heads are the 16 rows of the A operand (H_I <= 16, the rest zero), 16
+// entries are the columns; the head-weighted ReLU sum is a lane-local sum
+// over 4 heads plus two cross-lane adds.
+//   FP8  : v_mfma_f32_16x16x32_fp8_fp8; the row scales of q fold into the
+//          head weights, the key scale multiplies the sum (powers of two).
+//   MXFP4: v_mfma_scale_f32_16x16x128_f8f6f4 with E2M1 operands and the
+//          per-32-element E8M0 scales applied by the instruction; k-blocks
+//          beyond d_I are zero.
+template <int FMT, int DI>
+__device__ __forceinline__ void score_chunk_mfma(const IdxArgs& a, int b, int q, int64_t bq, int64_t c0, int cn,
+                                                 uint32_t* s_keys, float* s_w) {
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int col = lane & 15, g = lane >> 4;
+  const int64_t qrow0 = (int64_t)b * a.qidx.cap + (int64_t)q * a.H_I;
+  // head weights for the 4 heads of this lane's accumulator rows
+  for (int h = tid; h < 16; h += kIdxThreads) {
+    float w = 0.0f;
+    if (h < a.H_I) {
+      w = a.head_w[bq * a.H_I + h];
+      if (FMT == CSA_FP8_E4M3) w *= ((const float*)a.qidx.scales)[qrow0 + h];
+    }
+    s_w[h] = w;
+  }
+  __syncthreads();
+  float wl[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) wl[i] = s_w[4 * g + i];
+  const int64_t krow0 = (int64_t)b * a.keys.cap + c0;
+  const int ngroups = (cn + 15) / 16;
+  if constexpr (FMT == CSA_FP8_E4M3) {
+    // A operand: q row `col`, K-step 0 = bytes [16g, 16g+8), K-step 1 = [16g+8, 16g+16)
+    // (DI = 32: one K-step of bytes [8g, 8g+8))
+    long long qa0 = 0, qa1 = 0;
+    if (col < a.H_I) {
+      const uint8_t* qp = a.qidx.rows + (qrow0 + col) * a.qidx.row_bytes;
+      if (DI == 64) {
+        const uint4 v = *(const uint4*)(qp + 16 * g);
+        qa0 = (long long)(((unsigned long long)v.y << 32) | v.x);
+        qa1 = (long long)(((unsigned long long)v.w << 32) | v.z);
+      } else {
+        const uint2 v = *(const uint2*)(qp + 8 * g);
+        qa0 = (long long)(((unsigned long long)v.y << 32) | v.x);
+      }
+    }
+    const float* ksc = (const float*)a.keys.scales;
+    constexpr int U = 8;                    // groups in flight per wave
+    for (int grp0 = wave * U; grp0 < ngroups; grp0 += kIdxWaves * U) {
+      long long kb0[U], kb1[U];
+      float sk[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int e = (grp0 + u) * 16 + col;
+        kb0[u] = 0; kb1[u] = 0; sk[u] = 0.0f;
+        if (e < cn) {
+          const uint8_t* kp = a.keys.rows + (krow0 + e) * a.keys.row_bytes;
+          if (DI == 64) {
+            const uint4 v = *(const uint4*)(kp + 16 * g);
+            kb0[u] = (long long)(((unsigned long long)v.y << 32) | v.x);
+            kb1[u] = (long long)(((unsigned long long)v.w << 32) | v.z);
+          } else {
+            const uint2 v = *(const uint2*)(kp + 8 * g);
+            kb0[u] = (long long)(((unsigned long long)v.y << 32) | v.x);
+          }
+          sk[u] = ksc[krow0 + e];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int e = (grp0 + u) * 16 + col;
+        f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
+        c = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(qa0, kb0[u], c, 0, 0, 0);
+        if (DI == 64) c = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(qa1, kb1[u], c, 0, 0, 0);
+        float v = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v = fmaf(wl[i], fmaxf(c[i], 0.0f), v);
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        if (g == 0 && e < cn) s_keys[e] = score_key(v * sk[u]);
+      }
+    }
+  } else {
+    // A operand: q row `col`, k-block g (32 E2M1 = 16 bytes) and its E8M0
+    i32x8 qa = {0, 0, 0, 0, 0, 0, 0, 0};
+    int qs = 127;
+    if (col < a.H_I && g < DI / 32) {
+      const uint8_t* qp = a.qidx.rows + (qrow0 + col) * a.qidx.row_bytes;
+      const uint4 v = *(const uint4*)(qp + 16 * g);
+      qa[0] = (int)v.x; qa[1] = (int)v.y; qa[2] = (int)v.z; qa[3] = (int)v.w;
+      qs = ((const uint8_t*)a.qidx.scales)[(qrow0 + col) * (DI / 32) + g];
+    }
+    const uint8_t* ksc = (const uint8_t*)a.keys.scales;
+    constexpr int U = 8;
+    for (int grp0 = wave * U; grp0 < ngroups; grp0 += kIdxWaves * U) {
+      uint4 kv[U];
+      int ks[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int e = (grp0 + u) * 16 + col;
+        kv[u] = make_uint4(0u, 0u, 0u, 0u);
+        ks[u] = 127;
+        if (e < cn && g < DI / 32) {
+          const uint8_t* kp = a.keys.rows + (krow0 + e) * a.keys.row_bytes;
+          kv[u] = *(const uint4*)(kp + 16 * g);
+          ks[u] = ksc[(krow0 + e) * (DI / 32) + g];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int e = (grp0 + u) * 16 + col;
+        i32x8 kb = {(int)kv[u].x, (int)kv[u].y, (int)kv[u].z, (int)kv[u].w, 0, 0, 0, 0};
+        f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
+        c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa, kb, c, 4, 4, 0, qs, 0, ks[u]);
+        float v = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v = fmaf(wl[i], fmaxf(c[i], 0.0f), v);
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        if (g == 0 && e < cn) s_keys[e] = score_key(v);
+      }
+    }
+  }
+}
+
 template <int FMT, int DI>
 __global__ __launch_bounds__(kIdxThreads) void idx_chunk_kernel(IdxArgs a) {
   extern __shared__ uint32_t s_keys[];
@@ -196,25 +335,27 @@ __global__ __launch_bounds__(kIdxThreads) void idx_chunk_kernel(IdxArgs a) {
   }
   if (kk == 0) return;                        // uniform over the workgroup
 
-  // queries (dequantised) and head weights
-  for (int h = tid; h < a.H_I; h += kIdxThreads) {
-    decode_row<FMT>(a.qidx, (int64_t)b * a.qidx.cap + (int64_t)q * a.H_I + h, DI, s_q + h * DI);
-    s_w[h] = a.head_w[bq * a.H_I + h];
-  }
-  __syncthreads();
-
-  // score the chunk
-  for (int e = tid; e < cn; e += kIdxThreads) {
-    float kv[DI];
-    decode_row<FMT>(a.keys, (int64_t)b * a.keys.cap + c0 + e, DI, kv);
-    float s = 0.0f;
-    for (int h = 0; h < a.H_I; ++h) {
-      float dot = 0.0f;
-#pragma unroll
-      for (int d = 0; d < DI; ++d) dot = fmaf(s_q[h * DI + d], kv[d], dot);
-      s = fmaf(s_w[h], fmaxf(dot, 0.0f), s);
+  if constexpr (FMT == CSA_F32) {
+    // queries and head weights
+    for (int h = tid; h < a.H_I; h += kIdxThreads) {
+      decode_row<FMT>(a.qidx, (int64_t)b * a.qidx.cap + (int64_t)q * a.H_I + h, DI, s_q + h * DI);
+      s_w[h] = a.head_w[bq * a.H_I + h];
     }
-    s_keys[e] = score_key(s);
+    __syncthreads();
+    for (int e = tid; e < cn; e += kIdxThreads) {
+      float kv[DI];
+      decode_row<FMT>(a.keys, (int64_t)b * a.keys.cap + c0 + e, DI, kv);
+      float s = 0.0f;
+      for (int h = 0; h < a.H_I; ++h) {
+        float dot = 0.0f;
+#pragma unroll
+        for (int d = 0; d < DI; ++d) dot = fmaf(s_q[h * DI + d], kv[d], dot);
+        s = fmaf(s_w[h], fmaxf(dot, 0.0f), s);
+      }
+      s_keys[e] = score_key(s);
+    }
+  } else {
+    score_chunk_mfma<FMT, DI>(a, b, q, bq, c0, cn, s_keys, s_w);
   }
   __syncthreads();
 
