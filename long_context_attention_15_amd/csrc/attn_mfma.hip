@@ -29,7 +29,7 @@ typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
 
 constexpr int kMD = 512;                 // head dim
 constexpr int kMT = 32;                  // entries per tile
-constexpr int kKsPitch = kMD + 8;        // bf16 elements per Ks row (+16 B pad)
+constexpr int kKsPitch = kMD + 16;       // bf16 elements per Ks row: 264 words, 8 mod 64 banks
 constexpr int kVtPitch = kMT + 4;        // bf16 elements per Vt row (+8 B pad)
 constexpr int kMThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
@@ -108,7 +108,7 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
   const int lane = tid & 63, wave = tid >> 6;
   const int rh = wave >> 1, dh = wave & 1;
   const int g32 = lane >> 5, l32 = lane & 31;
-  const int64_t bq = blockIdx.x;
+  const int64_t bq = xcd_remap(blockIdx.x, gridDim.x);   // query row (b * Tq + q)
   const int b = (int)(bq / a.Tq);
   const int h = blockIdx.y * 64 + rh * 32 + l32;          // this lane's head
   const int64_t t = a.q_pos ? a.q_pos[bq] : (int64_t)(bq % a.Tq);
@@ -118,14 +118,16 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
   const int64_t i1 = a.nsplit == 1 ? L : (i0 + a.split_len < L ? i0 + a.split_len : L);
   const int ntiles = i1 > i0 ? (int)((i1 - i0 + kMT - 1) / kMT) : 0;
 
-  // slot table of tile `tile` (threads < 32 own one slot each)
-  auto write_table = [&](int tile, int jsel) {
+  // slot table of tile `tile` (threads < 32 own one slot each): the row
+  // address is stored now, the row scale is loaded now and returned, to be
+  // stored one iteration later so its latency never sits on the tile loop.
+  auto table_ptr = [&](int tile, int jsel) -> float {
     int64_t row;
     const int64_t slot = i0 + (int64_t)tile * kMT + tid;
     const int src = m_slot_row(a, b, t, Lc, slot, i1, jsel, row);
     const Store& stv = src == 2 ? a.win : a.ckv;
     Tptr[tile & 3][tid] = src ? stv.rows + row * stv.row_bytes : g_zero_row;
-    Tscl[tile & 3][tid] = src ? ((const float*)stv.scales)[row] : 0.0f;
+    return src ? ((const float*)stv.scales)[row] : 0.0f;
   };
   auto sel_of = [&](int tile) -> int {
     return m_slot_sel(a, bq, Lc, i0 + (int64_t)tile * kMT + tid, i1);
@@ -158,33 +160,28 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
     *(u32x4*)(kr + 448 + 8 * sub) = *(const u32x4*)(rr + 448 + 16 * sub);
   };
 
-  // ---- prologue
-  int selreg = 0;
-  if (tid < kMT) {
-    for (int tl = 0; tl < 3; ++tl) write_table(tl, sel_of(tl));
-    selreg = sel_of(3);
-  }
-  __syncthreads();
-  if (ntiles > 0) dma_tile(0);
-  if (ntiles > 1) dma_tile(1);
   bf16x8 qf[16];
   {
     const uint16_t* qp = a.q + (bq * a.H + h) * (int64_t)kMD + dh * 256 + g32 * 8;
 #pragma unroll
     for (int s = 0; s < 16; ++s) qf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qp + 16 * s));
   }
-  CSA_WAIT_VMCNT0();
-  __syncthreads();
-  if (ntiles > 0) convert_tile(0);
-  __syncthreads();
-
   f32x16 acc[8];
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[mt][r] = 0.0f;
-  float mrun = -INFINITY, lrun = 0.0f;
   const float sc2 = a.tau * kLog2e;
+  // Softmax reference (log2 units, per head = per lane column): fixed at the
+  // head's first non-empty tile and never moved, so no VALU code ever touches
+  // the O^T accumulators.  Probabilities relative to it stay below
+  // 2^kMaxLift; if some logit climbs further (not seen with normalised
+  // inputs) the whole query is recomputed once with the exact maximum, which
+  // the first pass tracks in mmax.
+  constexpr float kMaxLift = 64.0f;
+  float mref = -INFINITY, mmax = -INFINITY, lrun = 0.0f;
+  __shared__ int s_over;
+  if (tid == 0) s_over = 0;
 
   // transposed-read addressing of V^T (see the ds_read_b64_tr_b16 lane map):
   // lane j of a 16-lane group points at entry row 4*g + (j>>2) (+8 for the
@@ -193,96 +190,117 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
   const int tr_row = 4 * g32 + (trj >> 2);
   const int tr_col = dh * 256 + 16 * trhalf + 4 * (trj & 3);
 
-  for (int it = 0; it < ntiles; ++it) {
-    const uint16_t* ks = Ks[it & 1];
-    // S^T partial over this wave's dims: two accumulators for independent chains
-    f32x16 s0, s1;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) { s0[r] = 0.0f; s1[r] = 0.0f; }
-    const uint16_t* kp = ks + l32 * kKsPitch + dh * 256 + g32 * 8;
-#pragma unroll
-    for (int s = 0; s < 16; s += 2) {
-      const bf16x8 ka = __builtin_bit_cast(bf16x8, *(const u32x4*)(kp + 16 * s));
-      const bf16x8 kb = __builtin_bit_cast(bf16x8, *(const u32x4*)(kp + 16 * (s + 1)));
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qf[s + 1], s1, 0, 0, 0);
+#pragma nounroll
+  for (int attempt = 0; attempt < 2; ++attempt) {
+    // ---- prologue: tables of tiles 0..2, rows of tiles 0 and 1, tile 0 converted
+    int selreg = 0;
+    float scl_pending = 0.0f;                       // scale of table tile it+2, stored at iteration it
+    if (tid < kMT) {
+      const int j0 = sel_of(0), j1 = sel_of(1), j2 = sel_of(2);
+      selreg = sel_of(3);
+      const float s0v = table_ptr(0, j0), s1v = table_ptr(1, j1);
+      scl_pending = table_ptr(2, j2);
+      Tscl[0][tid] = s0v;
+      Tscl[1][tid] = s1v;
     }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s0[r] += s1[r];
-      Sx[wave][r][lane] = s0[r];
-    }
-    CSA_WAIT_VMCNT0();                      // raw rows of tile it+1 and the next sel are in
-    if (tid < kMT && it + 3 < ntiles) write_table(it + 3, selreg);
-    __syncthreads();                        // B1
-    if (it + 2 < ntiles) dma_tile(it + 2);  // into Raw[it & 1], converted last iteration
-    if (tid < kMT && it + 4 < ntiles) selreg = sel_of(it + 4);
+    __syncthreads();
+    if (ntiles > 0) dma_tile(0);
+    if (ntiles > 1) dma_tile(1);
+    CSA_WAIT_VMCNT0();
+    __syncthreads();
+    if (ntiles > 0) convert_tile(0);
+    __syncthreads();
 
-    // softmax on this tile's logits
-    unsigned int vmask = 0;
-    {
-      const float sv = Tscl[it & 3][l32];
-      vmask = (unsigned int)__ballot(lane < 32 && sv > 0.0f);
-    }
-    float p[16];
-    float mt = -INFINITY;
+    for (int it = 0; it < ntiles; ++it) {
+      const uint16_t* ks = Ks[it & 1];
+      // S^T partial over this wave's dims: two accumulators for independent chains
+      f32x16 s0, s1;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int e = (r >> 2) * 8 + g32 * 4 + (r & 3);
-      const float tot = s0[r] + Sx[wave ^ 1][r][lane];
-      p[r] = ((vmask >> e) & 1u) ? tot * sc2 : -INFINITY;
-      mt = fmaxf(mt, p[r]);
-    }
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    // Lazy rescaling: the accumulator keeps its reference max mrun until a
-    // tile's max exceeds it by more than 8 (factor 256); probabilities are
-    // then at most 2^8, which float32 and bf16 hold exactly enough.  This
-    // keeps the O^T accumulators out of VALU code on almost every tile.
-    if (__ballot(mt > mrun + 8.0f)) {
-      const float mnew = fmaxf(mrun, mt);
-      const float corr = mrun > -INFINITY ? exp2f(mrun - mnew) : 0.0f;
-      if (mrun > -INFINITY) {
+      for (int r = 0; r < 16; ++r) { s0[r] = 0.0f; s1[r] = 0.0f; }
+      const uint16_t* kp = ks + l32 * kKsPitch + dh * 256 + g32 * 8;
 #pragma unroll
-        for (int mt8 = 0; mt8 < 8; ++mt8)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[mt8][r] *= corr;
+      for (int s = 0; s < 16; s += 2) {
+        const bf16x8 ka = __builtin_bit_cast(bf16x8, *(const u32x4*)(kp + 16 * s));
+        const bf16x8 kb = __builtin_bit_cast(bf16x8, *(const u32x4*)(kp + 16 * (s + 1)));
+        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qf[s + 1], s1, 0, 0, 0);
       }
-      lrun *= corr;
-      mrun = mnew;
-    }
-    float psum = 0.0f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      p[r] = mrun > -INFINITY ? exp2f(p[r] - mrun) : 0.0f;
-      psum += p[r];
-    }
-    psum += __shfl_xor(psum, 32);
-    lrun += psum;
-    bf16x8 pb0, pb1;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      pb0[r] = (__bf16)p[r];
-      pb1[r] = (__bf16)p[r + 8];
-    }
-    if (it + 1 < ntiles) convert_tile(it + 1);   // Ks[(it+1)&1] was released at the last B2
+      for (int r = 0; r < 16; ++r) {
+        s0[r] += s1[r];
+        Sx[wave][r][lane] = s0[r];
+      }
+      CSA_WAIT_VMCNT0();                    // raw rows of tile it+1, the next sel and scale are in
+      if (tid < kMT) {
+        Tscl[(it + 2) & 3][tid] = scl_pending;
+        if (it + 3 < ntiles) scl_pending = table_ptr(it + 3, selreg);
+      }
+      __syncthreads();                      // B1
+      if (it + 2 < ntiles) dma_tile(it + 2);  // into Raw[it & 1], converted last iteration
+      if (tid < kMT && it + 4 < ntiles) selreg = sel_of(it + 4);
 
-    // O^T += V^T P^T, V^T read transposed from Ks
+      // softmax on this tile's logits
+      const unsigned int vmask = (unsigned int)__ballot(lane < 32 && Tscl[it & 3][l32] > 0.0f);
+      float p[16];
+      float mt = -INFINITY;
 #pragma unroll
-    for (int mt8 = 0; mt8 < 8; ++mt8) {
-      const uint16_t* vb = ks + tr_row * kKsPitch + tr_col + 32 * mt8;
-      const v4i16 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vb));
-      const v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vb + 8 * kKsPitch));
-      const v4i16 y0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vb + 16 * kKsPitch));
-      const v4i16 y1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vb + 24 * kKsPitch));
-      const u32x2 ux0 = __builtin_bit_cast(u32x2, x0), ux1 = __builtin_bit_cast(u32x2, x1);
-      const u32x2 uy0 = __builtin_bit_cast(u32x2, y0), uy1 = __builtin_bit_cast(u32x2, y1);
-      const u32x4 v0 = u32x4{ux0.x, ux0.y, ux1.x, ux1.y};
-      const u32x4 v1 = u32x4{uy0.x, uy0.y, uy1.x, uy1.y};
-      acc[mt8] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v0), pb0, acc[mt8], 0, 0, 0);
-      acc[mt8] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v1), pb1, acc[mt8], 0, 0, 0);
+      for (int r = 0; r < 16; ++r) {
+        const int e = (r >> 2) * 8 + g32 * 4 + (r & 3);
+        const float tot = s0[r] + Sx[wave ^ 1][r][lane];
+        p[r] = ((vmask >> e) & 1u) ? tot * sc2 : -INFINITY;
+        mt = fmaxf(mt, p[r]);
+      }
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      mmax = fmaxf(mmax, mt);
+      if (mref == -INFINITY) mref = mt;     // the head's first non-empty tile
+      if (__ballot(mt > mref + kMaxLift) != 0ull && lane == 0) s_over = 1;
+      float psum = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        p[r] = mref > -INFINITY ? exp2f(p[r] - mref) : 0.0f;
+        psum += p[r];
+      }
+      psum += __shfl_xor(psum, 32);
+      lrun += psum;
+      bf16x8 pb0, pb1;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        pb0[r] = (__bf16)p[r];
+        pb1[r] = (__bf16)p[r + 8];
+      }
+      if (it + 1 < ntiles) convert_tile(it + 1);   // Ks[(it+1)&1] was released at the last B2
+
+      // O^T += V^T P^T, V^T read transposed from Ks; K-step major so that
+      // consecutive MFMAs write different accumulators
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2) {
+        const bf16x8 pb = ks2 ? pb1 : pb0;
+#pragma unroll
+        for (int mt8 = 0; mt8 < 8; ++mt8) {
+          const uint16_t* vb = ks + (tr_row + 16 * ks2) * kKsPitch + tr_col + 32 * mt8;
+          const v4i16 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vb));
+          const v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vb + 8 * kKsPitch));
+          const u32x2 ux0 = __builtin_bit_cast(u32x2, x0), ux1 = __builtin_bit_cast(u32x2, x1);
+          const u32x4 v0 = u32x4{ux0.x, ux0.y, ux1.x, ux1.y};
+          acc[mt8] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v0), pb, acc[mt8], 0, 0, 0);
+        }
+      }
+      __syncthreads();                      // B2
     }
-    __syncthreads();                        // B2
+    CSA_WAIT_VMCNT0();                      // no DMA may still target Raw
+    __syncthreads();
+    if (!s_over) break;                     // uniform
+    // recompute with the exact per-head maximum (mref >= every logit now)
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[mt][r] = 0.0f;
+    lrun = 0.0f;
+    mref = mmax;
+    __syncthreads();
+    if (tid == 0) s_over = 0;
   }
+  const float mrun = mref;
 
   // ---- epilogue
   const int64_t qoff = (bq * a.H + h) * (int64_t)kMD;

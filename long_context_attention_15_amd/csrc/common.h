@@ -118,6 +118,22 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Workgroups are dealt round-robin to the 8 XCDs (each with its own L2).
+// Map the hardware workgroup index to a logical one so that runs of G
+// consecutive logical indices (neighbouring queries, which share most of
+// their window rows and many compressed entries) execute on one XCD, while
+// the runs themselves are interleaved across XCDs so that the load stays
+// balanced when work grows with position.  A permutation of [0, n): each
+// block of 8G indices is permuted within itself, a ragged tail is identity.
+template <int G = 64>
+__device__ __forceinline__ int64_t xcd_remap(int64_t i, int64_t n) {
+  constexpr int kXcd = 8;
+  const int64_t full = n / (kXcd * G) * (kXcd * G);
+  if (i >= full) return i;
+  const int64_t x = i % kXcd, j = i / kXcd;
+  return (j / G) * (kXcd * G) + x * G + (j % G);
+}
+
 // Order-preserving uint32 key of a float score; larger key = larger score.
 // -0 is folded into +0 first.  Every finite score maps to a key >= 0x00800000,
 // so 0 is free to mark "no entry".
