@@ -143,7 +143,8 @@ csa_status csa_indexer_topk(csa_store q_idx, const float* head_w, csa_store keys
   if (n_entries < 0 || n_entries > keys.cap) return fail(CSA_EINVAL, "n_entries outside [0, keys.cap]");
   if (q_idx.cap < (int64_t)Tq * H_I) return fail(CSA_EINVAL, "q_idx.cap < Tq * H_I");
   csa::IdxPlan plan = csa::indexer_plan(B, Tq, n_entries, k);
-  if (!plan.ok) return fail(CSA_EUNSUPPORTED, "n_entries * k too large for the candidate merge");
+  if (csa::indexer_stream_ok(keys, H_I, B, Tq, n_entries, k)) plan.ws = 0;
+  else if (!plan.ok) return fail(CSA_EUNSUPPORTED, "n_entries * k too large for the candidate merge");
   if (plan.ws > 0 && (!ws || ws_bytes < plan.ws))
     return fail(CSA_EWORKSPACE, "workspace of %zu bytes needed, %zu given", plan.ws, ws ? ws_bytes : (size_t)0);
   if (plan.ws > 0 && !aligned(ws, 16)) return fail(CSA_EINVAL, "ws must be 16-byte aligned");

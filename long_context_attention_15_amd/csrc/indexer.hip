@@ -182,13 +182,27 @@ struct IdxArgs {
 
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8v;
+
+// 8 FP8 codes (one 64-bit word) -> 8 BF16 values, exact.
+__device__ __forceinline__ bf16x8v fp8x8_bf16(long long v) {
+  const uint32_t w0 = (uint32_t)v, w1 = (uint32_t)((unsigned long long)v >> 32);
+  uint4 r;
+  r.x = __builtin_bit_cast(unsigned int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
+  r.y = __builtin_bit_cast(unsigned int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
+  r.z = __builtin_bit_cast(unsigned int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
+  r.w = __builtin_bit_cast(unsigned int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
+  return __builtin_bit_cast(bf16x8v, r);
+}
 
 // Scores of entries [c0, c0 + cn) for one query on MFMA, written to s_keys.
 // Heads are the 16 rows of the A operand (H_I <= 16, the rest zero), 16
 // entries are the columns; the head-weighted ReLU sum is a lane-local sum
 // over 4 heads plus two cross-lane adds.
-//   FP8  : v_mfma_f32_16x16x32_fp8_fp8; the row scales of q fold into the
-//          head weights, the key scale multiplies the sum (powers of two).
+//   FP8  : the codes convert exactly to BF16 for v_mfma_f32_16x16x32_bf16,
+//          whose float32 sums keep float32 accuracy (the FP8 MFMAs sum their
+//          products less precisely); the row scales of q fold into the head
+//          weights, the key scale multiplies the sum (powers of two).
 //   MXFP4: v_mfma_scale_f32_16x16x128_f8f6f4 with E2M1 operands and the
 //          per-32-element E8M0 scales applied by the instruction; k-blocks
 //          beyond d_I are zero.
@@ -228,6 +242,7 @@ __device__ __forceinline__ void score_chunk_mfma(const IdxArgs& a, int b, int q,
         qa0 = (long long)(((unsigned long long)v.y << 32) | v.x);
       }
     }
+    const bf16x8v qb0 = fp8x8_bf16(qa0), qb1 = fp8x8_bf16(qa1);
     const float* ksc = (const float*)a.keys.scales;
     constexpr int U = 8;                    // groups in flight per wave
     for (int grp0 = wave * U; grp0 < ngroups; grp0 += kIdxWaves * U) {
@@ -254,8 +269,8 @@ __device__ __forceinline__ void score_chunk_mfma(const IdxArgs& a, int b, int q,
       for (int u = 0; u < U; ++u) {
         const int e = (grp0 + u) * 16 + col;
         f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
-        c = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(qa0, kb0[u], c, 0, 0, 0);
-        if (DI == 64) c = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(qa1, kb1[u], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qb0, fp8x8_bf16(kb0[u]), c, 0, 0, 0);
+        if (DI == 64) c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qb1, fp8x8_bf16(kb1[u]), c, 0, 0, 0);
         float v = 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) v = fmaf(wl[i], fmaxf(c[i], 0.0f), v);
@@ -398,6 +413,472 @@ __global__ __launch_bounds__(kIdxThreads) void idx_merge_kernel(IdxArgs a) {
   emit_selected(s_keys, n, thr, need_eq, sh, [&](int pos, int rank) { out[rank] = ci[pos]; });
 }
 
+// ------------------------------------------------- streaming top-k (prefill)
+//
+// Many queries, FP8 keys of 64 dims, at most 8 heads: a workgroup owns 16
+// consecutive queries (4 per wavefront) and streams their visible entries in
+// ascending index order through LDS, 128 entries at a time, shared by all
+// four wavefronts.  Scores come from v_mfma_f32_32x32x16_bf16 with the 32
+// rows = 4 queries x 8 heads and 32 entries as columns (FP8 codes convert to
+// BF16 exactly; the products and their float32 sums are as accurate as a
+// float32 dot product).  Each query keeps a candidate list in LDS (entry
+// order, so index order) and a threshold: an entry is appended when its
+// score beats the threshold.  When a list is nearly full it is compacted:
+// one radix digit of the keys locates a bound L with at least k keys >= L;
+// the keys >= L stay and the threshold becomes L, which is safe because each
+// later entry with a key <= L ranks below at least k kept ones (larger key,
+// or equal key and smaller index).  If that bound keeps too much (heavy
+// ties) the exact k-th key is found instead and only the k best stay.  At the
+// end an exact radix select over the list gives the top-k, emitted in list
+// order = ascending index.  No workspace, one pass over the keys.
+constexpr int kSThreads = 256;
+constexpr int kSWaves = kSThreads / kWave;
+constexpr int kSQW = 4;                   // queries per wavefront
+constexpr int kSQ = kSWaves * kSQW;       // queries per workgroup
+constexpr int kSCap = 1024;               // candidate slots per query
+constexpr int kSSlots = kSCap / kWave;    // list slots per lane when a list is in registers
+constexpr int kSChunk = 128;              // entries per LDS stage
+constexpr int kSRow = 128;                // BF16 key row in LDS (64 dims)
+constexpr int kSStep = 64;                // entries per loop iteration (two MFMA column blocks)
+constexpr int kSKeep = kSCap - 256;       // a compaction must leave at most this many
+constexpr int kStreamMaxK = 768;
+constexpr int64_t kStreamMaxN = 65536;    // candidate indices are 16-bit
+constexpr int64_t kStreamMinQueries = 2048;
+
+struct StreamLds {
+  uint32_t ckey[kSQ][kSCap];
+  uint16_t cidx[kSQ][kSCap];
+  uint8_t kb[2][kSChunk * kSRow];
+  float ks[2][kSChunk];
+  uint32_t hist[kSWaves][256];
+};
+
+typedef __attribute__((ext_vector_type(8))) __bf16 sbf16x8;
+typedef __attribute__((ext_vector_type(16))) float sf32x16;
+
+// 8 FP8 codes (two words) -> 8 BF16 values, exact.
+__device__ __forceinline__ uint4 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
+  uint4 r;
+  r.x = __builtin_bit_cast(unsigned int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
+  r.y = __builtin_bit_cast(unsigned int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
+  r.z = __builtin_bit_cast(unsigned int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
+  r.w = __builtin_bit_cast(unsigned int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
+  return r;
+}
+
+// LDS accesses of this wavefront issued so far complete before later ones.
+__device__ __forceinline__ void lds_wave_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// max(x, 0) on the bit pattern: negative floats (and -0) become +0.
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// Float threshold equivalent to "key > thr" for every finite score.
+__device__ __forceinline__ float thr_float(uint32_t thr) {
+  if (thr < 0x007fffffu) return -INFINITY;
+  const float f = key_score(thr);
+  return (__float_as_uint(f) == 0x80000000u) ? -1.4e-45f : f;
+}
+
+// A candidate list held in registers: lane l owns positions 64 j + l; key 0
+// marks an empty slot (every real key is nonzero).
+struct RegList {
+  uint32_t key[kSSlots];
+  uint32_t id[kSSlots];
+};
+
+__device__ __forceinline__ void list_load(const uint32_t* keys, const uint16_t* ids, int n, RegList& r) {
+  const int lane = threadIdx.x % kWave;
+#pragma unroll
+  for (int j = 0; j < kSSlots; ++j) {
+    const int pos = kWave * j + lane;
+    r.key[j] = pos < n ? keys[pos] : 0u;
+    r.id[j] = pos < n ? (uint32_t)ids[pos] : 0u;
+  }
+}
+
+__device__ __forceinline__ void list_minmax(const RegList& r, uint32_t& kmin, uint32_t& kmax) {
+  uint32_t lo = 0xffffffffu, hi = 0u;
+#pragma unroll
+  for (int j = 0; j < kSSlots; ++j) {
+    const uint32_t k = r.key[j];
+    lo = (k != 0u && k < lo) ? k : lo;
+    hi = k > hi ? k : hi;
+  }
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) {
+    const uint32_t a = __shfl_xor(lo, o), b = __shfl_xor(hi, o);
+    lo = a < lo ? a : lo;
+    hi = b > hi ? b : hi;
+  }
+  kmin = lo;
+  kmax = hi;
+}
+
+// One 8-bit radix digit over the list's keys restricted to (key & mask) ==
+// prefix: the digit value `bin` holding the need-th largest key, the number
+// of keys in higher digits (`above`) and in that digit (`inbin`).
+__device__ void list_digit(const RegList& r, uint32_t prefix, uint32_t mask, int shift, int need, uint32_t* hist,
+                           int& bin, int& above, int& inbin) {
+  const int lane = threadIdx.x % kWave;
+  *(uint4*)(hist + 4 * lane) = make_uint4(0u, 0u, 0u, 0u);
+  lds_wave_sync();
+#pragma unroll
+  for (int j = 0; j < kSSlots; ++j) {
+    const uint32_t k = r.key[j];
+    if (k != 0u && (k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
+  }
+  lds_wave_sync();
+  const uint4 h = *(const uint4*)(hist + 4 * lane);
+  const int local = (int)(h.x + h.y + h.z + h.w);
+  int suf = local;                                    // keys in bins >= 4 * lane
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int t = __shfl_down(suf, o);
+    if (lane + o < kWave) suf += t;
+  }
+  const int ab = suf - local;
+  const uint64_t hit = __ballot(ab < need && suf >= need);
+  const int L = __ffsll((unsigned long long)hit) - 1;
+  int a = __builtin_amdgcn_readlane(ab, L);
+  const int c[4] = {(int)__builtin_amdgcn_readlane(h.x, L), (int)__builtin_amdgcn_readlane(h.y, L),
+                    (int)__builtin_amdgcn_readlane(h.z, L), (int)__builtin_amdgcn_readlane(h.w, L)};
+  int b = 0, cb = 0;
+#pragma unroll
+  for (int j = 3; j >= 0; --j) {
+    if (a + c[j] >= need) { b = j; cb = c[j]; break; }
+    a += c[j];
+  }
+  bin = 4 * L + b;
+  above = a;
+  inbin = cb;
+}
+
+// Exact select: the kk-th largest key T of the list and how many keys equal
+// to T are taken (the first ones by position).  1 <= kk <= length.
+__device__ void list_select(const RegList& r, int kk, uint32_t* hist, uint32_t& T, int& need_eq) {
+  uint32_t kmin, kmax;
+  list_minmax(r, kmin, kmax);
+  if (kmin == kmax) { T = kmin; need_eq = kk; return; }
+  int hb = 31 - __builtin_clz(kmin ^ kmax);           // highest differing bit
+  uint32_t mask = hb == 31 ? 0u : ~((2u << hb) - 1u);
+  uint32_t prefix = kmax & mask;
+  int need = kk;
+  while (true) {
+    const int shift = hb >= 7 ? hb - 7 : 0;
+    int bin, above, inbin;
+    list_digit(r, prefix, mask, shift, need, hist, bin, above, inbin);
+    prefix |= (uint32_t)bin << shift;
+    mask |= 255u << shift;
+    need -= above;
+    if (shift == 0) break;
+    hb = shift - 1;
+  }
+  T = prefix;
+  need_eq = need;
+}
+
+// Rewrite the list with the entries of key > T plus the first need_eq of
+// key == T, in order; returns the new length.
+__device__ int list_store_kept(const RegList& r, uint32_t T, int need_eq, uint32_t* keys, uint16_t* ids) {
+  const int lane = threadIdx.x % kWave;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int out = 0, eqs = 0;
+#pragma unroll
+  for (int j = 0; j < kSSlots; ++j) {
+    const uint32_t k = r.key[j];
+    const bool eq = k != 0u && k == T;
+    const uint64_t beq = __ballot(eq);
+    const bool keep = (k != 0u && k > T) || (eq && eqs + __popcll(beq & lt) < need_eq);
+    const uint64_t bk = __ballot(keep);
+    if (keep) {
+      const int d = out + __popcll(bk & lt);
+      keys[d] = k;
+      ids[d] = (uint16_t)r.id[j];
+    }
+    out += __popcll(bk);
+    eqs += __popcll(beq);
+  }
+  lds_wave_sync();
+  return __builtin_amdgcn_readfirstlane(out);
+}
+
+// Mid-stream compaction of one query's list (n > k): returns the new length
+// and raises thr (a strict bound: later entries need key > thr).
+__device__ int list_shrink(uint32_t* keys, uint16_t* ids, int n, int k, uint32_t* hist, uint32_t& thr) {
+  RegList r;
+  list_load(keys, ids, n, r);
+  uint32_t kmin, kmax;
+  list_minmax(r, kmin, kmax);
+  if (kmin != kmax) {
+    const int hb = 31 - __builtin_clz(kmin ^ kmax);
+    const uint32_t mask = hb == 31 ? 0u : ~((2u << hb) - 1u);
+    const int shift = hb >= 7 ? hb - 7 : 0;
+    int bin, above, inbin;
+    list_digit(r, kmax & mask, mask, shift, k, hist, bin, above, inbin);
+    const uint32_t L = (kmax & mask) | ((uint32_t)bin << shift);
+    if (L > 0u && above + inbin <= kSKeep) {
+      thr = L > thr ? L : thr;
+      return list_store_kept(r, L - 1u, 0, keys, ids);
+    }
+  }
+  uint32_t T;
+  int need_eq;
+  list_select(r, k, hist, T, need_eq);
+  thr = T > thr ? T : thr;
+  return list_store_kept(r, T, need_eq, keys, ids);
+}
+
+struct StreamArgs {
+  Store qidx, keys;
+  const float* head_w;
+  int64_t n_entries;
+  const int64_t* q_pos;
+  int B, Tq, H_I, m, k, ngroups;
+  int32_t* sel;
+};
+
+__global__ __launch_bounds__(kSThreads, 1) void idx_stream_kernel(StreamArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t s_raw[];
+  StreamLds& S = *reinterpret_cast<StreamLds*>(s_raw);
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int g = lane >> 5, l32 = lane & 31;
+  // heaviest groups (latest queries) first
+  const int b = blockIdx.x / a.ngroups;
+  const int grp = a.ngroups - 1 - (int)(blockIdx.x % a.ngroups);
+  const int q0 = grp * kSQ;
+
+  // visible entries of every query of the workgroup; the stream runs to the largest
+  auto visible = [&](int q) -> int {
+    if (q >= a.Tq) return 0;
+    const int64_t bq = (int64_t)b * a.Tq + q;
+    const int64_t t = a.q_pos ? a.q_pos[bq] : (int64_t)q;
+    const int64_t nt = t < 0 ? 0 : (t + 1) / a.m;
+    return (int)(nt < a.n_entries ? nt : a.n_entries);
+  };
+  int nmax = 0;
+  for (int j = 0; j < kSQ; ++j) nmax = max(nmax, visible(q0 + j));
+  int ntq[kSQW];
+  int ntw = 0;                                      // the largest of this wavefront's queries
+#pragma unroll
+  for (int qq = 0; qq < kSQW; ++qq) {
+    ntq[qq] = visible(q0 + wave * kSQW + qq);
+    ntw = max(ntw, ntq[qq]);
+  }
+
+  // A operand: rows = (query r >> 3, head r & 7); K-step j covers dims [16 j + 8 g, +8)
+  sbf16x8 qa[4];
+  {
+    const int qq = l32 >> 3, h = l32 & 7, q = q0 + wave * kSQW + qq;
+    const bool ok = q < a.Tq && h < a.H_I;
+    const uint8_t* qp = a.qidx.rows + ((int64_t)b * a.qidx.cap + (int64_t)(ok ? q : 0) * a.H_I + (ok ? h : 0)) *
+                                          a.qidx.row_bytes;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint2 v = ok ? *(const uint2*)(qp + 16 * j + 8 * g) : make_uint2(0u, 0u);
+      qa[j] = __builtin_bit_cast(sbf16x8, fp8x8_to_bf16(v.x, v.y));
+    }
+  }
+  // head weights of this lane's accumulator rows (query r >> 2, head 4 g + (r & 3)),
+  // with the query row scales folded in
+  float wl[kSQW][4];
+#pragma unroll
+  for (int qq = 0; qq < kSQW; ++qq)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int q = q0 + wave * kSQW + qq, h = 4 * g + i;
+      float w = 0.0f;
+      if (q < a.Tq && h < a.H_I) {
+        const int64_t bq = (int64_t)b * a.Tq + q;
+        w = a.head_w[bq * a.H_I + h] *
+            ((const float*)a.qidx.scales)[(int64_t)b * a.qidx.cap + (int64_t)q * a.H_I + h];
+      }
+      wl[qq][i] = w;
+    }
+
+  // lanes < 32 score queries 0 and 2 of the wave, lanes >= 32 queries 1 and 3
+  const int qA = g, qB = 2 + g;
+  const int ntA = g ? ntq[1] : ntq[0], ntB = g ? ntq[3] : ntq[2];
+  uint32_t thr[kSQW] = {0u, 0u, 0u, 0u};
+  int cnt[kSQW] = {0, 0, 0, 0};
+  float thrA = -INFINITY, thrB = -INFINITY;
+  uint32_t* ck = &S.ckey[wave * kSQW][0];
+  uint16_t* ci = &S.cidx[wave * kSQW][0];
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const uint64_t half = g ? 0xffffffff00000000ull : 0x00000000ffffffffull;
+
+  // staging: thread -> (entry tid >> 1, bytes [32 (tid & 1), +32) of its FP8 row);
+  // chunk c + 2 is loaded while chunk c is scored, chunk c + 1 is stored after it
+  const int sk_e = tid >> 1, sk_h = tid & 1;
+  const int64_t krow0 = (int64_t)b * a.keys.cap;
+  const int nchunks = (nmax + kSChunk - 1) / kSChunk;
+  struct Stage { uint4 w0, w1; float sc; };
+  auto stage_load = [&](int c, Stage& st) {
+    const int e = min(c * kSChunk + sk_e, nmax - 1);
+    const uint8_t* kp = a.keys.rows + (krow0 + e) * a.keys.row_bytes + 32 * sk_h;
+    st.w0 = *(const uint4*)kp;
+    st.w1 = *(const uint4*)(kp + 16);
+    st.sc = 0.0f;
+    if (tid < kSChunk) st.sc = ((const float*)a.keys.scales)[krow0 + min(c * kSChunk + tid, nmax - 1)];
+  };
+  // logical 16-byte unit u (dims [8 u, 8 u + 8)) of entry e sits at unit u ^ ((e >> 1) & 7)
+  auto stage_store = [&](int c, const Stage& st) {
+    uint8_t* dst = S.kb[c & 1] + sk_e * kSRow;
+    const int sw = (sk_e >> 1) & 7;
+    const uint32_t w[8] = {st.w0.x, st.w0.y, st.w0.z, st.w0.w, st.w1.x, st.w1.y, st.w1.z, st.w1.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int u = 4 * sk_h + j;
+      *(uint4*)(dst + 16 * (u ^ sw)) = fp8x8_to_bf16(w[2 * j], w[2 * j + 1]);
+    }
+    if (tid < kSChunk) S.ks[c & 1][tid] = st.sc;
+  };
+
+  // scores of the 32 entries at chunk offset ke0 + l32 for this lane's two queries
+  auto score = [&](const uint8_t* kb, const float* ksc, int ke0, float& sA, float& sB) {
+    const int ke = ke0 + l32;
+    const uint8_t* kr = kb + ke * kSRow;
+    const int sw = (ke >> 1) & 7;
+    sf32x16 acc;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint4 v = *(const uint4*)(kr + 16 * ((2 * j + g) ^ sw));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[j], __builtin_bit_cast(sbf16x8, v), acc, 0, 0, 0);
+    }
+    const float sk = ksc[ke];
+    float p[kSQW];
+#pragma unroll
+    for (int qq = 0; qq < kSQW; ++qq) {
+      float v = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v = fmaf(wl[qq][i], relu_bits(acc[4 * qq + i]), v);
+      p[qq] = v;
+    }
+    const auto r01 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0]), __float_as_uint(p[1]), false, false);
+    const auto r23 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[2]), __float_as_uint(p[3]), false, false);
+    sA = (__uint_as_float(r01[0]) + __uint_as_float(r01[1])) * sk;
+    sB = (__uint_as_float(r23[0]) + __uint_as_float(r23[1])) * sk;
+  };
+  // append the passing entries of one 32-entry block (entry index e for this lane)
+  auto append = [&](uint64_t mA, uint64_t mB, float sA, float sB, int e) {
+    if (mA & (1ull << lane)) {
+      const int d = (g ? cnt[1] : cnt[0]) + __popcll(mA & lt & half);
+      ck[qA * kSCap + d] = score_key(sA);
+      ci[qA * kSCap + d] = (uint16_t)e;
+    }
+    if (mB & (1ull << lane)) {
+      const int d = (g ? cnt[3] : cnt[2]) + __popcll(mB & lt & half);
+      ck[qB * kSCap + d] = score_key(sB);
+      ci[qB * kSCap + d] = (uint16_t)e;
+    }
+    cnt[0] += __popcll(mA & 0xffffffffull);
+    cnt[1] += __popcll(mA >> 32);
+    cnt[2] += __popcll(mB & 0xffffffffull);
+    cnt[3] += __popcll(mB >> 32);
+  };
+
+  Stage nxt, far;
+  if (nchunks > 0) {
+    stage_load(0, nxt);
+    stage_store(0, nxt);
+  }
+  if (nchunks > 1) stage_load(1, nxt);
+  __syncthreads();
+
+  for (int c = 0; c < nchunks; ++c) {
+    if (c + 2 < nchunks) stage_load(c + 2, far);
+    const uint8_t* kb = S.kb[c & 1];
+    const float* ksc = S.ks[c & 1];
+    for (int s = 0; s < kSChunk / kSStep; ++s) {
+      const int e0 = c * kSChunk + kSStep * s;
+      if (e0 >= ntw) break;                                        // uniform per wave
+      // room for one more iteration of appends in every list
+      bool shrunk = false;
+#pragma unroll
+      for (int qq = 0; qq < kSQW; ++qq) {
+        if (cnt[qq] > kSCap - kSStep) {                              // uniform
+          cnt[qq] = list_shrink(ck + qq * kSCap, ci + qq * kSCap, cnt[qq], a.k, S.hist[wave], thr[qq]);
+          shrunk = true;
+        }
+      }
+      if (shrunk) {
+        thrA = thr_float(g ? thr[1] : thr[0]);
+        thrB = thr_float(g ? thr[3] : thr[2]);
+      }
+      float sA0, sB0, sA1, sB1;
+      score(kb, ksc, kSStep * s, sA0, sB0);
+      score(kb, ksc, kSStep * s + 32, sA1, sB1);
+      const int e = e0 + l32;
+      const uint64_t mA0 = __ballot(e < ntA && sA0 > thrA), mB0 = __ballot(e < ntB && sB0 > thrB);
+      const uint64_t mA1 = __ballot(e + 32 < ntA && sA1 > thrA), mB1 = __ballot(e + 32 < ntB && sB1 > thrB);
+      if ((mA0 | mB0 | mA1 | mB1) != 0ull) {
+        append(mA0, mB0, sA0, sB0, e);
+        append(mA1, mB1, sA1, sB1, e + 32);
+#pragma unroll
+        for (int qq = 0; qq < kSQW; ++qq) cnt[qq] = __builtin_amdgcn_readfirstlane(cnt[qq]);
+      }
+    }
+    if (c + 1 < nchunks) stage_store(c + 1, nxt);
+    nxt = far;
+    __syncthreads();
+  }
+  lds_wave_sync();
+
+  // final exact top-k of each list, emitted in list order (ascending index)
+#pragma unroll
+  for (int qq = 0; qq < kSQW; ++qq) {
+    const int q = q0 + wave * kSQW + qq;
+    if (q >= a.Tq) continue;                                        // uniform
+    int32_t* out = a.sel + ((int64_t)b * a.Tq + q) * a.k;
+    const int n = cnt[qq];
+    const int kk = n < a.k ? n : a.k;
+    for (int i = kk + lane; i < a.k; i += kWave) out[i] = -1;
+    if (kk == 0) continue;
+    const uint32_t* keys = ck + qq * kSCap;
+    const uint16_t* ids = ci + qq * kSCap;
+    if (n <= a.k) {
+      for (int i = lane; i < n; i += kWave) out[i] = (int32_t)ids[i];
+      continue;
+    }
+    RegList r;
+    list_load(keys, ids, n, r);
+    uint32_t T;
+    int need_eq;
+    list_select(r, kk, S.hist[wave], T, need_eq);
+    int outn = 0, eqs = 0;
+#pragma unroll
+    for (int j = 0; j < kSSlots; ++j) {
+      const uint32_t k = r.key[j];
+      const bool eq = k != 0u && k == T;
+      const uint64_t beq = __ballot(eq);
+      const bool take = (k != 0u && k > T) || (eq && eqs + __popcll(beq & lt) < need_eq);
+      const uint64_t bt = __ballot(take);
+      if (take) out[outn + __popcll(bt & lt)] = (int32_t)r.id[j];
+      outn += __popcll(bt);
+      eqs += __popcll(beq);
+    }
+  }
+}
+
+bool indexer_stream_ok(const csa_store& keys, int H_I, int B, int Tq, int64_t n_entries, int k) {
+  return keys.fmt == CSA_FP8_E4M3 && keys.dim == 64 && keys.row_bytes == 64 && H_I <= 8 && k <= kStreamMaxK &&
+         n_entries <= kStreamMaxN && (int64_t)B * Tq >= kStreamMinQueries;
+}
+
+static hipError_t launch_idx_stream(const IdxArgs& ia, hipStream_t st) {
+  StreamArgs a;
+  a.qidx = ia.qidx; a.keys = ia.keys; a.head_w = ia.head_w; a.n_entries = ia.n_entries; a.q_pos = ia.q_pos;
+  a.B = ia.B; a.Tq = ia.Tq; a.H_I = ia.H_I; a.m = ia.m; a.k = ia.k; a.sel = ia.sel;
+  a.ngroups = (ia.Tq + kSQ - 1) / kSQ;
+  const size_t lds = sizeof(StreamLds);
+  hipError_t e = hipFuncSetAttribute((const void*)idx_stream_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(idx_stream_kernel, dim3((unsigned)((int64_t)a.B * a.ngroups)), dim3(kSThreads), lds, st, a);
+  return hipGetLastError();
+}
+
 IdxPlan indexer_plan(int B, int Tq, int64_t n_entries, int k) {
   IdxPlan p{0, 0, 0, false};
   if (n_entries <= 0) { p.chunk = 1024; p.nchunk = 1; p.ok = true; return p; }
@@ -450,6 +931,7 @@ hipError_t launch_indexer(const csa_store& qidx, const float* head_w, const csa_
   a.ws_key = (uint32_t*)ws;
   a.ws_idx = (int32_t*)((uint8_t*)ws + half);
   if ((int64_t)B * Tq == 0) return hipSuccess;
+  if (indexer_stream_ok(keys, H_I, B, Tq, n_entries, k)) return launch_idx_stream(a, st);
   const int d = keys.dim;
   switch (keys.fmt) {
     case CSA_F32: return d == 32 ? launch_idx_t<CSA_F32, 32>(a, st) : launch_idx_t<CSA_F32, 64>(a, st);

@@ -22,6 +22,9 @@ struct IdxPlan {
   bool ok;
 };
 IdxPlan indexer_plan(int B, int Tq, int64_t n_entries, int k);
+// Many queries over FP8 keys of 64 dims: the single-pass streaming top-k,
+// which needs no workspace.
+bool indexer_stream_ok(const csa_store& keys, int H_I, int B, int Tq, int64_t n_entries, int k);
 hipError_t launch_indexer(const csa_store& qidx, const float* head_w, const csa_store& keys,
                           int64_t n_entries, const int64_t* q_pos, int B, int Tq, int H_I, int m,
                           int k, int32_t* sel, void* ws, const IdxPlan& plan, hipStream_t st);

@@ -166,6 +166,51 @@ def test_indexer_exact_ties_go_to_the_smaller_index(lib):
         assert np.array_equal(sel[0, i], want), f"query {i}"
 
 
+@pytest.mark.parametrize("B,Tq,N,H_I,k", [(2, 2050, 20000, 8, 512), (1, 2048, 9000, 6, 700)])
+def test_indexer_stream_long_lists(lib, B, Tq, N, H_I, k):
+    """Many queries over FP8 keys: the single-pass streaming selection, with
+    query positions spread over the whole cache so that the candidate lists
+    are compacted many times; a ragged last group of queries; fewer than 8
+    heads."""
+    d_I, m = 64, 4
+    kst, kdeq, qst, qdeq, w = _indexer_inputs(B, Tq, N, H_I, d_I, "fp8", seed_shift=3)
+    rng = np.random.default_rng(5)
+    pos = [sorted(rng.integers(-3, m * N + 50, Tq).tolist()) for _ in range(B)]
+    for b in range(B):
+        pos[b][0], pos[b][1], pos[b][-1] = 0, m * k - 1, m * N + 9
+    sel = _run_indexer(lib, kst, qst, w, N, pos, B, Tq, H_I, m, k)
+    rows = sorted(set(range(0, Tq, 41)) | {0, 1, Tq - 2, Tq - 1})
+    flips = 0
+    for b in range(B):
+        flips += _check_indexer(sel[b:b + 1, rows], kdeq[b:b + 1], qdeq[b:b + 1, rows], w[b:b + 1, rows], N, m, k,
+                                [[pos[b][r] for r in rows]])
+    assert flips <= max(2, len(rows) * k // 2000)
+
+
+@pytest.mark.parametrize("k", [200, 512])
+def test_indexer_stream_exact_ties(lib, k):
+    """Streaming selection with integer-valued queries/keys and w = 1: the
+    scores are exact on both sides and tie massively (exact zeros included),
+    so every selected set must equal the oracle's, smaller index first."""
+    B, Tq, N, H_I, d_I, m = 1, 2048, 3000, 8, 64, 4
+    rng = np.random.default_rng(12)
+    keys = rng.integers(-2, 3, (B, N, d_I)).astype(np.float64)
+    keys[:, :, 0] = 2.0
+    q = rng.integers(-1, 2, (B, Tq * H_I, d_I)).astype(np.float64)
+    q[:, :, 1] = 1.0
+    w = np.ones((B, Tq, H_I), np.float32)
+    kst, kdeq = Hx.upload_store(keys, "fp8")
+    qst, qdeq = Hx.upload_store(q, "fp8")
+    assert np.array_equal(kdeq, keys) and np.array_equal(qdeq, q)
+    pos = [sorted(rng.integers(0, m * N + 8, Tq).tolist())]
+    sel = _run_indexer(lib, kst, qst, w, N, pos, B, Tq, H_I, m, k)
+    qd = q.reshape(B, Tq, H_I, d_I)
+    for i in range(Tq):
+        nt = int(O.n_visible(pos[0][i], m, N))
+        want = O.topk_select(O.indexer_scores(qd[0, i], w[0, i], keys[0, :nt]), k)
+        assert np.array_equal(sel[0, i], want), f"query {i} at {pos[0][i]}"
+
+
 def test_indexer_no_visible_entries_and_k_above_count(lib):
     B, T, N, H_I, d_I, m, k = 1, 40, 10, 2, 64, 4, 16
     kst, kdeq, qst, qdeq, w = _indexer_inputs(B, T, N, H_I, d_I, "fp8", seed_shift=2)
