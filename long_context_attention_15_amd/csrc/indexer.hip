@@ -440,14 +440,16 @@ constexpr int kSSlots = kSCap / kWave;    // list slots per lane when a list is 
 constexpr int kSChunk = 128;              // entries per LDS stage
 constexpr int kSRow = 128;                // BF16 key row in LDS (64 dims)
 constexpr int kSStep = 64;                // entries per loop iteration (two MFMA column blocks)
-constexpr int kSKeep = kSCap - 256;       // a compaction must leave at most this many
-constexpr int kStreamMaxK = 768;
+constexpr int kSSlack = 96;               // a compaction keeps at most k + kSSlack entries
+constexpr int kStreamMaxK = kSCap - kSSlack - 2 * 64;
 constexpr int64_t kStreamMaxN = 65536;    // candidate indices are 16-bit
 constexpr int64_t kStreamMinQueries = 2048;
 
+constexpr int kSRowCap = kSCap + kWave;   // list slots + one spare slot per lane
+
 struct StreamLds {
-  uint32_t ckey[kSQ][kSCap];
-  uint16_t cidx[kSQ][kSCap];
+  uint32_t ckey[kSQ][kSRowCap];
+  uint16_t cidx[kSQ][kSRowCap];
   uint8_t kb[2][kSChunk * kSRow];
   float ks[2][kSChunk];
   uint32_t hist[kSWaves][256];
@@ -469,8 +471,42 @@ __device__ __forceinline__ uint4 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
 // LDS accesses of this wavefront issued so far complete before later ones.
 __device__ __forceinline__ void lds_wave_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
+// Wave-wide inclusive prefix sum / max / min in registers with DPP row
+// shifts and row broadcasts (no LDS round trips).  Lane 63 ends with the
+// total.
+template <int OP>   // 0: add, 1: max (unsigned), 2: min (unsigned)
+__device__ __forceinline__ uint32_t dpp_op(uint32_t a, uint32_t b) {
+  return OP == 0 ? a + b : (OP == 1 ? (a > b ? a : b) : (a < b ? a : b));
+}
+template <int OP>
+__device__ __forceinline__ uint32_t wave_scan(uint32_t x) {
+  constexpr uint32_t id = OP == 2 ? 0xffffffffu : 0u;
+  x = dpp_op<OP>(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x111, 0xf, 0xf, false));  // row_shr:1
+  x = dpp_op<OP>(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x112, 0xf, 0xf, false));  // row_shr:2
+  x = dpp_op<OP>(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x114, 0xf, 0xf, false));  // row_shr:4
+  x = dpp_op<OP>(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x118, 0xf, 0xf, false));  // row_shr:8
+  x = dpp_op<OP>(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  x = dpp_op<OP>(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return x;
+}
+template <int OP>
+__device__ __forceinline__ uint32_t wave_total(uint32_t x) {
+  return __builtin_amdgcn_readlane(wave_scan<OP>(x), 63);
+}
+
 // max(x, 0) on the bit pattern: negative floats (and -0) become +0.
 __device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// base + the number of set bits of m below this lane.
+__device__ __forceinline__ int lane_rank(uint64_t m, int base) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, (uint32_t)base));
+}
+
+// score_key with the sign flip done arithmetically (adding +0 first folds -0).
+__device__ __forceinline__ uint32_t key_of(float s) {
+  const uint32_t u = __float_as_uint(s + 0.0f);
+  return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+}
 
 // Float threshold equivalent to "key > thr" for every finite score.
 __device__ __forceinline__ float thr_float(uint32_t thr) {
@@ -504,14 +540,8 @@ __device__ __forceinline__ void list_minmax(const RegList& r, uint32_t& kmin, ui
     lo = (k != 0u && k < lo) ? k : lo;
     hi = k > hi ? k : hi;
   }
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) {
-    const uint32_t a = __shfl_xor(lo, o), b = __shfl_xor(hi, o);
-    lo = a < lo ? a : lo;
-    hi = b > hi ? b : hi;
-  }
-  kmin = lo;
-  kmax = hi;
+  kmin = wave_total<2>(lo);
+  kmax = wave_total<1>(hi);
 }
 
 // One 8-bit radix digit over the list's keys restricted to (key & mask) ==
@@ -528,16 +558,13 @@ __device__ void list_digit(const RegList& r, uint32_t prefix, uint32_t mask, int
     if (k != 0u && (k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
   }
   lds_wave_sync();
-  const uint4 h = *(const uint4*)(hist + 4 * lane);
+  // lane l holds bins [4 (63 - l), +4): a prefix scan over lanes counts the
+  // keys in this lane's bins and all higher ones
+  const uint4 h = *(const uint4*)(hist + 4 * (kWave - 1 - lane));
   const int local = (int)(h.x + h.y + h.z + h.w);
-  int suf = local;                                    // keys in bins >= 4 * lane
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int t = __shfl_down(suf, o);
-    if (lane + o < kWave) suf += t;
-  }
-  const int ab = suf - local;
-  const uint64_t hit = __ballot(ab < need && suf >= need);
+  const int incl = (int)wave_scan<0>((uint32_t)local);
+  const int ab = incl - local;
+  const uint64_t hit = __ballot(ab < need && incl >= need);
   const int L = __ffsll((unsigned long long)hit) - 1;
   int a = __builtin_amdgcn_readlane(ab, L);
   const int c[4] = {(int)__builtin_amdgcn_readlane(h.x, L), (int)__builtin_amdgcn_readlane(h.y, L),
@@ -548,26 +575,34 @@ __device__ void list_digit(const RegList& r, uint32_t prefix, uint32_t mask, int
     if (a + c[j] >= need) { b = j; cb = c[j]; break; }
     a += c[j];
   }
-  bin = 4 * L + b;
+  bin = 4 * (kWave - 1 - L) + b;
   above = a;
   inbin = cb;
 }
 
-// Exact select: the kk-th largest key T of the list and how many keys equal
-// to T are taken (the first ones by position).  1 <= kk <= length.
-__device__ void list_select(const RegList& r, int kk, uint32_t* hist, uint32_t& T, int& need_eq) {
+// A cut of the list that keeps every entry of its top kk: the entries with
+// key > T plus the first need_eq entries with key == T.  Radix digits of 8
+// bits are resolved from the highest bit in which the keys differ; the walk
+// stops as soon as the digit bin holding the kk-th key brings the kept count
+// to at most kk + slack (then T = bin lower bound - 1 and need_eq = 0: all
+// keys >= the bound stay); otherwise it runs to the last bit and the cut is
+// exact (kept == kk).  1 <= kk <= length.
+__device__ void list_cut(const RegList& r, int kk, int slack, uint32_t* hist, uint32_t& T, int& need_eq) {
   uint32_t kmin, kmax;
   list_minmax(r, kmin, kmax);
   if (kmin == kmax) { T = kmin; need_eq = kk; return; }
   int hb = 31 - __builtin_clz(kmin ^ kmax);           // highest differing bit
   uint32_t mask = hb == 31 ? 0u : ~((2u << hb) - 1u);
   uint32_t prefix = kmax & mask;
-  int need = kk;
+  int need = kk, above_all = 0;
   while (true) {
     const int shift = hb >= 7 ? hb - 7 : 0;
     int bin, above, inbin;
     list_digit(r, prefix, mask, shift, need, hist, bin, above, inbin);
-    prefix |= (uint32_t)bin << shift;
+    above_all += above;
+    const uint32_t lo = prefix | ((uint32_t)bin << shift);
+    if (lo > 0u && above_all + inbin <= kk + slack) { T = lo - 1u; need_eq = 0; return; }
+    prefix = lo;
     mask |= 255u << shift;
     need -= above;
     if (shift == 0) break;
@@ -603,28 +638,17 @@ __device__ int list_store_kept(const RegList& r, uint32_t T, int need_eq, uint32
 }
 
 // Mid-stream compaction of one query's list (n > k): returns the new length
-// and raises thr (a strict bound: later entries need key > thr).
+// and raises thr (a strict bound: later entries need key > thr; every kept
+// entry has key > T, or key == T and a smaller index, so an entry with key
+// <= T ranks below at least k kept ones).
 __device__ int list_shrink(uint32_t* keys, uint16_t* ids, int n, int k, uint32_t* hist, uint32_t& thr) {
   RegList r;
   list_load(keys, ids, n, r);
-  uint32_t kmin, kmax;
-  list_minmax(r, kmin, kmax);
-  if (kmin != kmax) {
-    const int hb = 31 - __builtin_clz(kmin ^ kmax);
-    const uint32_t mask = hb == 31 ? 0u : ~((2u << hb) - 1u);
-    const int shift = hb >= 7 ? hb - 7 : 0;
-    int bin, above, inbin;
-    list_digit(r, kmax & mask, mask, shift, k, hist, bin, above, inbin);
-    const uint32_t L = (kmax & mask) | ((uint32_t)bin << shift);
-    if (L > 0u && above + inbin <= kSKeep) {
-      thr = L > thr ? L : thr;
-      return list_store_kept(r, L - 1u, 0, keys, ids);
-    }
-  }
   uint32_t T;
   int need_eq;
-  list_select(r, k, hist, T, need_eq);
-  thr = T > thr ? T : thr;
+  list_cut(r, k, kSSlack, hist, T, need_eq);
+  const uint32_t bound = need_eq == 0 ? T + 1u : T;
+  thr = bound > thr ? bound : thr;
   return list_store_kept(r, T, need_eq, keys, ids);
 }
 
@@ -733,8 +757,8 @@ __global__ __launch_bounds__(kSThreads, 1) void idx_stream_kernel(StreamArgs a) 
     if (tid < kSChunk) S.ks[c & 1][tid] = st.sc;
   };
 
-  // scores of the 32 entries at chunk offset ke0 + l32 for this lane's two queries
-  auto score = [&](const uint8_t* kb, const float* ksc, int ke0, float& sA, float& sB) {
+  // S^T block of the 32 entries at chunk offset ke0 + l32 (rows: 4 queries x 8 heads)
+  auto block_mfma = [&](const uint8_t* kb, int ke0) -> sf32x16 {
     const int ke = ke0 + l32;
     const uint8_t* kr = kb + ke * kSRow;
     const int sw = (ke >> 1) & 7;
@@ -746,7 +770,10 @@ __global__ __launch_bounds__(kSThreads, 1) void idx_stream_kernel(StreamArgs a) 
       const uint4 v = *(const uint4*)(kr + 16 * ((2 * j + g) ^ sw));
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[j], __builtin_bit_cast(sbf16x8, v), acc, 0, 0, 0);
     }
-    const float sk = ksc[ke];
+    return acc;
+  };
+  // head-weighted ReLU sums: lanes < 32 get queries 0 and 2, lanes >= 32 queries 1 and 3
+  auto block_scores = [&](const sf32x16& acc, float sk, float& sA, float& sB) {
     float p[kSQW];
 #pragma unroll
     for (int qq = 0; qq < kSQW; ++qq) {
@@ -760,22 +787,24 @@ __global__ __launch_bounds__(kSThreads, 1) void idx_stream_kernel(StreamArgs a) 
     sA = (__uint_as_float(r01[0]) + __uint_as_float(r01[1])) * sk;
     sB = (__uint_as_float(r23[0]) + __uint_as_float(r23[1])) * sk;
   };
-  // append the passing entries of one 32-entry block (entry index e for this lane)
-  auto append = [&](uint64_t mA, uint64_t mB, float sA, float sB, int e) {
-    if (mA & (1ull << lane)) {
-      const int d = (g ? cnt[1] : cnt[0]) + __popcll(mA & lt & half);
-      ck[qA * kSCap + d] = score_key(sA);
-      ci[qA * kSCap + d] = (uint16_t)e;
-    }
-    if (mB & (1ull << lane)) {
-      const int d = (g ? cnt[3] : cnt[2]) + __popcll(mB & lt & half);
-      ck[qB * kSCap + d] = score_key(sB);
-      ci[qB * kSCap + d] = (uint16_t)e;
-    }
-    cnt[0] += __popcll(mA & 0xffffffffull);
-    cnt[1] += __popcll(mA >> 32);
-    cnt[2] += __popcll(mB & 0xffffffffull);
-    cnt[3] += __popcll(mB >> 32);
+  // append the passing entries of one 32-entry block (entry index e for this
+  // lane); a lane's slot is its list length plus the passing lanes below it
+  // in its half of the wave.  Branch-free: a lane that does not pass writes
+  // to its own spare slot behind the list.
+  auto append = [&](bool pA, bool pB, float sA, float sB, int e) {
+    const uint64_t mA = __ballot(pA), mB = __ballot(pB);
+    const int a_lo = __popcll(mA & 0xffffffffull), a_hi = __popcll(mA >> 32);
+    const int b_lo = __popcll(mB & 0xffffffffull), b_hi = __popcll(mB >> 32);
+    const int dA = pA ? lane_rank(mA, g ? cnt[1] - a_lo : cnt[0]) : kSCap + lane;
+    const int dB = pB ? lane_rank(mB, g ? cnt[3] - b_lo : cnt[2]) : kSCap + lane;
+    ck[qA * kSRowCap + dA] = key_of(sA);
+    ci[qA * kSRowCap + dA] = (uint16_t)e;
+    ck[qB * kSRowCap + dB] = key_of(sB);
+    ci[qB * kSRowCap + dB] = (uint16_t)e;
+    cnt[0] += a_lo;
+    cnt[1] += a_hi;
+    cnt[2] += b_lo;
+    cnt[3] += b_hi;
   };
 
   Stage nxt, far;
@@ -790,33 +819,39 @@ __global__ __launch_bounds__(kSThreads, 1) void idx_stream_kernel(StreamArgs a) 
     if (c + 2 < nchunks) stage_load(c + 2, far);
     const uint8_t* kb = S.kb[c & 1];
     const float* ksc = S.ks[c & 1];
-    for (int s = 0; s < kSChunk / kSStep; ++s) {
-      const int e0 = c * kSChunk + kSStep * s;
-      if (e0 >= ntw) break;                                        // uniform per wave
-      // room for one more iteration of appends in every list
-      bool shrunk = false;
+    if (c * kSChunk < ntw) {                                       // uniform per wave
+      // all four column blocks of the chunk on the MFMA pipe first; their
+      // latency overlaps the VALU work on the earlier blocks
+      sf32x16 acc[kSChunk / 32];
+      float sk[kSChunk / 32];
 #pragma unroll
-      for (int qq = 0; qq < kSQW; ++qq) {
-        if (cnt[qq] > kSCap - kSStep) {                              // uniform
-          cnt[qq] = list_shrink(ck + qq * kSCap, ci + qq * kSCap, cnt[qq], a.k, S.hist[wave], thr[qq]);
-          shrunk = true;
+      for (int blk = 0; blk < kSChunk / 32; ++blk) {
+        acc[blk] = block_mfma(kb, 32 * blk);
+        sk[blk] = ksc[32 * blk + l32];
+      }
+#pragma unroll
+      for (int s = 0; s < kSChunk / kSStep; ++s) {
+        const int e0 = c * kSChunk + kSStep * s;
+        if (e0 >= ntw) break;                                      // uniform per wave
+        // room for one more iteration of appends in every list
+        bool shrunk = false;
+#pragma unroll
+        for (int qq = 0; qq < kSQW; ++qq) {
+          if (cnt[qq] > kSCap - kSStep) {                            // uniform
+            cnt[qq] = list_shrink(ck + qq * kSRowCap, ci + qq * kSRowCap, cnt[qq], a.k, S.hist[wave], thr[qq]);
+            shrunk = true;
+          }
         }
-      }
-      if (shrunk) {
-        thrA = thr_float(g ? thr[1] : thr[0]);
-        thrB = thr_float(g ? thr[3] : thr[2]);
-      }
-      float sA0, sB0, sA1, sB1;
-      score(kb, ksc, kSStep * s, sA0, sB0);
-      score(kb, ksc, kSStep * s + 32, sA1, sB1);
-      const int e = e0 + l32;
-      const uint64_t mA0 = __ballot(e < ntA && sA0 > thrA), mB0 = __ballot(e < ntB && sB0 > thrB);
-      const uint64_t mA1 = __ballot(e + 32 < ntA && sA1 > thrA), mB1 = __ballot(e + 32 < ntB && sB1 > thrB);
-      if ((mA0 | mB0 | mA1 | mB1) != 0ull) {
-        append(mA0, mB0, sA0, sB0, e);
-        append(mA1, mB1, sA1, sB1, e + 32);
-#pragma unroll
-        for (int qq = 0; qq < kSQW; ++qq) cnt[qq] = __builtin_amdgcn_readfirstlane(cnt[qq]);
+        if (shrunk) {
+          thrA = thr_float(g ? thr[1] : thr[0]);
+          thrB = thr_float(g ? thr[3] : thr[2]);
+        }
+        float sA0, sB0, sA1, sB1;
+        block_scores(acc[2 * s], sk[2 * s], sA0, sB0);
+        block_scores(acc[2 * s + 1], sk[2 * s + 1], sA1, sB1);
+        const int e = e0 + l32;
+        append(e < ntA && sA0 > thrA, e < ntB && sB0 > thrB, sA0, sB0, e);
+        append(e + 32 < ntA && sA1 > thrA, e + 32 < ntB && sB1 > thrB, sA1, sB1, e + 32);
       }
     }
     if (c + 1 < nchunks) stage_store(c + 1, nxt);
@@ -835,8 +870,8 @@ __global__ __launch_bounds__(kSThreads, 1) void idx_stream_kernel(StreamArgs a) 
     const int kk = n < a.k ? n : a.k;
     for (int i = kk + lane; i < a.k; i += kWave) out[i] = -1;
     if (kk == 0) continue;
-    const uint32_t* keys = ck + qq * kSCap;
-    const uint16_t* ids = ci + qq * kSCap;
+    const uint32_t* keys = ck + qq * kSRowCap;
+    const uint16_t* ids = ci + qq * kSRowCap;
     if (n <= a.k) {
       for (int i = lane; i < n; i += kWave) out[i] = (int32_t)ids[i];
       continue;
@@ -845,7 +880,7 @@ __global__ __launch_bounds__(kSThreads, 1) void idx_stream_kernel(StreamArgs a) 
     list_load(keys, ids, n, r);
     uint32_t T;
     int need_eq;
-    list_select(r, kk, S.hist[wave], T, need_eq);
+    list_cut(r, kk, 0, S.hist[wave], T, need_eq);
     int outn = 0, eqs = 0;
 #pragma unroll
     for (int j = 0; j < kSSlots; ++j) {
