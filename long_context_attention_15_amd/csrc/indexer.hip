@@ -415,44 +415,38 @@ __global__ __launch_bounds__(kIdxThreads) void idx_merge_kernel(IdxArgs a) {
 
 // ------------------------------------------------- streaming top-k (prefill)
 //
-// Many queries, FP8 keys of 64 dims, at most 8 heads: a workgroup owns 16
-// consecutive queries (4 per wavefront) and streams their visible entries in
-// ascending index order through LDS, 128 entries at a time, shared by all
-// four wavefronts.  Scores come from v_mfma_f32_32x32x16_bf16 with the 32
-// rows = 4 queries x 8 heads and 32 entries as columns (FP8 codes convert to
-// BF16 exactly; the products and their float32 sums are as accurate as a
-// float32 dot product).  Each query keeps a candidate list in LDS (entry
-// order, so index order) and a threshold: an entry is appended when its
-// score beats the threshold.  When a list is nearly full it is compacted:
-// one radix digit of the keys locates a bound L with at least k keys >= L;
-// the keys >= L stay and the threshold becomes L, which is safe because each
+// Many queries, FP8 keys of 64 dims, at most 8 heads: one wavefront owns 4
+// consecutive queries and streams their visible entries in ascending index
+// order straight from L2 into registers (the compressed keys of a sequence
+// are a few MB and stay cached), 64 entries per iteration, two iterations
+// ahead.  Scores come from v_mfma_f32_32x32x16_bf16 with the 32 rows = 4
+// queries x 8 heads and 32 entries as columns (FP8 codes convert to BF16
+// exactly; the products and their float32 sums are as accurate as a float32
+// dot product).  Each query keeps a candidate list in LDS (entry order, so
+// index order) and a threshold: an entry is appended when its score beats
+// the threshold.  When a list is nearly full it is compacted: radix digits
+// of the keys locate a bound L with at least k keys >= L and few more; the
+// keys >= L stay and the threshold becomes L, which is safe because each
 // later entry with a key <= L ranks below at least k kept ones (larger key,
-// or equal key and smaller index).  If that bound keeps too much (heavy
-// ties) the exact k-th key is found instead and only the k best stay.  At the
-// end an exact radix select over the list gives the top-k, emitted in list
-// order = ascending index.  No workspace, one pass over the keys.
-constexpr int kSThreads = 256;
-constexpr int kSWaves = kSThreads / kWave;
-constexpr int kSQW = 4;                   // queries per wavefront
-constexpr int kSQ = kSWaves * kSQW;       // queries per workgroup
-constexpr int kSCap = 1024;               // candidate slots per query
-constexpr int kSSlots = kSCap / kWave;    // list slots per lane when a list is in registers
-constexpr int kSChunk = 128;              // entries per LDS stage
-constexpr int kSRow = 128;                // BF16 key row in LDS (64 dims)
-constexpr int kSStep = 64;                // entries per loop iteration (two MFMA column blocks)
+// or equal key and smaller index).  If no such bound exists (heavy ties) the
+// exact k-th key is found and only the k best stay.  At the end an exact
+// radix select over the list gives the top-k, emitted in list order =
+// ascending index.  No workspace, no barriers, one pass over the keys.
+constexpr int kSQW = 4;                   // queries per wavefront (= workgroup)
+constexpr int kSCap = 992;                // candidate slots per query
+constexpr int kSSlots = (kSCap + kWave - 1) / kWave;   // list slots per lane when a list is in registers
+constexpr int kSStep = 64;                // entries per iteration (two MFMA column blocks)
 constexpr int kSSlack = 96;               // a compaction keeps at most k + kSSlack entries
-constexpr int kStreamMaxK = kSCap - kSSlack - 2 * 64;
+constexpr int kStreamMaxK = kSCap - kSSlack - 2 * kSStep;
 constexpr int64_t kStreamMaxN = 65536;    // candidate indices are 16-bit
 constexpr int64_t kStreamMinQueries = 2048;
 
 constexpr int kSRowCap = kSCap + kWave;   // list slots + one spare slot per lane
 
 struct StreamLds {
-  uint32_t ckey[kSQ][kSRowCap];
-  uint16_t cidx[kSQ][kSRowCap];
-  uint8_t kb[2][kSChunk * kSRow];
-  float ks[2][kSChunk];
-  uint32_t hist[kSWaves][256];
+  uint32_t ckey[kSQW][kSRowCap];
+  uint16_t cidx[kSQW][kSRowCap];
+  uint32_t hist[256];
 };
 
 typedef __attribute__((ext_vector_type(8))) __bf16 sbf16x8;
@@ -661,17 +655,22 @@ struct StreamArgs {
   int32_t* sel;
 };
 
-__global__ __launch_bounds__(kSThreads, 1) void idx_stream_kernel(StreamArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t s_raw[];
-  StreamLds& S = *reinterpret_cast<StreamLds*>(s_raw);
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+// Raw key bytes of one iteration for this lane: entry (32 blk + l32) of the
+// iteration, bytes [32 g, 32 g + 32) of its FP8 row, and the row scale.
+struct KeyRegs {
+  uint4 w[2][2];
+  float sc[2];
+};
+
+__global__ __launch_bounds__(kWave) void idx_stream_kernel(StreamArgs a) {
+  __shared__ StreamLds S;
+  const int lane = threadIdx.x;
   const int g = lane >> 5, l32 = lane & 31;
   // heaviest groups (latest queries) first
   const int b = blockIdx.x / a.ngroups;
   const int grp = a.ngroups - 1 - (int)(blockIdx.x % a.ngroups);
-  const int q0 = grp * kSQ;
+  const int q0 = grp * kSQW;
 
-  // visible entries of every query of the workgroup; the stream runs to the largest
   auto visible = [&](int q) -> int {
     if (q >= a.Tq) return 0;
     const int64_t bq = (int64_t)b * a.Tq + q;
@@ -679,28 +678,28 @@ __global__ __launch_bounds__(kSThreads, 1) void idx_stream_kernel(StreamArgs a) 
     const int64_t nt = t < 0 ? 0 : (t + 1) / a.m;
     return (int)(nt < a.n_entries ? nt : a.n_entries);
   };
-  int nmax = 0;
-  for (int j = 0; j < kSQ; ++j) nmax = max(nmax, visible(q0 + j));
   int ntq[kSQW];
-  int ntw = 0;                                      // the largest of this wavefront's queries
+  int ntw = 0;                                      // the stream runs to the largest
 #pragma unroll
   for (int qq = 0; qq < kSQW; ++qq) {
-    ntq[qq] = visible(q0 + wave * kSQW + qq);
+    ntq[qq] = visible(q0 + qq);
     ntw = max(ntw, ntq[qq]);
   }
 
-  // A operand: rows = (query r >> 3, head r & 7); K-step j covers dims [16 j + 8 g, +8)
+  // A operand: rows = (query r >> 3, head r & 7); K-step j covers dims
+  // [32 g + 8 j, +8) (the same split as the B operand below)
   sbf16x8 qa[4];
   {
-    const int qq = l32 >> 3, h = l32 & 7, q = q0 + wave * kSQW + qq;
+    const int qq = l32 >> 3, h = l32 & 7, q = q0 + qq;
     const bool ok = q < a.Tq && h < a.H_I;
     const uint8_t* qp = a.qidx.rows + ((int64_t)b * a.qidx.cap + (int64_t)(ok ? q : 0) * a.H_I + (ok ? h : 0)) *
-                                          a.qidx.row_bytes;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint2 v = ok ? *(const uint2*)(qp + 16 * j + 8 * g) : make_uint2(0u, 0u);
-      qa[j] = __builtin_bit_cast(sbf16x8, fp8x8_to_bf16(v.x, v.y));
-    }
+                                          a.qidx.row_bytes + 32 * g;
+    const uint4 v0 = ok ? *(const uint4*)qp : make_uint4(0u, 0u, 0u, 0u);
+    const uint4 v1 = ok ? *(const uint4*)(qp + 16) : make_uint4(0u, 0u, 0u, 0u);
+    qa[0] = __builtin_bit_cast(sbf16x8, fp8x8_to_bf16(v0.x, v0.y));
+    qa[1] = __builtin_bit_cast(sbf16x8, fp8x8_to_bf16(v0.z, v0.w));
+    qa[2] = __builtin_bit_cast(sbf16x8, fp8x8_to_bf16(v1.x, v1.y));
+    qa[3] = __builtin_bit_cast(sbf16x8, fp8x8_to_bf16(v1.z, v1.w));
   }
   // head weights of this lane's accumulator rows (query r >> 2, head 4 g + (r & 3)),
   // with the query row scales folded in
@@ -709,7 +708,7 @@ __global__ __launch_bounds__(kSThreads, 1) void idx_stream_kernel(StreamArgs a) 
   for (int qq = 0; qq < kSQW; ++qq)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int q = q0 + wave * kSQW + qq, h = 4 * g + i;
+      const int q = q0 + qq, h = 4 * g + i;
       float w = 0.0f;
       if (q < a.Tq && h < a.H_I) {
         const int64_t bq = (int64_t)b * a.Tq + q;
@@ -719,55 +718,39 @@ __global__ __launch_bounds__(kSThreads, 1) void idx_stream_kernel(StreamArgs a) 
       wl[qq][i] = w;
     }
 
-  // lanes < 32 score queries 0 and 2 of the wave, lanes >= 32 queries 1 and 3
+  // lanes < 32 score queries 0 and 2, lanes >= 32 queries 1 and 3
   const int qA = g, qB = 2 + g;
   const int ntA = g ? ntq[1] : ntq[0], ntB = g ? ntq[3] : ntq[2];
   uint32_t thr[kSQW] = {0u, 0u, 0u, 0u};
   int cnt[kSQW] = {0, 0, 0, 0};
   float thrA = -INFINITY, thrB = -INFINITY;
-  uint32_t* ck = &S.ckey[wave * kSQW][0];
-  uint16_t* ci = &S.cidx[wave * kSQW][0];
+  uint32_t* ck = &S.ckey[0][0];
+  uint16_t* ci = &S.cidx[0][0];
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const uint64_t half = g ? 0xffffffff00000000ull : 0x00000000ffffffffull;
 
-  // staging: thread -> (entry tid >> 1, bytes [32 (tid & 1), +32) of its FP8 row);
-  // chunk c + 2 is loaded while chunk c is scored, chunk c + 1 is stored after it
-  const int sk_e = tid >> 1, sk_h = tid & 1;
   const int64_t krow0 = (int64_t)b * a.keys.cap;
-  const int nchunks = (nmax + kSChunk - 1) / kSChunk;
-  struct Stage { uint4 w0, w1; float sc; };
-  auto stage_load = [&](int c, Stage& st) {
-    const int e = min(c * kSChunk + sk_e, nmax - 1);
-    const uint8_t* kp = a.keys.rows + (krow0 + e) * a.keys.row_bytes + 32 * sk_h;
-    st.w0 = *(const uint4*)kp;
-    st.w1 = *(const uint4*)(kp + 16);
-    st.sc = 0.0f;
-    if (tid < kSChunk) st.sc = ((const float*)a.keys.scales)[krow0 + min(c * kSChunk + tid, nmax - 1)];
-  };
-  // logical 16-byte unit u (dims [8 u, 8 u + 8)) of entry e sits at unit u ^ ((e >> 1) & 7)
-  auto stage_store = [&](int c, const Stage& st) {
-    uint8_t* dst = S.kb[c & 1] + sk_e * kSRow;
-    const int sw = (sk_e >> 1) & 7;
-    const uint32_t w[8] = {st.w0.x, st.w0.y, st.w0.z, st.w0.w, st.w1.x, st.w1.y, st.w1.z, st.w1.w};
+  const int niter = (ntw + kSStep - 1) / kSStep;
+  auto load_iter = [&](int it, KeyRegs& kr) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int u = 4 * sk_h + j;
-      *(uint4*)(dst + 16 * (u ^ sw)) = fp8x8_to_bf16(w[2 * j], w[2 * j + 1]);
+    for (int blk = 0; blk < 2; ++blk) {
+      const int e = min(it * kSStep + 32 * blk + l32, ntw - 1);
+      const uint8_t* kp = a.keys.rows + (krow0 + e) * a.keys.row_bytes + 32 * g;
+      kr.w[blk][0] = *(const uint4*)kp;
+      kr.w[blk][1] = *(const uint4*)(kp + 16);
+      kr.sc[blk] = ((const float*)a.keys.scales)[krow0 + e];
     }
-    if (tid < kSChunk) S.ks[c & 1][tid] = st.sc;
   };
 
-  // S^T block of the 32 entries at chunk offset ke0 + l32 (rows: 4 queries x 8 heads)
-  auto block_mfma = [&](const uint8_t* kb, int ke0) -> sf32x16 {
-    const int ke = ke0 + l32;
-    const uint8_t* kr = kb + ke * kSRow;
-    const int sw = (ke >> 1) & 7;
+  // S^T block (rows: 4 queries x 8 heads, columns: the block's 32 entries)
+  auto block_mfma = [&](const KeyRegs& kr, int blk) -> sf32x16 {
     sf32x16 acc;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+    const uint4 w0 = kr.w[blk][0], w1 = kr.w[blk][1];
+    const uint32_t wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint4 v = *(const uint4*)(kr + 16 * ((2 * j + g) ^ sw));
+      const uint4 v = fp8x8_to_bf16(wv[2 * j], wv[2 * j + 1]);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[j], __builtin_bit_cast(sbf16x8, v), acc, 0, 0, 0);
     }
     return acc;
@@ -806,64 +789,49 @@ __global__ __launch_bounds__(kSThreads, 1) void idx_stream_kernel(StreamArgs a) 
     cnt[2] += b_lo;
     cnt[3] += b_hi;
   };
-
-  Stage nxt, far;
-  if (nchunks > 0) {
-    stage_load(0, nxt);
-    stage_store(0, nxt);
-  }
-  if (nchunks > 1) stage_load(1, nxt);
-  __syncthreads();
-
-  for (int c = 0; c < nchunks; ++c) {
-    if (c + 2 < nchunks) stage_load(c + 2, far);
-    const uint8_t* kb = S.kb[c & 1];
-    const float* ksc = S.ks[c & 1];
-    if (c * kSChunk < ntw) {                                       // uniform per wave
-      // all four column blocks of the chunk on the MFMA pipe first; their
-      // latency overlaps the VALU work on the earlier blocks
-      sf32x16 acc[kSChunk / 32];
-      float sk[kSChunk / 32];
+  auto iteration = [&](int it, const KeyRegs& kr) {
+    // room for one more iteration of appends in every list
+    bool shrunk = false;
 #pragma unroll
-      for (int blk = 0; blk < kSChunk / 32; ++blk) {
-        acc[blk] = block_mfma(kb, 32 * blk);
-        sk[blk] = ksc[32 * blk + l32];
-      }
-#pragma unroll
-      for (int s = 0; s < kSChunk / kSStep; ++s) {
-        const int e0 = c * kSChunk + kSStep * s;
-        if (e0 >= ntw) break;                                      // uniform per wave
-        // room for one more iteration of appends in every list
-        bool shrunk = false;
-#pragma unroll
-        for (int qq = 0; qq < kSQW; ++qq) {
-          if (cnt[qq] > kSCap - kSStep) {                            // uniform
-            cnt[qq] = list_shrink(ck + qq * kSRowCap, ci + qq * kSRowCap, cnt[qq], a.k, S.hist[wave], thr[qq]);
-            shrunk = true;
-          }
-        }
-        if (shrunk) {
-          thrA = thr_float(g ? thr[1] : thr[0]);
-          thrB = thr_float(g ? thr[3] : thr[2]);
-        }
-        float sA0, sB0, sA1, sB1;
-        block_scores(acc[2 * s], sk[2 * s], sA0, sB0);
-        block_scores(acc[2 * s + 1], sk[2 * s + 1], sA1, sB1);
-        const int e = e0 + l32;
-        append(e < ntA && sA0 > thrA, e < ntB && sB0 > thrB, sA0, sB0, e);
-        append(e + 32 < ntA && sA1 > thrA, e + 32 < ntB && sB1 > thrB, sA1, sB1, e + 32);
+    for (int qq = 0; qq < kSQW; ++qq) {
+      if (cnt[qq] > kSCap - kSStep) {                              // uniform
+        cnt[qq] = list_shrink(ck + qq * kSRowCap, ci + qq * kSRowCap, cnt[qq], a.k, S.hist, thr[qq]);
+        shrunk = true;
       }
     }
-    if (c + 1 < nchunks) stage_store(c + 1, nxt);
-    nxt = far;
-    __syncthreads();
+    if (shrunk) {
+      thrA = thr_float(g ? thr[1] : thr[0]);
+      thrB = thr_float(g ? thr[3] : thr[2]);
+    }
+    const sf32x16 acc0 = block_mfma(kr, 0);
+    const sf32x16 acc1 = block_mfma(kr, 1);
+    float sA0, sB0, sA1, sB1;
+    block_scores(acc0, kr.sc[0], sA0, sB0);
+    block_scores(acc1, kr.sc[1], sA1, sB1);
+    const int e = it * kSStep + l32;
+    append(e < ntA && sA0 > thrA, e < ntB && sB0 > thrB, sA0, sB0, e);
+    append(e + 32 < ntA && sA1 > thrA, e + 32 < ntB && sB1 > thrB, sA1, sB1, e + 32);
+  };
+
+  // two register sets, each reloaded right after use: iteration it + 2 is in
+  // flight while it + 1 is scored
+  KeyRegs r0, r1;
+  if (niter > 0) load_iter(0, r0);
+  if (niter > 1) load_iter(1, r1);
+  for (int it = 0; it < niter; it += 2) {
+    iteration(it, r0);
+    if (it + 2 < niter) load_iter(it + 2, r0);
+    if (it + 1 < niter) {
+      iteration(it + 1, r1);
+      if (it + 3 < niter) load_iter(it + 3, r1);
+    }
   }
   lds_wave_sync();
 
   // final exact top-k of each list, emitted in list order (ascending index)
 #pragma unroll
   for (int qq = 0; qq < kSQW; ++qq) {
-    const int q = q0 + wave * kSQW + qq;
+    const int q = q0 + qq;
     if (q >= a.Tq) continue;                                        // uniform
     int32_t* out = a.sel + ((int64_t)b * a.Tq + q) * a.k;
     const int n = cnt[qq];
@@ -880,7 +848,7 @@ __global__ __launch_bounds__(kSThreads, 1) void idx_stream_kernel(StreamArgs a) 
     list_load(keys, ids, n, r);
     uint32_t T;
     int need_eq;
-    list_cut(r, kk, 0, S.hist[wave], T, need_eq);
+    list_cut(r, kk, 0, S.hist, T, need_eq);
     int outn = 0, eqs = 0;
 #pragma unroll
     for (int j = 0; j < kSSlots; ++j) {
@@ -905,12 +873,8 @@ static hipError_t launch_idx_stream(const IdxArgs& ia, hipStream_t st) {
   StreamArgs a;
   a.qidx = ia.qidx; a.keys = ia.keys; a.head_w = ia.head_w; a.n_entries = ia.n_entries; a.q_pos = ia.q_pos;
   a.B = ia.B; a.Tq = ia.Tq; a.H_I = ia.H_I; a.m = ia.m; a.k = ia.k; a.sel = ia.sel;
-  a.ngroups = (ia.Tq + kSQ - 1) / kSQ;
-  const size_t lds = sizeof(StreamLds);
-  hipError_t e = hipFuncSetAttribute((const void*)idx_stream_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(idx_stream_kernel, dim3((unsigned)((int64_t)a.B * a.ngroups)), dim3(kSThreads), lds, st, a);
+  a.ngroups = (ia.Tq + kSQW - 1) / kSQW;
+  hipLaunchKernelGGL(idx_stream_kernel, dim3((unsigned)((int64_t)a.B * a.ngroups)), dim3(kWave), 0, st, a);
   return hipGetLastError();
 }
 
