@@ -2,36 +2,37 @@
 // FP8 bulk + BF16 RoPE dims, bf16 queries, 64 heads per workgroup.
 //
 // Work item: one query row, 64 heads, one split of its entry list (the
-// top-k / visible compressed entries followed by the window rows).
-// Four waves: wave w owns heads [32*(w>>1), +32) and dims [256*(w&1), +256).
-// Per tile of 32 entries:
-//   * all threads gather the 32 rows, convert FP8*scale -> BF16 with the
-//     hardware scaled conversion (exact), and stage them in LDS twice:
-//     Ks[entry][dim] (A operand of S^T) and Vt[dim][entry] (A operand of O^T);
-//   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 over the wave's 256 dims, the
-//     two dim-halves exchange partial sums through LDS;
+// top-k / visible compressed entries followed by the window rows).  Four
+// wavefronts; wavefront w owns heads [16 w, 16 w + 16) over all 512 dims,
+// so it needs no partial sums from the others, and two workgroups share a
+// CU.  Per tile of 32 entries:
+//   * the raw 576-byte rows are DMA'd into LDS one tile ahead
+//     (global_load_lds), each 16-byte unit placed with a per-row rotation
+//     so that both access patterns below are free of bank conflicts;
+//   * S^T = K Q^T on v_mfma_f32_16x16x32_bf16: each lane reads 8 FP8 bytes
+//     (or 8 BF16 RoPE values) of its entry row and converts FP8 * row scale
+//     -> BF16 in registers with the exact hardware conversion;
 //   * online softmax in base 2 per head (a head is one lane column of the
-//     32x32 accumulator, so max/sum need one cross-half exchange);
-//   * O^T += V^T P^T: P stays in registers as the B operand (the entry order
-//     inside a 16-entry K-step is permuted identically on both operands).
-// HBM traffic per query: the gathered rows plus q and out; the rows are
-// decoded once per workgroup.
+//     16x16 accumulators);
+//   * O^T += V^T P^T: V^T comes straight from the raw rows with the 8-bit
+//     (FP8 dims) and 16-bit (RoPE dims) transposing LDS reads; the FP8 codes
+//     convert unscaled and the row scale multiplies P instead; P stays in
+//     registers as the B operand (its entry order is the one the S^T
+//     accumulators already hold, the V^T reads follow it).
 #include "common.h"
 #include "launch.h"
 
 namespace csa {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
 
 constexpr int kMD = 512;                 // head dim
 constexpr int kMT = 32;                  // entries per tile
-constexpr int kKsPitch = kMD + 16;       // bf16 elements per Ks row: 264 words, 8 mod 64 banks
-constexpr int kVtPitch = kMT + 4;        // bf16 elements per Vt row (+8 B pad)
-constexpr int kMThreads = 256;
+constexpr int kMThreads = 256;           // four wavefronts
+constexpr int kMHeads = 16;              // heads per wavefront
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -73,6 +74,7 @@ __device__ __forceinline__ int m_slot_row(const MfmaArgs& a, int b, int64_t t, i
   return 2;
 }
 
+// 8 FP8 codes -> 8 BF16 values times s (exact for a power-of-two s).
 __device__ __forceinline__ u32x4 cvt8_fp8(u32x2 w, float s) {
   u32x4 r;
   r.x = __builtin_bit_cast(unsigned int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, s, false));
@@ -86,31 +88,54 @@ __device__ __forceinline__ u32x4 cvt8_fp8(u32x2 w, float s) {
 __device__ __attribute__((aligned(16))) uint8_t g_zero_row[1024];
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef int v2i32 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) v2i32 lds_v2i32;
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kRawRow = 576;                      // 448 FP8 + 64 BF16
+constexpr int kUnits = kRawRow / 16;              // 16-byte units per row
 constexpr int kRawTile = kMT * kRawRow;           // 18432 B = 18 wave-wide 1 KiB loads
 constexpr int kRawLoads = kRawTile / 1024;
-constexpr int kKsTile = kMT * kKsPitch;           // bf16 elements per converted tile
 
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
-#define CSA_WAIT_VMCNT0() __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8))
+// LDS placement of 16-byte unit c of tile row r: rows follow each other,
+// units rotate by unit_rot(r) within a row.  Sixteen consecutive rows
+// reading the same unit then hit sixteen different 16-byte bank groups, and
+// so do the row sets {0-7, 16-23} and {8-15, 24-31} that the transposing
+// reads gather.
+__device__ __forceinline__ int unit_rot(int r) { return ((r >> 2) ^ ((r >> 4) << 1)) & 3; }
+__device__ __forceinline__ int unit_pos(int r, int c) {
+  const int cc = c + unit_rot(r);
+  return kUnits * r + (cc >= kUnits ? cc - kUnits : cc);
+}
+
+// Entry behind K slot 8 G + i of the PV product (G = lane >> 4): the order
+// in which the S^T accumulators hold a lane's entries (16 (i >> 2) + 4 G + (i & 3)).
+__device__ __forceinline__ int pv_entry(int G, int i) { return 16 * (i >> 2) + 4 * G + (i & 3); }
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+#define CSA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+#define CSA_WAIT_VMCNT0() CSA_WAIT_VMCNT(0)
+
+// Gathered rows come from HBM with microsecond latency: kStages tile buffers
+// keep kStages - 1 tiles of row loads in flight per workgroup.
+constexpr int kStages = 4;
+constexpr int kSlots = 8;                         // slot tables (>= kStages + 2, power of two)
+constexpr int kDmaPerWave = 5;                    // DMA loads per wave per tile (18 spread over 4 waves, padded)
 
 __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][kKsTile];
-  __shared__ __attribute__((aligned(16))) uint8_t Raw[2][kRawTile];
-  __shared__ __attribute__((aligned(16))) float Sx[4][16][64];
-  __shared__ const uint8_t* Tptr[4][kMT];         // per tile slot: row address (zero row if empty)
-  __shared__ float Tscl[4][kMT];                  // row scale, 0 if empty
+  __shared__ __attribute__((aligned(16))) uint8_t Raw[kStages][kRawTile];
+  __shared__ const uint8_t* Tptr[kSlots][kMT];    // per tile slot: row address (zero row if empty)
+  __shared__ __attribute__((aligned(16))) float Tscl[kSlots][kMT];   // row scale, 0 if empty
+  __shared__ int s_over;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int rh = wave >> 1, dh = wave & 1;
-  const int g32 = lane >> 5, l32 = lane & 31;
+  const int G = lane >> 4, l16 = lane & 15;           // 16-lane group and position in it
   const int64_t bq = xcd_remap(blockIdx.x, gridDim.x);   // query row (b * Tq + q)
   const int b = (int)(bq / a.Tq);
-  const int h = blockIdx.y * 64 + rh * 32 + l32;          // this lane's head
+  const int h = blockIdx.y * 64 + wave * kMHeads + l16;   // this lane's head
   const int64_t t = a.q_pos ? a.q_pos[bq] : (int64_t)(bq % a.Tq);
   const int64_t Lc = a.mode == kModeSel ? a.k : (a.mode == kModeRange ? m_visible(t, a.m, a.n_entries) : 0);
   const int64_t L = Lc + a.W;
@@ -126,51 +151,72 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
     const int64_t slot = i0 + (int64_t)tile * kMT + tid;
     const int src = m_slot_row(a, b, t, Lc, slot, i1, jsel, row);
     const Store& stv = src == 2 ? a.win : a.ckv;
-    Tptr[tile & 3][tid] = src ? stv.rows + row * stv.row_bytes : g_zero_row;
+    Tptr[tile & (kSlots - 1)][tid] = src ? stv.rows + row * stv.row_bytes : g_zero_row;
     return src ? ((const float*)stv.scales)[row] : 0.0f;
   };
   auto sel_of = [&](int tile) -> int {
     return m_slot_sel(a, bq, Lc, i0 + (int64_t)tile * kMT + tid, i1);
   };
-  // DMA the raw rows of `tile` into Raw[tile & 1]: 18 wave-wide loads of
-  // 1 KiB, load q covering raw bytes [1024 q, 1024 q + 1024).
+  // DMA the raw rows of `tile` into Raw[tile % kStages]: 18 wave-wide loads
+  // of 1 KiB; lane l of load qd fills LDS unit 64 qd + l, i.e. the (row,
+  // unit) that unit_pos places there.  Every wave issues kDmaPerWave loads
+  // (waves 2 and 3 repeat one load of theirs, writing the same bytes again)
+  // so that all waves can wait on the same vmcnt.
   auto dma_tile = [&](int tile) {
-    uint8_t* dst = Raw[tile & 1];
-    for (int qd = wave; qd < kRawLoads; qd += 4) {
-      const int ci = qd * 64 + lane;                   // 16-byte chunk of the tile
-      const int slot = ci / 36, ch = ci - slot * 36;
-      const uint8_t* src = Tptr[tile & 3][slot] + 16 * ch;
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(dst + 1024 * qd), 16, 0, 0);
-    }
-  };
-  // Raw[tile & 1] -> Ks[tile & 1]: FP8 * row scale -> BF16 (exact), RoPE dims copied.
-  auto convert_tile = [&](int tile) {
-    const uint8_t* raw = Raw[tile & 1];
-    uint16_t* ks = Ks[tile & 1];
-    const int row = tid >> 3, sub = tid & 7;
-    const float sc = Tscl[tile & 3][row];
-    const uint8_t* rr = raw + row * kRawRow;
-    uint16_t* kr = ks + row * kKsPitch;
+    uint8_t* dst = Raw[tile % kStages];
+    const uint8_t* const* tp = Tptr[tile & (kSlots - 1)];
 #pragma unroll
-    for (int mm = 0; mm < 7; ++mm) {
-      const int u = sub + 8 * mm;                       // 8-byte unit of the 448 FP8 bytes
-      const u32x2 w = *(const u32x2*)(rr + 8 * u);
-      *(u32x4*)(kr + 8 * u) = cvt8_fp8(w, sc);
+    for (int j = 0; j < kDmaPerWave; ++j) {
+      int qd = wave + 4 * j;
+      qd = qd < kRawLoads ? qd : qd - 4;
+      const int u = qd * 64 + lane;
+      const int r = u / kUnits, cc = u - r * kUnits;
+      int c = cc - unit_rot(r);
+      c = c < 0 ? c + kUnits : c;
+      __builtin_amdgcn_global_load_lds((const void*)(tp[r] + 16 * c), (lds_void*)(dst + 1024 * qd), 16, 0, 0);
     }
-    *(u32x4*)(kr + 448 + 8 * sub) = *(const u32x4*)(rr + 448 + 16 * sub);
   };
 
+  // Q^T operands: K-step ks covers dims [32 ks, 32 ks + 32); lane group G
+  // takes dims 32 ks + 8 G .. +8.  Steps 0..13 are the FP8 dims, 14 and 15
+  // the BF16 RoPE dims.
   bf16x8 qf[16];
   {
-    const uint16_t* qp = a.q + (bq * a.H + h) * (int64_t)kMD + dh * 256 + g32 * 8;
+    const uint16_t* qp = a.q + (bq * a.H + h) * (int64_t)kMD + 8 * G;
 #pragma unroll
-    for (int s = 0; s < 16; ++s) qf[s] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qp + 16 * s));
+    for (int ks = 0; ks < 16; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qp + 32 * ks));
   }
-  f32x16 acc[8];
+  // LDS byte offsets (within a tile) of this lane's reads.
+  // S^T A operand, row block eb: entry 16 eb + l16; FP8 K-step ks reads bytes
+  // 32 ks + 8 G .. +8 = unit 2 ks + (G >> 1), half G & 1; RoPE step 14 + j
+  // reads BF16 dims 32 j + 8 G = unit 28 + 4 j + G.
+  int s_fp8[2], s_rope[2][2];
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt)
+  for (int eb = 0; eb < 2; ++eb) {
+    const int e = 16 * eb + l16;
+    s_fp8[eb] = 16 * (kUnits * e + unit_rot(e) + (G >> 1)) + 8 * (G & 1);   // + 32 ks
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[mt][r] = 0.0f;
+    for (int j = 0; j < 2; ++j) s_rope[eb][j] = 16 * unit_pos(e, 28 + 4 * j + G);
+  }
+  // V^T A operand, FP8 dim block db (dims 16 db .. +16, unit db): lane
+  // (16 G + l16) points at entry pv_entry(G, l16 >> 1), half l16 & 1.
+  const int ve = pv_entry(G, l16 >> 1);
+  const int v_fp8 = 16 * (kUnits * ve + unit_rot(ve)) + 8 * (l16 & 1);            // + 16 db
+  // V^T A operand, RoPE dim block 28 + j, j < 4 (bf16 dims 16 j .. +16), read hh:
+  // entry pv_entry(G, 4 hh + (l16 >> 2)), bf16 dims 16 j + 4 (l16 & 3).
+  int v_rope[4][2];                                                                 // [j][hh]
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int e = pv_entry(G, 4 * hh + (l16 >> 2));
+      const int dbyte = 448 + 2 * (16 * j + 4 * (l16 & 3));
+      v_rope[j][hh] = 16 * unit_pos(e, dbyte >> 4) + (dbyte & 15);
+    }
+
+  f32x4 acc[32];
+#pragma unroll
+  for (int db = 0; db < 32; ++db) acc[db] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   const float sc2 = a.tau * kLog2e;
   // Softmax reference (log2 units, per head = per lane column): fixed at the
   // head's first non-empty tile and never moved, so no VALU code ever touches
@@ -180,121 +226,159 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
   // the first pass tracks in mmax.
   constexpr float kMaxLift = 64.0f;
   float mref = -INFINITY, mmax = -INFINITY, lrun = 0.0f;
-  __shared__ int s_over;
   if (tid == 0) s_over = 0;
-
-  // transposed-read addressing of V^T (see the ds_read_b64_tr_b16 lane map):
-  // lane j of a 16-lane group points at entry row 4*g + (j>>2) (+8 for the
-  // second half of a K-step), dims D0 + 16*half + 4*(j&3).
-  const int trj = lane & 15, trhalf = (lane >> 4) & 1;
-  const int tr_row = 4 * g32 + (trj >> 2);
-  const int tr_col = dh * 256 + 16 * trhalf + 4 * (trj & 3);
 
 #pragma nounroll
   for (int attempt = 0; attempt < 2; ++attempt) {
-    // ---- prologue: tables of tiles 0..2, rows of tiles 0 and 1, tile 0 converted
+    // ---- prologue: tables of tiles 0 .. kStages-1, rows of tiles 0 .. kStages-2
+    // (iteration it stores the scale of tile it + kStages - 1, computes the
+    // table of tile it + kStages and loads the sel of tile it + kStages + 1)
     int selreg = 0;
-    float scl_pending = 0.0f;                       // scale of table tile it+2, stored at iteration it
+    float scl_pending = 0.0f;
     if (tid < kMT) {
-      const int j0 = sel_of(0), j1 = sel_of(1), j2 = sel_of(2);
-      selreg = sel_of(3);
-      const float s0v = table_ptr(0, j0), s1v = table_ptr(1, j1);
-      scl_pending = table_ptr(2, j2);
-      Tscl[0][tid] = s0v;
-      Tscl[1][tid] = s1v;
+      int jn = sel_of(0);
+#pragma unroll
+      for (int tl = 0; tl < kStages; ++tl) {
+        const int jcur = jn;
+        jn = sel_of(tl + 1);
+        const float sv = table_ptr(tl, jcur);
+        if (tl < kStages - 1) Tscl[tl][tid] = sv;
+        else scl_pending = sv;
+      }
+      selreg = jn;
     }
     __syncthreads();
-    if (ntiles > 0) dma_tile(0);
-    if (ntiles > 1) dma_tile(1);
+#pragma unroll
+    for (int tl = 0; tl < kStages - 1; ++tl)
+      if (tl < ntiles) dma_tile(tl);
     CSA_WAIT_VMCNT0();
-    __syncthreads();
-    if (ntiles > 0) convert_tile(0);
     __syncthreads();
 
     for (int it = 0; it < ntiles; ++it) {
-      const uint16_t* ks = Ks[it & 1];
-      // S^T partial over this wave's dims: two accumulators for independent chains
-      f32x16 s0, s1;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) { s0[r] = 0.0f; s1[r] = 0.0f; }
-      const uint16_t* kp = ks + l32 * kKsPitch + dh * 256 + g32 * 8;
-#pragma unroll
-      for (int s = 0; s < 16; s += 2) {
-        const bf16x8 ka = __builtin_bit_cast(bf16x8, *(const u32x4*)(kp + 16 * s));
-        const bf16x8 kb = __builtin_bit_cast(bf16x8, *(const u32x4*)(kp + 16 * (s + 1)));
-        s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[s], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qf[s + 1], s1, 0, 0, 0);
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s0[r] += s1[r];
-        Sx[wave][r][lane] = s0[r];
-      }
-      CSA_WAIT_VMCNT0();                    // raw rows of tile it+1, the next sel and scale are in
       if (tid < kMT) {
-        Tscl[(it + 2) & 3][tid] = scl_pending;
-        if (it + 3 < ntiles) scl_pending = table_ptr(it + 3, selreg);
+        Tscl[(it + kStages - 1) & (kSlots - 1)][tid] = scl_pending;
+        if (it + kStages < ntiles) scl_pending = table_ptr(it + kStages, selreg);
+        if (it + kStages + 1 < ntiles) selreg = sel_of(it + kStages + 1);
       }
-      __syncthreads();                      // B1
-      if (it + 2 < ntiles) dma_tile(it + 2);  // into Raw[it & 1], converted last iteration
-      if (tid < kMT && it + 4 < ntiles) selreg = sel_of(it + 4);
+      // rows of tile it + kStages - 1 (its table was written one iteration ago)
+      if (it + kStages - 1 < ntiles) dma_tile(it + kStages - 1);
+      const uint8_t* raw = Raw[it % kStages];
+      const float* tsc = Tscl[it & (kSlots - 1)];
 
-      // softmax on this tile's logits
-      const unsigned int vmask = (unsigned int)__ballot(lane < 32 && Tscl[it & 3][l32] > 0.0f);
-      float p[16];
+      // ---- S^T = K Q^T: two row blocks of 16 entries, this wave's 16 heads.
+      // All fragment reads are issued first so that their LDS latency
+      // overlaps the conversions and MFMAs.
+      u32x2 kf[2][14];
+      u32x4 kr[2][2];
+#pragma unroll
+      for (int ks = 0; ks < 14; ++ks)
+#pragma unroll
+        for (int eb = 0; eb < 2; ++eb) kf[eb][ks] = *(const u32x2*)(raw + s_fp8[eb] + 32 * ks);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int eb = 0; eb < 2; ++eb) kr[eb][j] = *(const u32x4*)(raw + s_rope[eb][j]);
+      __builtin_amdgcn_sched_barrier(0);            // keep the reads ahead of their uses
+      f32x4 sa[2], sb[2];                           // even / odd K-step chains
+#pragma unroll
+      for (int eb = 0; eb < 2; ++eb) { sa[eb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f}; sb[eb] = sa[eb]; }
+      const float srow0 = tsc[l16], srow1 = tsc[16 + l16];
+#pragma unroll
+      for (int ks = 0; ks < 14; ++ks) {
+#pragma unroll
+        for (int eb = 0; eb < 2; ++eb) {
+          const u32x4 k = cvt8_fp8(kf[eb][ks], eb ? srow1 : srow0);
+          if (ks & 1) sb[eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k), qf[ks], sb[eb], 0, 0, 0);
+          else sa[eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k), qf[ks], sa[eb], 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int eb = 0; eb < 2; ++eb) {
+          if (j) sb[eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[eb][j]), qf[14 + j], sb[eb], 0, 0, 0);
+          else sa[eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[eb][j]), qf[14 + j], sa[eb], 0, 0, 0);
+        }
+      // V^T fragments for the PV product, read now so that the softmax below
+      // covers their latency
+      v2i32 vf[28];
+#pragma unroll
+      for (int db = 0; db < 28; ++db) vf[db] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32*)(raw + v_fp8 + 16 * db));
+      v4i16 vr[4][2];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) vr[j][hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(raw + v_rope[j][hh]));
+
+      // ---- softmax; lane holds entries 16 (i >> 2) + 4 G + (i & 3), i = 0..7, of head h
+      const unsigned int vmask = (unsigned int)__ballot(lane < 32 && tsc[lane & 31] > 0.0f);
+      float p[8];
       float mt = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int e = (r >> 2) * 8 + g32 * 4 + (r & 3);
-        const float tot = s0[r] + Sx[wave ^ 1][r][lane];
-        p[r] = ((vmask >> e) & 1u) ? tot * sc2 : -INFINITY;
-        mt = fmaxf(mt, p[r]);
+      for (int i = 0; i < 8; ++i) {
+        const int e = pv_entry(G, i);
+        const float tot = sa[i >> 2][i & 3] + sb[i >> 2][i & 3];
+        p[i] = ((vmask >> e) & 1u) ? tot * sc2 : -INFINITY;
+        mt = fmaxf(mt, p[i]);
       }
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      mt = fmaxf(mt, __shfl_xor(mt, 16));
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+        mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
       mmax = fmaxf(mmax, mt);
       if (mref == -INFINITY) mref = mt;     // the head's first non-empty tile
       if (__ballot(mt > mref + kMaxLift) != 0ull && lane == 0) s_over = 1;
       float psum = 0.0f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        p[r] = mref > -INFINITY ? exp2f(p[r] - mref) : 0.0f;
-        psum += p[r];
+      for (int i = 0; i < 8; ++i) {
+        p[i] = mref > -INFINITY ? exp2f(p[i] - mref) : 0.0f;
+        psum += p[i];
       }
-      psum += __shfl_xor(psum, 32);
+      psum += __shfl_xor(psum, 16);
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(psum), __float_as_uint(psum), false, false);
+        psum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      }
       lrun += psum;
-      bf16x8 pb0, pb1;
+      // P^T operands: raw for the RoPE dims, times the row scale for the FP8 dims
+      bf16x8 pr, ps;
+      {
+        const float4 e0 = *(const float4*)(tsc + 4 * G), e1 = *(const float4*)(tsc + 16 + 4 * G);
+        const float es[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        pb0[r] = (__bf16)p[r];
-        pb1[r] = (__bf16)p[r + 8];
-      }
-      if (it + 1 < ntiles) convert_tile(it + 1);   // Ks[(it+1)&1] was released at the last B2
-
-      // O^T += V^T P^T, V^T read transposed from Ks; K-step major so that
-      // consecutive MFMAs write different accumulators
-#pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2) {
-        const bf16x8 pb = ks2 ? pb1 : pb0;
-#pragma unroll
-        for (int mt8 = 0; mt8 < 8; ++mt8) {
-          const uint16_t* vb = ks + (tr_row + 16 * ks2) * kKsPitch + tr_col + 32 * mt8;
-          const v4i16 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vb));
-          const v4i16 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vb + 8 * kKsPitch));
-          const u32x2 ux0 = __builtin_bit_cast(u32x2, x0), ux1 = __builtin_bit_cast(u32x2, x1);
-          const u32x4 v0 = u32x4{ux0.x, ux0.y, ux1.x, ux1.y};
-          acc[mt8] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v0), pb, acc[mt8], 0, 0, 0);
+        for (int i = 0; i < 8; ++i) {
+          pr[i] = (__bf16)p[i];
+          ps[i] = (__bf16)(p[i] * es[i]);
         }
       }
-      __syncthreads();                      // B2
+
+      // ---- O^T += V^T P^T over 32 dim blocks of 16
+#pragma unroll
+      for (int db = 0; db < 28; ++db) {
+        const u32x4 v = cvt8_fp8(u32x2{(unsigned)vf[db].x, (unsigned)vf[db].y}, 1.0f);
+        acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), ps, acc[db], 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x2 ux0 = __builtin_bit_cast(u32x2, vr[j][0]), ux1 = __builtin_bit_cast(u32x2, vr[j][1]);
+        const u32x4 v = u32x4{ux0.x, ux0.y, ux1.x, ux1.y};
+        acc[28 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), pr, acc[28 + j], 0, 0, 0);
+      }
+      // the rows of tile it+1 are in: loads complete in order, and after
+      // them this wave issued the DMA of the next kStages - 2 tiles (plus,
+      // on wave 0, some table loads), so allowing that many DMA loads to be
+      // outstanding is safe; near the end of the list fewer were issued, so
+      // wait for everything there
+      if (it + kStages - 1 < ntiles) CSA_WAIT_VMCNT((kStages - 2) * kDmaPerWave);
+      else CSA_WAIT_VMCNT0();
+      __syncthreads();
     }
-    CSA_WAIT_VMCNT0();                      // no DMA may still target Raw
     __syncthreads();
     if (!s_over) break;                     // uniform
     // recompute with the exact per-head maximum (mref >= every logit now)
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mt][r] = 0.0f;
+    for (int db = 0; db < 32; ++db) acc[db] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     lrun = 0.0f;
     mref = mmax;
     __syncthreads();
@@ -302,21 +386,16 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
   }
   const float mrun = mref;
 
-  // ---- epilogue
+  // ---- epilogue: lane holds O^T rows (dims) 16 db + 4 G + (0..3) of head h
   const int64_t qoff = (bq * a.H + h) * (int64_t)kMD;
   if (a.nsplit > 1) {
     // partial: m (natural log units), l, unnormalised o
     float* wo = a.ws + ((bq * a.H + h) * a.nsplit + blockIdx.z) * (int64_t)kMD;
     float* wml = a.ws + (int64_t)a.B * a.Tq * a.H * a.nsplit * kMD + ((bq * a.H + h) * a.nsplit + blockIdx.z) * 2;
 #pragma unroll
-    for (int mt8 = 0; mt8 < 8; ++mt8)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int d = dh * 256 + mt8 * 32 + r4 * 8 + g32 * 4;
-        *(float4*)(wo + d) = make_float4(acc[mt8][r4 * 4], acc[mt8][r4 * 4 + 1], acc[mt8][r4 * 4 + 2],
-                                         acc[mt8][r4 * 4 + 3]);
-      }
-    if (dh == 0 && g32 == 0) {
+    for (int db = 0; db < 32; ++db)
+      *(float4*)(wo + 16 * db + 4 * G) = make_float4(acc[db][0], acc[db][1], acc[db][2], acc[db][3]);
+    if (G == 0) {
       wml[0] = mrun > -INFINITY ? mrun * kLn2 : -INFINITY;
       wml[1] = lrun;
     }
@@ -332,23 +411,21 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
     lse = (M + log2f(Z)) * kLn2;
   }
 #pragma unroll
-  for (int mt8 = 0; mt8 < 8; ++mt8)
+  for (int db = 0; db < 32; ++db) {
+    const int d = 16 * db + 4 * G;
+    float v[4];
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int d = dh * 256 + mt8 * 32 + r4 * 8 + g32 * 4;
-      float v[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = acc[mt8][r4 * 4 + i] * scale;
-      if (a.out_f32) {
-        *(float4*)((float*)a.out + qoff + d) = make_float4(v[0], v[1], v[2], v[3]);
-      } else {
-        u32x2 w;
-        w.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
-        w.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
-        *(u32x2*)((uint16_t*)a.out + qoff + d) = w;
-      }
+    for (int i = 0; i < 4; ++i) v[i] = acc[db][i] * scale;
+    if (a.out_f32) {
+      *(float4*)((float*)a.out + qoff + d) = make_float4(v[0], v[1], v[2], v[3]);
+    } else {
+      u32x2 w;
+      w.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+      w.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+      *(u32x2*)((uint16_t*)a.out + qoff + d) = w;
     }
-  if (a.lse && dh == 0 && g32 == 0) a.lse[bq * a.H + h] = lse;
+  }
+  if (a.lse && G == 0) a.lse[bq * a.H + h] = lse;
 }
 
 bool attn_mfma_eligible(int q_fmt, int H, int D, const csa_store& kv, bool has_prior) {
