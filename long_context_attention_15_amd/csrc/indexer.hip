@@ -20,65 +20,101 @@ constexpr int kMaxCand = 32768;      // merge: candidates per query
 constexpr int kMaxHI = 16;
 constexpr int kMaxDI = 64;
 
+// Wave-wide inclusive prefix sum / max / min in registers with DPP row
+// shifts and row broadcasts (no LDS round trips).  Lane 63 ends with the
+// total.
+template <int OP>   // 0: add, 1: max (unsigned), 2: min (unsigned)
+__device__ __forceinline__ uint32_t dpp_op(uint32_t a, uint32_t b) {
+  return OP == 0 ? a + b : (OP == 1 ? (a > b ? a : b) : (a < b ? a : b));
+}
+template <int OP>
+__device__ __forceinline__ uint32_t wave_scan(uint32_t x) {
+  constexpr uint32_t id = OP == 2 ? 0xffffffffu : 0u;
+  x = dpp_op<OP>(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x111, 0xf, 0xf, false));  // row_shr:1
+  x = dpp_op<OP>(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x112, 0xf, 0xf, false));  // row_shr:2
+  x = dpp_op<OP>(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x114, 0xf, 0xf, false));  // row_shr:4
+  x = dpp_op<OP>(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x118, 0xf, 0xf, false));  // row_shr:8
+  x = dpp_op<OP>(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  x = dpp_op<OP>(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return x;
+}
+template <int OP>
+__device__ __forceinline__ uint32_t wave_total(uint32_t x) {
+  return __builtin_amdgcn_readlane(wave_scan<OP>(x), 63);
+}
+
 struct SelShared {
-  uint32_t hist[2048];
+  uint32_t hist[256];
   uint32_t misc[4];
   uint32_t wtot[2][kIdxWaves];
 };
 
-// Exact radix select on keys[0, n): returns the kk-th largest key `thr` and
-// how many keys equal to thr are to be taken (the first ones by position).
-// Three passes over 11/11/10-bit digits, most significant first; each pass
+// Exact radix select on keys[0, n) (LDS or global memory; 0 = no entry):
+// returns the kk-th largest key `thr` and how many keys equal to thr are to
+// be taken (the first ones by position).  The bits above the highest bit in
+// which the smallest and largest keys differ are common to all keys; the
+// rest is resolved in 8-bit digits, most significant first: each pass
 // histograms the keys that match the digits found so far and one wavefront
-// locates the digit holding the kk-th key with a suffix scan.
+// locates the digit holding the kk-th key with a DPP prefix scan.
 // Needs 1 <= kk <= #nonzero keys.  Called by all kIdxThreads threads.
 __device__ void radix_select(const uint32_t* keys, int n, int kk, SelShared& sh, uint32_t& thr,
                              int& need_eq) {
-  const int tid = threadIdx.x, lane = tid % kWave;
-  uint32_t prefix = 0, mask = 0;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  uint32_t lo = 0xffffffffu, hi = 0u;
+  for (int i = tid; i < n; i += kIdxThreads) {
+    const uint32_t key = keys[i];
+    lo = (key != 0u && key < lo) ? key : lo;
+    hi = key > hi ? key : hi;
+  }
+  lo = wave_total<2>(lo);
+  hi = wave_total<1>(hi);
+  if (lane == 0) { sh.wtot[0][wave] = lo; sh.wtot[1][wave] = hi; }
+  __syncthreads();
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+  for (int w = 0; w < kIdxWaves; ++w) {
+    kmin = sh.wtot[0][w] < kmin ? sh.wtot[0][w] : kmin;
+    kmax = sh.wtot[1][w] > kmax ? sh.wtot[1][w] : kmax;
+  }
+  __syncthreads();
+  if (kmin >= kmax) { thr = kmax; need_eq = kk; return; }    // one distinct key value
+  int hb = 31 - __builtin_clz(kmin ^ kmax);
+  uint32_t mask = hb == 31 ? 0u : ~((2u << hb) - 1u);
+  uint32_t prefix = kmax & mask;
   int remaining = kk;
-  const int shifts[3] = {21, 10, 0};
-  const int widths[3] = {11, 11, 10};
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = shifts[pass];
-    const int nb = 1 << widths[pass];
-    const uint32_t dmask = (uint32_t)nb - 1u;
-    for (int i = tid; i < nb; i += kIdxThreads) sh.hist[i] = 0;
+  while (true) {
+    const int shift = hb >= 7 ? hb - 7 : 0;
+    for (int i = tid; i < 256; i += kIdxThreads) sh.hist[i] = 0u;
     __syncthreads();
     for (int i = tid; i < n; i += kIdxThreads) {
       const uint32_t key = keys[i];
-      if (key != 0u && (key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & dmask], 1u);
+      if (key != 0u && (key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
     }
     __syncthreads();
     if (tid < kWave) {
-      const int per = nb / kWave;            // 32 or 16 bins per lane
-      uint32_t local = 0;
-      for (int i = 0; i < per; ++i) local += sh.hist[per * lane + i];
-      uint32_t suf = local;                  // inclusive suffix sum over lanes >= lane
-#pragma unroll
-      for (int o = 1; o < kWave; o <<= 1) {
-        uint32_t t = __shfl_down(suf, o);
-        if (lane + o < kWave) suf += t;
-      }
-      uint32_t above = suf - local;          // keys in bins of higher lanes
-      if (above < (uint32_t)remaining && suf >= (uint32_t)remaining) {
-        for (int i = per - 1; i >= 0; --i) {
-          const uint32_t c = sh.hist[per * lane + i];
-          if (above + c >= (uint32_t)remaining) {
-            sh.misc[0] = per * lane + i;
-            sh.misc[1] = above;
+      // lane l holds bins [4 (63 - l), +4): the prefix scan counts this lane's bins and all higher ones
+      const uint4 h = *(const uint4*)(sh.hist + 4 * (kWave - 1 - lane));
+      const int local = (int)(h.x + h.y + h.z + h.w);
+      const int incl = (int)wave_scan<0>((uint32_t)local);
+      int ab = incl - local;
+      if (ab < remaining && incl >= remaining) {
+        const int c[4] = {(int)h.x, (int)h.y, (int)h.z, (int)h.w};
+        for (int j = 3; j >= 0; --j) {
+          if (ab + c[j] >= remaining) {
+            sh.misc[0] = 4 * (kWave - 1 - lane) + j;
+            sh.misc[1] = (uint32_t)ab;
             break;
           }
-          above += c;
+          ab += c[j];
         }
       }
     }
     __syncthreads();
-    const uint32_t d = sh.misc[0];
+    prefix |= sh.misc[0] << shift;
+    mask |= 255u << shift;
     remaining -= (int)sh.misc[1];
-    prefix |= d << shift;
-    mask |= dmask << shift;
     __syncthreads();
+    if (shift == 0) break;
+    hb = shift - 1;
   }
   thr = prefix;
   need_eq = remaining;
@@ -178,7 +214,18 @@ struct IdxArgs {
   int32_t* sel;
   uint32_t* ws_key;
   int32_t* ws_idx;
+  // long lists: per-query workspace block and the offsets inside it
+  uint8_t* ws;
+  size_t per_query, off_scores, off_uni, off_region, off_counts, off_skey, off_sidx;
+  int lm, nseg;
 };
+
+// visible entries of query bq
+__device__ __forceinline__ int64_t idx_visible(const IdxArgs& a, int64_t bq) {
+  const int64_t t = a.q_pos ? a.q_pos[bq] : (int64_t)(bq % a.Tq);
+  int64_t nt = t < 0 ? 0 : (t + 1) / a.m;
+  return nt > a.n_entries ? a.n_entries : nt;
+}
 
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(8))) int i32x8;
@@ -322,6 +369,35 @@ __device__ __forceinline__ void score_chunk_mfma(const IdxArgs& a, int b, int q,
   }
 }
 
+// Keys of entries [c0, c0 + cn) for one query into s_keys (LDS): MFMA for
+// FP8 / MXFP4, float32 FMAs for F32.  Called by all kIdxThreads threads.
+template <int FMT, int DI>
+__device__ __forceinline__ void score_chunk(const IdxArgs& a, int b, int q, int64_t bq, int64_t c0, int cn,
+                                            uint32_t* s_keys, float* s_q, float* s_w) {
+  const int tid = threadIdx.x;
+  if constexpr (FMT == CSA_F32) {
+    for (int h = tid; h < a.H_I; h += kIdxThreads) {
+      decode_row<FMT>(a.qidx, (int64_t)b * a.qidx.cap + (int64_t)q * a.H_I + h, DI, s_q + h * DI);
+      s_w[h] = a.head_w[bq * a.H_I + h];
+    }
+    __syncthreads();
+    for (int e = tid; e < cn; e += kIdxThreads) {
+      float kv[DI];
+      decode_row<FMT>(a.keys, (int64_t)b * a.keys.cap + c0 + e, DI, kv);
+      float s = 0.0f;
+      for (int h = 0; h < a.H_I; ++h) {
+        float dot = 0.0f;
+#pragma unroll
+        for (int d = 0; d < DI; ++d) dot = fmaf(s_q[h * DI + d], kv[d], dot);
+        s = fmaf(s_w[h], fmaxf(dot, 0.0f), s);
+      }
+      s_keys[e] = score_key(s);
+    }
+  } else {
+    score_chunk_mfma<FMT, DI>(a, b, q, bq, c0, cn, s_keys, s_w);
+  }
+}
+
 template <int FMT, int DI>
 __global__ __launch_bounds__(kIdxThreads) void idx_chunk_kernel(IdxArgs a) {
   extern __shared__ uint32_t s_keys[];
@@ -350,28 +426,7 @@ __global__ __launch_bounds__(kIdxThreads) void idx_chunk_kernel(IdxArgs a) {
   }
   if (kk == 0) return;                        // uniform over the workgroup
 
-  if constexpr (FMT == CSA_F32) {
-    // queries and head weights
-    for (int h = tid; h < a.H_I; h += kIdxThreads) {
-      decode_row<FMT>(a.qidx, (int64_t)b * a.qidx.cap + (int64_t)q * a.H_I + h, DI, s_q + h * DI);
-      s_w[h] = a.head_w[bq * a.H_I + h];
-    }
-    __syncthreads();
-    for (int e = tid; e < cn; e += kIdxThreads) {
-      float kv[DI];
-      decode_row<FMT>(a.keys, (int64_t)b * a.keys.cap + c0 + e, DI, kv);
-      float s = 0.0f;
-      for (int h = 0; h < a.H_I; ++h) {
-        float dot = 0.0f;
-#pragma unroll
-        for (int d = 0; d < DI; ++d) dot = fmaf(s_q[h * DI + d], kv[d], dot);
-        s = fmaf(s_w[h], fmaxf(dot, 0.0f), s);
-      }
-      s_keys[e] = score_key(s);
-    }
-  } else {
-    score_chunk_mfma<FMT, DI>(a, b, q, bq, c0, cn, s_keys, s_w);
-  }
+  score_chunk<FMT, DI>(a, b, q, bq, c0, cn, s_keys, s_q, s_w);
   __syncthreads();
 
   uint32_t thr;
@@ -464,29 +519,6 @@ __device__ __forceinline__ uint4 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
 
 // LDS accesses of this wavefront issued so far complete before later ones.
 __device__ __forceinline__ void lds_wave_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
-
-// Wave-wide inclusive prefix sum / max / min in registers with DPP row
-// shifts and row broadcasts (no LDS round trips).  Lane 63 ends with the
-// total.
-template <int OP>   // 0: add, 1: max (unsigned), 2: min (unsigned)
-__device__ __forceinline__ uint32_t dpp_op(uint32_t a, uint32_t b) {
-  return OP == 0 ? a + b : (OP == 1 ? (a > b ? a : b) : (a < b ? a : b));
-}
-template <int OP>
-__device__ __forceinline__ uint32_t wave_scan(uint32_t x) {
-  constexpr uint32_t id = OP == 2 ? 0xffffffffu : 0u;
-  x = dpp_op<OP>(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x111, 0xf, 0xf, false));  // row_shr:1
-  x = dpp_op<OP>(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x112, 0xf, 0xf, false));  // row_shr:2
-  x = dpp_op<OP>(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x114, 0xf, 0xf, false));  // row_shr:4
-  x = dpp_op<OP>(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x118, 0xf, 0xf, false));  // row_shr:8
-  x = dpp_op<OP>(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x142, 0xa, 0xf, false));  // row_bcast:15
-  x = dpp_op<OP>(x, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, 0x143, 0xc, 0xf, false));  // row_bcast:31
-  return x;
-}
-template <int OP>
-__device__ __forceinline__ uint32_t wave_total(uint32_t x) {
-  return __builtin_amdgcn_readlane(wave_scan<OP>(x), 63);
-}
 
 // max(x, 0) on the bit pattern: negative floats (and -0) become +0.
 __device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
@@ -878,16 +910,219 @@ static hipError_t launch_idx_stream(const IdxArgs& ia, hipStream_t st) {
   return hipGetLastError();
 }
 
+// ------------------------------------------------------ long lists (decode)
+//
+// Few queries over many entries (decode at long context).  Three kernels,
+// exact, reading each key once at full HBM rate:
+//   A  chunks of kLChunk entries: the keys of the chunk's scores go to the
+//      workspace, and the largest key of each of kLUnion strided subsets of
+//      the chunk joins the "union" (each is a real entry);
+//   T  per query: T = the k-th largest key of the union.  At least k
+//      entries have a key >= T, so T is at most the k-th largest key overall
+//      and every member of the top-k has a key >= T;
+//   B  per (query, segment of kLSeg entries): the segment's entries with
+//      key >= T are compacted, in index order, into the segment's region;
+//   C  per query: the regions, concatenated in segment order (= index
+//      order), hold every candidate; the exact top-k (ties to the smaller
+//      index) is selected from them and emitted in ascending index order.
+constexpr int kLChunk = 4096;
+constexpr int kLSeg = 16384;
+constexpr int kLUnion = 128;                  // union keys per chunk (strided-set maxima)
+constexpr int kLUnionLds = 32768;             // union keys per query (128 KiB of LDS)
+
+template <int FMT, int DI>
+__global__ __launch_bounds__(kIdxThreads) void idx_long_score_kernel(IdxArgs a) {
+  extern __shared__ uint32_t s_keys[];
+  __shared__ float s_q[kMaxHI * kMaxDI];
+  __shared__ float s_w[kMaxHI];
+  __shared__ SelShared sh;
+  const int tid = threadIdx.x;
+  const int64_t bq = blockIdx.x;
+  const int b = (int)(bq / a.Tq), q = (int)(bq % a.Tq);
+  const int c = blockIdx.y;
+  const int64_t nt = idx_visible(a, bq);
+  const int64_t c0 = (int64_t)c * kLChunk;
+  const int64_t cn64 = nt - c0;
+  const int cn = cn64 < 0 ? 0 : (cn64 > kLChunk ? kLChunk : (int)cn64);
+  uint8_t* wq = a.ws + bq * a.per_query;
+  uint32_t* scores = (uint32_t*)(wq + a.off_scores);
+  uint32_t* uni = (uint32_t*)(wq + a.off_uni) + (int64_t)c * a.lm;
+  if (cn == 0) {                                // uniform
+    for (int i = tid; i < a.lm; i += kIdxThreads) uni[i] = 0u;
+    return;
+  }
+  score_chunk<FMT, DI>(a, b, q, bq, c0, cn, s_keys, s_q, s_w);
+  __syncthreads();
+  for (int i = tid; i < cn; i += kIdxThreads) scores[c0 + i] = s_keys[i];
+  // union: the largest key of each strided set {r + lm j} of the chunk (a
+  // real entry, 0 if the set is empty)
+  for (int r = tid; r < a.lm; r += kIdxThreads) {
+    uint32_t mx = 0u;
+    for (int e = r; e < cn; e += a.lm) mx = s_keys[e] > mx ? s_keys[e] : mx;
+    uni[r] = mx;
+  }
+}
+
+// Per query: T = the k-th largest key of the union (0 when the union holds
+// fewer than k entries: then every entry is a candidate).
+__global__ __launch_bounds__(kIdxThreads) void idx_long_thr_kernel(IdxArgs a) {
+  extern __shared__ uint32_t s_uni[];
+  __shared__ SelShared sh;
+  __shared__ uint32_t s_cnt;
+  const int tid = threadIdx.x;
+  const int64_t bq = blockIdx.x;
+  uint8_t* wq = a.ws + bq * a.per_query;
+  const uint32_t* uni = (const uint32_t*)(wq + a.off_uni);
+  uint32_t* thr_out = (uint32_t*)(wq + a.off_counts) + a.nseg;
+  const int nu = a.nchunk * a.lm;
+  if (tid == 0) s_cnt = 0u;
+  __syncthreads();
+  uint32_t mine = 0;
+  for (int i = tid; i < nu; i += kIdxThreads) {
+    const uint32_t key = uni[i];
+    s_uni[i] = key;
+    mine += key != 0u;
+  }
+  atomicAdd(&s_cnt, mine);
+  __syncthreads();
+  uint32_t T = 0u;
+  if ((int)s_cnt >= a.k) {
+    int need_eq;
+    radix_select(s_uni, nu, a.k, sh, T, need_eq);
+  }
+  if (tid == 0) *thr_out = T;
+}
+
+__global__ __launch_bounds__(kIdxThreads) void idx_long_compact_kernel(IdxArgs a) {
+  __shared__ SelShared sh;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int64_t bq = blockIdx.x;
+  const int seg = blockIdx.y;
+  const int64_t nt = idx_visible(a, bq);
+  uint8_t* wq = a.ws + bq * a.per_query;
+  const uint32_t* scores = (const uint32_t*)(wq + a.off_scores);
+  uint32_t* counts = (uint32_t*)(wq + a.off_counts);
+  uint2* region = (uint2*)(wq + a.off_region);
+  const int64_t s0 = (int64_t)seg * kLSeg;
+  const int64_t s1 = nt < s0 + kLSeg ? nt : s0 + kLSeg;
+  if (s1 <= s0 || nt <= a.k) {                  // uniform; short lists need no candidates
+    if (tid == 0) counts[seg] = 0u;
+    return;
+  }
+  const uint32_t T = counts[a.nseg];           // from idx_long_thr_kernel
+  // compaction in index order: wave w owns a contiguous range of the segment
+  const int len = (int)(s1 - s0);
+  const int per = ((len + kIdxWaves * kWave - 1) / (kIdxWaves * kWave)) * kWave;
+  const int p0 = wave * per, p1 = p0 + per < len ? p0 + per : len;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  uint32_t n_mine = 0;
+  for (int r0 = p0; r0 < p1; r0 += kWave) {
+    const int pos = r0 + lane;
+    const bool take = pos < p1 && scores[s0 + pos] >= T;
+    n_mine += (uint32_t)__popcll(__ballot(take));
+  }
+  if (lane == 0) sh.wtot[0][wave] = n_mine;
+  __syncthreads();
+  uint32_t base = 0;
+  for (int w = 0; w < wave; ++w) base += sh.wtot[0][w];
+  for (int r0 = p0; r0 < p1; r0 += kWave) {
+    const int pos = r0 + lane;
+    const uint32_t key = pos < p1 ? scores[s0 + pos] : 0u;
+    const bool take = pos < p1 && key >= T;
+    const uint64_t bt = __ballot(take);
+    if (take) region[s0 + base + __popcll(bt & lt)] = make_uint2(key, (uint32_t)(s0 + pos));
+    base += (uint32_t)__popcll(bt);
+  }
+  if (wave == kIdxWaves - 1 && lane == 0) counts[seg] = base;
+}
+
+constexpr int kLFinalLds = 8192;
+
+__global__ __launch_bounds__(kIdxThreads) void idx_long_final_kernel(IdxArgs a) {
+  __shared__ uint32_t s_cand[kLFinalLds];
+  __shared__ SelShared sh;
+  __shared__ uint32_t s_pre[kIdxThreads + 1];
+  const int tid = threadIdx.x;
+  const int64_t bq = blockIdx.x;
+  const int64_t nt = idx_visible(a, bq);
+  int32_t* out = a.sel + bq * a.k;
+  if (nt <= a.k) {
+    for (int i = tid; i < a.k; i += kIdxThreads) out[i] = i < nt ? i : -1;
+    return;
+  }
+  uint8_t* wq = a.ws + bq * a.per_query;
+  const uint32_t* counts = (const uint32_t*)(wq + a.off_counts);
+  const uint2* region = (const uint2*)(wq + a.off_region);
+  uint32_t* skey = (uint32_t*)(wq + a.off_skey);
+  int32_t* sidx = (int32_t*)(wq + a.off_sidx);
+  // segment offsets in the concatenated candidate list
+  for (int s0 = 0; s0 < a.nseg; s0 += kIdxThreads) {
+    if (tid == 0) {
+      uint32_t run = s0 == 0 ? 0u : s_pre[kIdxThreads];
+      for (int i = 0; i < kIdxThreads && s0 + i < a.nseg; ++i) {
+        s_pre[i] = run;
+        run += counts[s0 + i];
+      }
+      s_pre[kIdxThreads] = run;
+    }
+    __syncthreads();
+    for (int i = 0; i < kIdxThreads && s0 + i < a.nseg; ++i) {
+      const uint32_t cnt = counts[s0 + i], off = s_pre[i];
+      const uint2* rg = region + (int64_t)(s0 + i) * kLSeg;
+      for (uint32_t j = tid; j < cnt; j += kIdxThreads) {
+        const uint2 v = rg[j];
+        skey[off + j] = v.x;
+        sidx[off + j] = (int32_t)v.y;
+      }
+    }
+    __syncthreads();
+  }
+  const int ncand = (int)s_pre[kIdxThreads];
+  const int kk = ncand < a.k ? ncand : a.k;
+  for (int i = kk + tid; i < a.k; i += kIdxThreads) out[i] = -1;
+  if (kk == 0) return;
+  // select from an LDS copy when the candidates fit (the usual case: about k)
+  const uint32_t* keys = skey;
+  if (ncand <= kLFinalLds) {
+    for (int i = tid; i < ncand; i += kIdxThreads) s_cand[i] = skey[i];
+    __syncthreads();
+    keys = s_cand;
+  }
+  uint32_t thr;
+  int need_eq;
+  radix_select(keys, ncand, kk, sh, thr, need_eq);
+  emit_selected(keys, ncand, thr, need_eq, sh, [&](int pos, int rank) { out[rank] = sidx[pos]; });
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 IdxPlan indexer_plan(int B, int Tq, int64_t n_entries, int k) {
-  IdxPlan p{0, 0, 0, false};
-  if (n_entries <= 0) { p.chunk = 1024; p.nchunk = 1; p.ok = true; return p; }
-  int64_t chunk = 1024;
+  IdxPlan p{};
   const int64_t queries = (int64_t)B * Tq;
-  // many queries: one chunk per query when it fits; few queries (decode):
-  // chunks of at most 8192 entries for more workgroups
-  const int64_t target = queries >= 256 ? n_entries : (n_entries < 8192 ? n_entries : 8192);
-  while (chunk < target && chunk < kMaxChunk) chunk <<= 1;
-  // the merge keeps nchunk * k candidates in LDS
+  if (n_entries <= 0) { p.chunk = 1024; p.nchunk = 1; p.ok = true; return p; }
+  if (queries < 256 && n_entries > 8192) {
+    // long lists: score / compact / final select
+    p.mode = 1;
+    p.nchunk = (int)((n_entries + kLChunk - 1) / kLChunk);
+    p.lm = kLUnion;
+    if ((int64_t)p.nchunk * p.lm > kLUnionLds) return p;       // union must fit the LDS of the T kernel
+    p.nseg = (int)((n_entries + kLSeg - 1) / kLSeg);
+    const size_t npad = align256((size_t)p.nseg * kLSeg);
+    p.off_scores = 0;
+    p.off_uni = align256(npad * 4);
+    p.off_region = p.off_uni + align256((size_t)p.nchunk * p.lm * 4);
+    p.off_counts = p.off_region + npad * 8;
+    p.off_skey = p.off_counts + align256((size_t)(p.nseg + 1) * 4);
+    p.off_sidx = p.off_skey + npad * 4;
+    p.per_query = p.off_sidx + npad * 4;
+    p.chunk = kLChunk;
+    p.ws = (size_t)queries * p.per_query;
+    p.ok = true;
+    return p;
+  }
+  int64_t chunk = 1024;
+  // one chunk per query when it fits, else chunks whose local top-k lists are merged
+  while (chunk < n_entries && chunk < kMaxChunk) chunk <<= 1;
   while ((n_entries + chunk - 1) / chunk * (int64_t)k > kMaxCand && chunk < kMaxChunk) chunk <<= 1;
   const int64_t nch = (n_entries + chunk - 1) / chunk;
   if (nch > 1 && nch * (int64_t)k > kMaxCand) return p;
@@ -896,6 +1131,26 @@ IdxPlan indexer_plan(int B, int Tq, int64_t n_entries, int k) {
   p.ws = nch > 1 ? (size_t)queries * nch * k * 8 : 0;
   p.ok = true;
   return p;
+}
+
+template <int FMT, int DI>
+static hipError_t launch_idx_long(const IdxArgs& a, hipStream_t st) {
+  const unsigned nq = (unsigned)((int64_t)a.B * a.Tq);
+  auto ka = idx_long_score_kernel<FMT, DI>;
+  hipLaunchKernelGGL(ka, dim3(nq, a.nchunk), dim3(kIdxThreads), kLChunk * 4, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const size_t lds = (size_t)a.nchunk * a.lm * 4;
+  e = hipFuncSetAttribute((const void*)idx_long_thr_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(idx_long_thr_kernel, dim3(nq), dim3(kIdxThreads), lds, st, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(idx_long_compact_kernel, dim3(nq, a.nseg), dim3(kIdxThreads), 0, st, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(idx_long_final_kernel, dim3(nq), dim3(kIdxThreads), 0, st, a);
+  return hipGetLastError();
 }
 
 template <int FMT, int DI>
@@ -925,6 +1180,10 @@ hipError_t launch_indexer(const csa_store& qidx, const float* head_w, const csa_
   a.q_pos = q_pos;
   a.B = B; a.Tq = Tq; a.H_I = H_I; a.m = m; a.k = k;
   a.chunk = plan.chunk; a.nchunk = plan.nchunk;
+  a.ws = (uint8_t*)ws;
+  a.per_query = plan.per_query; a.off_scores = plan.off_scores; a.off_uni = plan.off_uni;
+  a.off_region = plan.off_region; a.off_counts = plan.off_counts; a.off_skey = plan.off_skey;
+  a.off_sidx = plan.off_sidx; a.lm = plan.lm; a.nseg = plan.nseg;
   a.sel = sel;
   const size_t half = plan.ws / 2;
   a.ws_key = (uint32_t*)ws;
@@ -932,6 +1191,14 @@ hipError_t launch_indexer(const csa_store& qidx, const float* head_w, const csa_
   if ((int64_t)B * Tq == 0) return hipSuccess;
   if (indexer_stream_ok(keys, H_I, B, Tq, n_entries, k)) return launch_idx_stream(a, st);
   const int d = keys.dim;
+  if (plan.mode == 1) {
+    switch (keys.fmt) {
+      case CSA_F32: return d == 32 ? launch_idx_long<CSA_F32, 32>(a, st) : launch_idx_long<CSA_F32, 64>(a, st);
+      case CSA_FP8_E4M3:
+        return d == 32 ? launch_idx_long<CSA_FP8_E4M3, 32>(a, st) : launch_idx_long<CSA_FP8_E4M3, 64>(a, st);
+      default: return d == 32 ? launch_idx_long<CSA_MXFP4, 32>(a, st) : launch_idx_long<CSA_MXFP4, 64>(a, st);
+    }
+  }
   switch (keys.fmt) {
     case CSA_F32: return d == 32 ? launch_idx_t<CSA_F32, 32>(a, st) : launch_idx_t<CSA_F32, 64>(a, st);
     case CSA_FP8_E4M3: return d == 32 ? launch_idx_t<CSA_FP8_E4M3, 32>(a, st) : launch_idx_t<CSA_FP8_E4M3, 64>(a, st);

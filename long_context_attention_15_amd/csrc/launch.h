@@ -18,8 +18,11 @@ int compress_max_m();
 struct IdxPlan {
   int chunk;      // entries scored per workgroup
   int nchunk;     // chunks per query
-  size_t ws;      // workspace bytes (0 when nchunk == 1)
+  size_t ws;      // workspace bytes
   bool ok;
+  int mode;       // 0: chunk(s) + merge, 1: long lists (score / compact / select)
+  int lm, nseg;   // long lists: union keys per chunk, segments per query
+  size_t per_query, off_scores, off_uni, off_region, off_counts, off_skey, off_sidx;
 };
 IdxPlan indexer_plan(int B, int Tq, int64_t n_entries, int k);
 // Many queries over FP8 keys of 64 dims: the single-pass streaming top-k,

@@ -211,6 +211,31 @@ def test_indexer_stream_exact_ties(lib, k):
         assert np.array_equal(sel[0, i], want), f"query {i} at {pos[0][i]}"
 
 
+@pytest.mark.parametrize("N,k", [(20000, 512), (50000, 1024)])
+def test_indexer_long_list_exact_ties(lib, N, k):
+    """Few queries over many entries (the decode path: chunk scores, union
+    threshold, compaction, final select) with integer-valued inputs: exact
+    scores, massive ties including exact zeros; the sets must equal the
+    oracle's, smaller index first."""
+    B, Tq, H_I, d_I, m = 2, 3, 8, 64, 4
+    rng = np.random.default_rng(13)
+    keys = rng.integers(-2, 3, (B, N, d_I)).astype(np.float64)
+    keys[:, :, 0] = 2.0
+    q = rng.integers(-1, 2, (B, Tq * H_I, d_I)).astype(np.float64)
+    q[:, :, 1] = 1.0
+    w = np.ones((B, Tq, H_I), np.float32)
+    kst, kdeq = Hx.upload_store(keys, "fp8")
+    qst, qdeq = Hx.upload_store(q, "fp8")
+    pos = [[m * N + 2, m * N // 2 + 1, m * k - 1], [m * N - 1, m * 3000 + 3, 5]]
+    sel = _run_indexer(lib, kst, qst, w, N, pos, B, Tq, H_I, m, k)
+    qd = q.reshape(B, Tq, H_I, d_I)
+    for b in range(B):
+        for i in range(Tq):
+            nt = int(O.n_visible(pos[b][i], m, N))
+            want = O.topk_select(O.indexer_scores(qd[b, i], w[b, i], keys[b, :nt]), k)
+            assert np.array_equal(sel[b, i], want), f"sequence {b} query {i}"
+
+
 def test_indexer_no_visible_entries_and_k_above_count(lib):
     B, T, N, H_I, d_I, m, k = 1, 40, 10, 2, 64, 4, 16
     kst, kdeq, qst, qdeq, w = _indexer_inputs(B, T, N, H_I, d_I, "fp8", seed_shift=2)
