@@ -43,8 +43,10 @@ __device__ __forceinline__ uint32_t wave_total(uint32_t x) {
   return __builtin_amdgcn_readlane(wave_scan<OP>(x), 63);
 }
 
+constexpr int kHistCopies = 8;                // histogram copies (lane & 7) against same-bin atomics
+
 struct SelShared {
-  uint32_t hist[256];
+  uint32_t hist[256 * kHistCopies];
   uint32_t misc[4];
   uint32_t wtot[2][kIdxWaves];
 };
@@ -83,16 +85,28 @@ __device__ void radix_select(const uint32_t* keys, int n, int kk, SelShared& sh,
   int remaining = kk;
   while (true) {
     const int shift = hb >= 7 ? hb - 7 : 0;
-    for (int i = tid; i < 256; i += kIdxThreads) sh.hist[i] = 0u;
+    for (int i = tid; i < 256 * kHistCopies; i += kIdxThreads) sh.hist[i] = 0u;
     __syncthreads();
+    const uint32_t copy = (uint32_t)tid & (kHistCopies - 1);
     for (int i = tid; i < n; i += kIdxThreads) {
       const uint32_t key = keys[i];
-      if (key != 0u && (key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
+      if (key != 0u && (key & mask) == prefix)
+        atomicAdd(&sh.hist[((key >> shift) & 255u) * kHistCopies + copy], 1u);
     }
     __syncthreads();
     if (tid < kWave) {
       // lane l holds bins [4 (63 - l), +4): the prefix scan counts this lane's bins and all higher ones
-      const uint4 h = *(const uint4*)(sh.hist + 4 * (kWave - 1 - lane));
+      uint4 h = make_uint4(0u, 0u, 0u, 0u);
+      const uint32_t* hb0 = sh.hist + 4 * (kWave - 1 - lane) * kHistCopies;
+#pragma unroll
+      for (int cpy = 0; cpy < kHistCopies; cpy += 4) {
+        const uint4 x0 = *(const uint4*)(hb0 + cpy), x1 = *(const uint4*)(hb0 + kHistCopies + cpy);
+        const uint4 x2 = *(const uint4*)(hb0 + 2 * kHistCopies + cpy), x3 = *(const uint4*)(hb0 + 3 * kHistCopies + cpy);
+        h.x += x0.x + x0.y + x0.z + x0.w;
+        h.y += x1.x + x1.y + x1.z + x1.w;
+        h.z += x2.x + x2.y + x2.z + x2.w;
+        h.w += x3.x + x3.y + x3.z + x3.w;
+      }
       const int local = (int)(h.x + h.y + h.z + h.w);
       const int incl = (int)wave_scan<0>((uint32_t)local);
       int ab = incl - local;
@@ -295,22 +309,23 @@ __device__ __forceinline__ void score_chunk_mfma(const IdxArgs& a, int b, int q,
     for (int grp0 = wave * U; grp0 < ngroups; grp0 += kIdxWaves * U) {
       long long kb0[U], kb1[U];
       float sk[U];
+      // every load is issued (rows past the chunk read its last row, their
+      // scores are never stored) so that all of them are in flight together
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int e = (grp0 + u) * 16 + col;
-        kb0[u] = 0; kb1[u] = 0; sk[u] = 0.0f;
-        if (e < cn) {
-          const uint8_t* kp = a.keys.rows + (krow0 + e) * a.keys.row_bytes;
-          if (DI == 64) {
-            const uint4 v = *(const uint4*)(kp + 16 * g);
-            kb0[u] = (long long)(((unsigned long long)v.y << 32) | v.x);
-            kb1[u] = (long long)(((unsigned long long)v.w << 32) | v.z);
-          } else {
-            const uint2 v = *(const uint2*)(kp + 8 * g);
-            kb0[u] = (long long)(((unsigned long long)v.y << 32) | v.x);
-          }
-          sk[u] = ksc[krow0 + e];
+        int e = (grp0 + u) * 16 + col;
+        e = e < cn ? e : cn - 1;
+        const uint8_t* kp = a.keys.rows + (krow0 + e) * a.keys.row_bytes;
+        if (DI == 64) {
+          const uint4 v = *(const uint4*)(kp + 16 * g);
+          kb0[u] = (long long)(((unsigned long long)v.y << 32) | v.x);
+          kb1[u] = (long long)(((unsigned long long)v.w << 32) | v.z);
+        } else {
+          const uint2 v = *(const uint2*)(kp + 8 * g);
+          kb0[u] = (long long)(((unsigned long long)v.y << 32) | v.x);
+          kb1[u] = 0;
         }
+        sk[u] = ksc[krow0 + e];
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -343,14 +358,14 @@ __device__ __forceinline__ void score_chunk_mfma(const IdxArgs& a, int b, int q,
       int ks[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int e = (grp0 + u) * 16 + col;
-        kv[u] = make_uint4(0u, 0u, 0u, 0u);
-        ks[u] = 127;
-        if (e < cn && g < DI / 32) {
-          const uint8_t* kp = a.keys.rows + (krow0 + e) * a.keys.row_bytes;
-          kv[u] = *(const uint4*)(kp + 16 * g);
-          ks[u] = ksc[(krow0 + e) * (DI / 32) + g];
-        }
+        int e = (grp0 + u) * 16 + col;
+        e = e < cn ? e : cn - 1;
+        const int gg = g < DI / 32 ? g : 0;
+        const uint8_t* kp = a.keys.rows + (krow0 + e) * a.keys.row_bytes;
+        const uint4 v = *(const uint4*)(kp + 16 * gg);
+        const int sv = ksc[(krow0 + e) * (DI / 32) + gg];
+        kv[u] = g < DI / 32 ? v : make_uint4(0u, 0u, 0u, 0u);
+        ks[u] = g < DI / 32 ? sv : 127;
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -363,6 +378,121 @@ __device__ __forceinline__ void score_chunk_mfma(const IdxArgs& a, int b, int q,
         for (int i = 0; i < 4; ++i) v = fmaf(wl[i], fmaxf(c[i], 0.0f), v);
         v += __shfl_xor(v, 16);
         v += __shfl_xor(v, 32);
+        if (g == 0 && e < cn) s_keys[e] = score_key(v);
+      }
+    }
+  }
+}
+
+// Scores of entries [c0, c0 + cn) for one query with 64-dim keys on 32x32
+// MFMA tiles: rows = heads (H_I <= 8 of 32, the rest zero), 32 entries as
+// columns, so a lane holds 4 heads of one entry and one permlane32 swap adds
+// the other 4.  FP8: codes convert exactly to BF16 for four
+// v_mfma_f32_32x32x16_bf16 steps, lane group g taking dims [32 g, 32 g + 32)
+// (the q row scales fold into the head weights, the key scale multiplies the
+// sum).  MXFP4: one v_mfma_scale_f32_32x32x64_f8f6f4 with E2M1 operands, lane
+// group g holding the 32-element block g and its E8M0 scale.
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8s;
+typedef __attribute__((ext_vector_type(16))) float f32x16s;
+
+template <int FMT>
+__device__ __forceinline__ void score_chunk_mfma32(const IdxArgs& a, int b, int q, int64_t bq, int64_t c0, int cn,
+                                                   uint32_t* s_keys) {
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int64_t qrow0 = (int64_t)b * a.qidx.cap + (int64_t)q * a.H_I;
+  // head weights of this lane's accumulator rows 4 g .. 4 g + 3
+  float wl[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * g + i;
+    float w = 0.0f;
+    if (h < a.H_I) {
+      w = a.head_w[bq * a.H_I + h];
+      if (FMT == CSA_FP8_E4M3) w *= ((const float*)a.qidx.scales)[qrow0 + h];
+    }
+    wl[i] = w;
+  }
+  const bool hrow = l32 < a.H_I;
+  const uint8_t* qp = a.qidx.rows + (qrow0 + (hrow ? l32 : 0)) * a.qidx.row_bytes;
+  const int64_t krow0 = (int64_t)b * a.keys.cap + c0;
+  const int ngroups = (cn + 31) / 32;
+  constexpr int U = 4;                          // groups of 32 entries in flight per wave
+  if constexpr (FMT == CSA_FP8_E4M3) {
+    bf16x8s qa[4];
+    {
+      const uint4 v0 = hrow ? *(const uint4*)(qp + 32 * g) : make_uint4(0u, 0u, 0u, 0u);
+      const uint4 v1 = hrow ? *(const uint4*)(qp + 32 * g + 16) : make_uint4(0u, 0u, 0u, 0u);
+      qa[0] = fp8x8_bf16((long long)(((unsigned long long)v0.y << 32) | v0.x));
+      qa[1] = fp8x8_bf16((long long)(((unsigned long long)v0.w << 32) | v0.z));
+      qa[2] = fp8x8_bf16((long long)(((unsigned long long)v1.y << 32) | v1.x));
+      qa[3] = fp8x8_bf16((long long)(((unsigned long long)v1.w << 32) | v1.z));
+    }
+    const float* ksc = (const float*)a.keys.scales;
+    for (int grp0 = wave * U; grp0 < ngroups; grp0 += kIdxWaves * U) {
+      uint4 k0[U], k1[U];
+      float sk[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {             // every load issued (rows past the chunk read its last row)
+        int e = (grp0 + u) * 32 + l32;
+        e = e < cn ? e : cn - 1;
+        const uint8_t* kp = a.keys.rows + (krow0 + e) * a.keys.row_bytes + 32 * g;
+        k0[u] = *(const uint4*)kp;
+        k1[u] = *(const uint4*)(kp + 16);
+        sk[u] = ksc[krow0 + e];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        f32x16s acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+        const uint32_t wv[8] = {k0[u].x, k0[u].y, k0[u].z, k0[u].w, k1[u].x, k1[u].y, k1[u].z, k1[u].w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bf16x8s kb = fp8x8_bf16((long long)(((unsigned long long)wv[2 * j + 1] << 32) | wv[2 * j]));
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[j], kb, acc, 0, 0, 0);
+        }
+        float v = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v = fmaf(wl[i], fmaxf(acc[i], 0.0f), v);
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        const int e = (grp0 + u) * 32 + l32;
+        if (g == 0 && e < cn) s_keys[e] = score_key(v * sk[u]);
+      }
+    }
+  } else {
+    i32x8 qa = {0, 0, 0, 0, 0, 0, 0, 0};
+    int qs = 127;
+    if (hrow) {
+      const uint4 v = *(const uint4*)(qp + 16 * g);
+      qa[0] = (int)v.x; qa[1] = (int)v.y; qa[2] = (int)v.z; qa[3] = (int)v.w;
+      qs = ((const uint8_t*)a.qidx.scales)[(qrow0 + l32) * 2 + g];
+    }
+    const uint8_t* ksc = (const uint8_t*)a.keys.scales;
+    for (int grp0 = wave * U; grp0 < ngroups; grp0 += kIdxWaves * U) {
+      uint4 kv[U];
+      int ks[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        int e = (grp0 + u) * 32 + l32;
+        e = e < cn ? e : cn - 1;
+        kv[u] = *(const uint4*)(a.keys.rows + (krow0 + e) * a.keys.row_bytes + 16 * g);
+        ks[u] = ksc[(krow0 + e) * 2 + g];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        f32x16s acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+        const i32x8 kb = {(int)kv[u].x, (int)kv[u].y, (int)kv[u].z, (int)kv[u].w, 0, 0, 0, 0};
+        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa, kb, acc, 4, 4, 0, qs, 0, ks[u]);
+        float v = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v = fmaf(wl[i], fmaxf(acc[i], 0.0f), v);
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+        v = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        const int e = (grp0 + u) * 32 + l32;
         if (g == 0 && e < cn) s_keys[e] = score_key(v);
       }
     }
@@ -392,6 +522,12 @@ __device__ __forceinline__ void score_chunk(const IdxArgs& a, int b, int q, int6
         s = fmaf(s_w[h], fmaxf(dot, 0.0f), s);
       }
       s_keys[e] = score_key(s);
+    }
+  } else if constexpr (DI == 64) {
+    if (a.H_I <= 8) {
+      score_chunk_mfma32<FMT>(a, b, q, bq, c0, cn, s_keys);
+    } else {
+      score_chunk_mfma<FMT, DI>(a, b, q, bq, c0, cn, s_keys, s_w);
     }
   } else {
     score_chunk_mfma<FMT, DI>(a, b, q, bq, c0, cn, s_keys, s_w);
@@ -915,20 +1051,23 @@ static hipError_t launch_idx_stream(const IdxArgs& ia, hipStream_t st) {
 // Few queries over many entries (decode at long context).  Three kernels,
 // exact, reading each key once at full HBM rate:
 //   A  chunks of kLChunk entries: the keys of the chunk's scores go to the
-//      workspace, and the largest key of each of kLUnion strided subsets of
-//      the chunk joins the "union" (each is a real entry);
-//   T  per query: T = the k-th largest key of the union.  At least k
-//      entries have a key >= T, so T is at most the k-th largest key overall
-//      and every member of the top-k has a key >= T;
-//   B  per (query, segment of kLSeg entries): the segment's entries with
-//      key >= T are compacted, in index order, into the segment's region;
+//      workspace, and so do the kLTop largest of the maxima of kLSets
+//      strided subsets of the chunk (each maximum is a real entry);
+//   B  per (query, segment of kLSeg entries): T = the smallest, over the
+//      chunks whose subsets are all nonempty, of their m-th largest subset
+//      maximum, m = ceil(k / #such chunks).  Each such chunk has at least m
+//      entries >= T, so at least k entries have a key >= T: T is at most the
+//      k-th largest key and every member of the top-k has a key >= T.  The
+//      segment's entries with key >= T are compacted, in index order, into
+//      the segment's region;
 //   C  per query: the regions, concatenated in segment order (= index
 //      order), hold every candidate; the exact top-k (ties to the smaller
 //      index) is selected from them and emitted in ascending index order.
 constexpr int kLChunk = 4096;
 constexpr int kLSeg = 16384;
-constexpr int kLUnion = 128;                  // union keys per chunk (strided-set maxima)
-constexpr int kLUnionLds = 32768;             // union keys per query (128 KiB of LDS)
+constexpr int kLPerWave = kLSeg / kIdxWaves;  // segment entries per wave in the compaction
+constexpr int kLSets = 128;                   // strided sets per chunk
+constexpr int kLTop = 32;                     // largest set maxima kept per chunk
 
 template <int FMT, int DI>
 __global__ __launch_bounds__(kIdxThreads) void idx_long_score_kernel(IdxArgs a) {
@@ -947,50 +1086,35 @@ __global__ __launch_bounds__(kIdxThreads) void idx_long_score_kernel(IdxArgs a) 
   uint8_t* wq = a.ws + bq * a.per_query;
   uint32_t* scores = (uint32_t*)(wq + a.off_scores);
   uint32_t* uni = (uint32_t*)(wq + a.off_uni) + (int64_t)c * a.lm;
-  if (cn == 0) {                                // uniform
-    for (int i = tid; i < a.lm; i += kIdxThreads) uni[i] = 0u;
-    return;
-  }
+  if (cn == 0) return;                          // uniform (such chunks are never read)
   score_chunk<FMT, DI>(a, b, q, bq, c0, cn, s_keys, s_q, s_w);
   __syncthreads();
   for (int i = tid; i < cn; i += kIdxThreads) scores[c0 + i] = s_keys[i];
-  // union: the largest key of each strided set {r + lm j} of the chunk (a
-  // real entry, 0 if the set is empty)
-  for (int r = tid; r < a.lm; r += kIdxThreads) {
+  // the largest key of each strided set {r + kLSets j} of the chunk (a real
+  // entry, 0 if the set is empty); the kLTop largest of these maxima, in
+  // descending order, go to the workspace
+  __shared__ uint32_t s_max[kLSets];
+  for (int r = tid; r < kLSets; r += kIdxThreads) {
     uint32_t mx = 0u;
-    for (int e = r; e < cn; e += a.lm) mx = s_keys[e] > mx ? s_keys[e] : mx;
-    uni[r] = mx;
+    for (int e = r; e < cn; e += kLSets) mx = s_keys[e] > mx ? s_keys[e] : mx;
+    s_max[r] = mx;
   }
-}
-
-// Per query: T = the k-th largest key of the union (0 when the union holds
-// fewer than k entries: then every entry is a candidate).
-__global__ __launch_bounds__(kIdxThreads) void idx_long_thr_kernel(IdxArgs a) {
-  extern __shared__ uint32_t s_uni[];
-  __shared__ SelShared sh;
-  __shared__ uint32_t s_cnt;
-  const int tid = threadIdx.x;
-  const int64_t bq = blockIdx.x;
-  uint8_t* wq = a.ws + bq * a.per_query;
-  const uint32_t* uni = (const uint32_t*)(wq + a.off_uni);
-  uint32_t* thr_out = (uint32_t*)(wq + a.off_counts) + a.nseg;
-  const int nu = a.nchunk * a.lm;
-  if (tid == 0) s_cnt = 0u;
   __syncthreads();
-  uint32_t mine = 0;
-  for (int i = tid; i < nu; i += kIdxThreads) {
-    const uint32_t key = uni[i];
-    s_uni[i] = key;
-    mine += key != 0u;
+  if (tid < kWave) {
+    const int lane = tid;
+    uint32_t v0 = s_max[lane], v1 = s_max[lane + kWave];
+    for (int j = 0; j < kLTop; ++j) {
+      const uint32_t mx = wave_total<1>(v0 > v1 ? v0 : v1);
+      // remove one occurrence of mx
+      const uint64_t b0 = __ballot(v0 == mx), b1 = __ballot(v1 == mx);
+      if (b0 != 0ull) {
+        if (lane == __ffsll((unsigned long long)b0) - 1) v0 = 0u;
+      } else if (lane == __ffsll((unsigned long long)b1) - 1) {
+        v1 = 0u;
+      }
+      if (lane == 0) uni[j] = mx;
+    }
   }
-  atomicAdd(&s_cnt, mine);
-  __syncthreads();
-  uint32_t T = 0u;
-  if ((int)s_cnt >= a.k) {
-    int need_eq;
-    radix_select(s_uni, nu, a.k, sh, T, need_eq);
-  }
-  if (tid == 0) *thr_out = T;
 }
 
 __global__ __launch_bounds__(kIdxThreads) void idx_long_compact_kernel(IdxArgs a) {
@@ -1009,28 +1133,52 @@ __global__ __launch_bounds__(kIdxThreads) void idx_long_compact_kernel(IdxArgs a
     if (tid == 0) counts[seg] = 0u;
     return;
   }
-  const uint32_t T = counts[a.nseg];           // from idx_long_thr_kernel
-  // compaction in index order: wave w owns a contiguous range of the segment
+  // T: chunk c is "full" when all its kLSets strided sets are nonempty; with
+  // m = ceil(k / #full), each full chunk holds at least m entries >= its
+  // m-th largest set maximum, so at least k entries are >= the smallest of
+  // those (every entry when no such m exists)
+  const int64_t nfull = nt >= kLSets ? (nt - kLSets) / kLChunk + 1 : 0;
+  uint32_t T = 0u;
+  if (nfull > 0) {
+    const int64_t mm = ((int64_t)a.k + nfull - 1) / nfull;
+    if (mm <= kLTop) {
+      const uint32_t* uni = (const uint32_t*)(wq + a.off_uni);
+      T = 0xffffffffu;
+      for (int64_t c = 0; c < nfull; ++c) {
+        const uint32_t v = uni[c * a.lm + mm - 1];
+        T = v < T ? v : T;
+      }
+    }
+  }
+  // compaction in index order: wave w owns the contiguous range
+  // [w * kLPerWave, +kLPerWave) of the segment; its scores are loaded once,
+  // all loads in flight together, and kept in registers for both passes
   const int len = (int)(s1 - s0);
-  const int per = ((len + kIdxWaves * kWave - 1) / (kIdxWaves * kWave)) * kWave;
-  const int p0 = wave * per, p1 = p0 + per < len ? p0 + per : len;
+  const int p0 = wave * kLPerWave;
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  uint32_t sv[kLPerWave / kWave];
+#pragma unroll
+  for (int r = 0; r < kLPerWave / kWave; ++r) {
+    int pos = p0 + r * kWave + lane;
+    pos = pos < len ? pos : len - 1;
+    sv[r] = scores[s0 + pos];
+  }
   uint32_t n_mine = 0;
-  for (int r0 = p0; r0 < p1; r0 += kWave) {
-    const int pos = r0 + lane;
-    const bool take = pos < p1 && scores[s0 + pos] >= T;
-    n_mine += (uint32_t)__popcll(__ballot(take));
+#pragma unroll
+  for (int r = 0; r < kLPerWave / kWave; ++r) {
+    const int pos = p0 + r * kWave + lane;
+    n_mine += (uint32_t)__popcll(__ballot(pos < len && sv[r] >= T));
   }
   if (lane == 0) sh.wtot[0][wave] = n_mine;
   __syncthreads();
   uint32_t base = 0;
   for (int w = 0; w < wave; ++w) base += sh.wtot[0][w];
-  for (int r0 = p0; r0 < p1; r0 += kWave) {
-    const int pos = r0 + lane;
-    const uint32_t key = pos < p1 ? scores[s0 + pos] : 0u;
-    const bool take = pos < p1 && key >= T;
+#pragma unroll
+  for (int r = 0; r < kLPerWave / kWave; ++r) {
+    const int pos = p0 + r * kWave + lane;
+    const bool take = pos < len && sv[r] >= T;
     const uint64_t bt = __ballot(take);
-    if (take) region[s0 + base + __popcll(bt & lt)] = make_uint2(key, (uint32_t)(s0 + pos));
+    if (take) region[s0 + base + __popcll(bt & lt)] = make_uint2(sv[r], (uint32_t)(s0 + pos));
     base += (uint32_t)__popcll(bt);
   }
   if (wave == kIdxWaves - 1 && lane == 0) counts[seg] = base;
@@ -1055,28 +1203,27 @@ __global__ __launch_bounds__(kIdxThreads) void idx_long_final_kernel(IdxArgs a) 
   const uint2* region = (const uint2*)(wq + a.off_region);
   uint32_t* skey = (uint32_t*)(wq + a.off_skey);
   int32_t* sidx = (int32_t*)(wq + a.off_sidx);
-  // segment offsets in the concatenated candidate list
-  for (int s0 = 0; s0 < a.nseg; s0 += kIdxThreads) {
-    if (tid == 0) {
-      uint32_t run = s0 == 0 ? 0u : s_pre[kIdxThreads];
-      for (int i = 0; i < kIdxThreads && s0 + i < a.nseg; ++i) {
-        s_pre[i] = run;
-        run += counts[s0 + i];
-      }
-      s_pre[kIdxThreads] = run;
+  // segment offsets in the concatenated candidate list (nseg <= kIdxThreads)
+  const int lane = tid % kWave, wave = tid / kWave;
+  const uint32_t cnt_mine = tid < a.nseg ? counts[tid] : 0u;
+  const uint32_t incl = wave_scan<0>(cnt_mine);
+  if (lane == kWave - 1) sh.wtot[0][wave] = incl;
+  __syncthreads();
+  uint32_t wbase = 0;
+  for (int w = 0; w < wave; ++w) wbase += sh.wtot[0][w];
+  if (tid < a.nseg) s_pre[tid] = wbase + incl - cnt_mine;
+  if (tid == kIdxThreads - 1) s_pre[kIdxThreads] = wbase + incl;
+  __syncthreads();
+  for (int sg = 0; sg < a.nseg; ++sg) {
+    const uint32_t cnt = counts[sg], off = s_pre[sg];
+    const uint2* rg = region + (int64_t)sg * kLSeg;
+    for (uint32_t j = tid; j < cnt; j += kIdxThreads) {
+      const uint2 v = rg[j];
+      skey[off + j] = v.x;
+      sidx[off + j] = (int32_t)v.y;
     }
-    __syncthreads();
-    for (int i = 0; i < kIdxThreads && s0 + i < a.nseg; ++i) {
-      const uint32_t cnt = counts[s0 + i], off = s_pre[i];
-      const uint2* rg = region + (int64_t)(s0 + i) * kLSeg;
-      for (uint32_t j = tid; j < cnt; j += kIdxThreads) {
-        const uint2 v = rg[j];
-        skey[off + j] = v.x;
-        sidx[off + j] = (int32_t)v.y;
-      }
-    }
-    __syncthreads();
   }
+  __syncthreads();
   const int ncand = (int)s_pre[kIdxThreads];
   const int kk = ncand < a.k ? ncand : a.k;
   for (int i = kk + tid; i < a.k; i += kIdxThreads) out[i] = -1;
@@ -1104,15 +1251,15 @@ IdxPlan indexer_plan(int B, int Tq, int64_t n_entries, int k) {
     // long lists: score / compact / final select
     p.mode = 1;
     p.nchunk = (int)((n_entries + kLChunk - 1) / kLChunk);
-    p.lm = kLUnion;
-    if ((int64_t)p.nchunk * p.lm > kLUnionLds) return p;       // union must fit the LDS of the T kernel
+    p.lm = kLTop;
     p.nseg = (int)((n_entries + kLSeg - 1) / kLSeg);
+    if (p.nseg > kIdxThreads) return p;                          // up to 8M entries per query
     const size_t npad = align256((size_t)p.nseg * kLSeg);
     p.off_scores = 0;
     p.off_uni = align256(npad * 4);
     p.off_region = p.off_uni + align256((size_t)p.nchunk * p.lm * 4);
     p.off_counts = p.off_region + npad * 8;
-    p.off_skey = p.off_counts + align256((size_t)(p.nseg + 1) * 4);
+    p.off_skey = p.off_counts + align256((size_t)p.nseg * 4);
     p.off_sidx = p.off_skey + npad * 4;
     p.per_query = p.off_sidx + npad * 4;
     p.chunk = kLChunk;
@@ -1139,12 +1286,6 @@ static hipError_t launch_idx_long(const IdxArgs& a, hipStream_t st) {
   auto ka = idx_long_score_kernel<FMT, DI>;
   hipLaunchKernelGGL(ka, dim3(nq, a.nchunk), dim3(kIdxThreads), kLChunk * 4, st, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const size_t lds = (size_t)a.nchunk * a.lm * 4;
-  e = hipFuncSetAttribute((const void*)idx_long_thr_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(idx_long_thr_kernel, dim3(nq), dim3(kIdxThreads), lds, st, a);
-  e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(idx_long_compact_kernel, dim3(nq, a.nseg), dim3(kIdxThreads), 0, st, a);
   e = hipGetLastError();
