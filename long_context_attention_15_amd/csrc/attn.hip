@@ -199,34 +199,53 @@ __global__ __launch_bounds__(kAttnThreads) void attn_valu_kernel(AttnArgs a) {
   if (a.lse && p == 0) a.lse[bq * a.H + h] = lse;
 }
 
-// Fixed-order merge of split partials, with the sink.
-__global__ __launch_bounds__(kAttnThreads) void attn_split_merge_kernel(AttnArgs a) {
+// Fixed-order merge of split partials, with the sink.  One workgroup per
+// (query, head): the split weights e^{m_s - M} / Z are formed once, then each
+// thread combines four dims at a time.
+constexpr int kMaxSplit = 64;
+
+__global__ __launch_bounds__(64) void attn_split_merge_kernel(AttnArgs a) {
+  __shared__ float s_wt[kMaxSplit];
+  __shared__ float s_lse;
   const int64_t bq = blockIdx.x;
   const int h = blockIdx.y;
   const int D = a.D;
   const float* wo = a.ws + (bq * a.H + h) * a.nsplit * (int64_t)D;
   const float* wml = a.ws + (int64_t)a.B * a.Tq * a.H * a.nsplit * D + (bq * a.H + h) * a.nsplit * 2;
-  const float sig = (a.partial || !a.sink) ? -INFINITY : a.sink[h];
-  float M = sig;
-  for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, wml[2 * s]);
-  float Z = 0.0f;
-  if (M > -INFINITY) {
-    Z = sig > -INFINITY ? expf(sig - M) : 0.0f;
-    for (int s = 0; s < a.nsplit; ++s)
-      if (wml[2 * s] > -INFINITY) Z += wml[2 * s + 1] * expf(wml[2 * s] - M);
-  }
-  const int64_t qoff = (bq * a.H + h) * (int64_t)D;
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
-    float acc = 0.0f;
+  if (threadIdx.x == 0) {
+    const float sig = (a.partial || !a.sink) ? -INFINITY : a.sink[h];
+    float M = sig;
+    for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, wml[2 * s]);
+    float Z = 0.0f;
     if (M > -INFINITY) {
+      Z = sig > -INFINITY ? expf(sig - M) : 0.0f;
       for (int s = 0; s < a.nsplit; ++s)
-        if (wml[2 * s] > -INFINITY) acc = fmaf(wo[(int64_t)s * D + d], expf(wml[2 * s] - M), acc);
-      acc = acc / Z;
+        if (wml[2 * s] > -INFINITY) Z += wml[2 * s + 1] * expf(wml[2 * s] - M);
     }
-    if (a.out_f32) ((float*)a.out)[qoff + d] = acc;
-    else ((uint16_t*)a.out)[qoff + d] = (uint16_t)f32_to_bf16(acc);
+    for (int s = 0; s < a.nsplit; ++s)
+      s_wt[s] = (M > -INFINITY && wml[2 * s] > -INFINITY) ? expf(wml[2 * s] - M) / Z : 0.0f;
+    s_lse = M > -INFINITY ? M + logf(Z) : -INFINITY;
   }
-  if (a.lse && threadIdx.x == 0) a.lse[bq * a.H + h] = M > -INFINITY ? M + logf(Z) : -INFINITY;
+  __syncthreads();
+  const int64_t qoff = (bq * a.H + h) * (int64_t)D;
+  for (int d = 4 * threadIdx.x; d < D; d += 4 * blockDim.x) {
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int s = 0; s < a.nsplit; ++s) {
+      const float w = s_wt[s];
+      const float4 v = *(const float4*)(wo + (int64_t)s * D + d);
+      acc.x = fmaf(v.x, w, acc.x); acc.y = fmaf(v.y, w, acc.y);
+      acc.z = fmaf(v.z, w, acc.z); acc.w = fmaf(v.w, w, acc.w);
+    }
+    if (a.out_f32) {
+      *(float4*)((float*)a.out + qoff + d) = acc;
+    } else {
+      uint2 w;
+      w.x = f32_to_bf16(acc.x) | (f32_to_bf16(acc.y) << 16);
+      w.y = f32_to_bf16(acc.z) | (f32_to_bf16(acc.w) << 16);
+      *(uint2*)((uint16_t*)a.out + qoff + d) = w;
+    }
+  }
+  if (a.lse && threadIdx.x == 0) a.lse[bq * a.H + h] = s_lse;
 }
 
 // ------------------------------------------------------------ host side
@@ -247,23 +266,42 @@ static AttnShape attn_shape(int H, int D) {
 
 bool attn_supported(int H, int D) { return H >= 1 && attn_shape(H, D).ok; }
 
-static int attn_nsplit(int B, int Tq, int H, int D, int64_t max_list, int& split_len) {
-  const AttnShape s = attn_shape(H, D);
-  const int64_t wgs = (int64_t)B * Tq * (H / (s.hg ? s.hg : 1));
+// Splits of the entry list per query: enough workgroups to cover the chip
+// (about 2 per CU) when the queries alone do not, each split a whole number
+// of 32-entry tiles and at least `min_len` entries.  hpw = heads per
+// workgroup of the kernel that runs.
+static int attn_nsplit_for(int B, int Tq, int H, int hpw, int64_t max_list, int min_len, int& split_len) {
+  const int64_t wgs = (int64_t)B * Tq * ((H + hpw - 1) / hpw);
   split_len = 0;
-  if (wgs >= 1024 || max_list <= 128) return 1;
-  int64_t want = (1024 + wgs - 1) / wgs;                 // splits per query for ~1024 workgroups
+  if (wgs >= 512 || max_list <= min_len) return 1;
+  const int64_t want = (512 + wgs - 1) / wgs;            // splits per query
   int64_t len = (max_list + want - 1) / want;
-  len = ((len + 31) / 32) * 32;                          // whole 32-entry tiles
-  if (len < 64) len = 64;
+  len = ((len + 31) / 32) * 32;
+  if (len < min_len) len = min_len;
+  int64_t ns = (max_list + len - 1) / len;
+  if (ns > kMaxSplit) {
+    len = ((max_list + kMaxSplit - 1) / kMaxSplit + 31) / 32 * 32;
+    ns = (max_list + len - 1) / len;
+  }
   split_len = (int)len;
-  return (int)((max_list + len - 1) / len);
+  return (int)ns;
+}
+
+static int attn_nsplit(int B, int Tq, int H, int D, int64_t max_list, bool mfma, int& split_len) {
+  if (mfma) return attn_nsplit_for(B, Tq, H, 64, max_list, 256, split_len);
+  const AttnShape s = attn_shape(H, D);
+  return attn_nsplit_for(B, Tq, H, s.hg ? s.hg : 1, max_list, 64, split_len);
 }
 
 size_t attn_workspace(int B, int Tq, int H, int D, int64_t max_list) {
   if (!attn_supported(H, D)) return 0;
   int len;
-  const int ns = attn_nsplit(B, Tq, H, D, max_list, len);
+  // the larger of the two kernels' needs (the query format decides which runs)
+  int ns = attn_nsplit(B, Tq, H, D, max_list, false, len);
+  if (D == 512 && H % 64 == 0) {
+    const int ns2 = attn_nsplit(B, Tq, H, D, max_list, true, len);
+    ns = ns2 > ns ? ns2 : ns;
+  }
   if (ns <= 1) return 0;
   return (size_t)B * Tq * H * ns * (D + 2) * sizeof(float);
 }
@@ -279,11 +317,12 @@ hipError_t launch_attn(const AttnCall& c, hipStream_t st) {
   a.out = c.out; a.out_f32 = c.partial || c.q_fmt == CSA_F32; a.lse = c.lse; a.partial = c.partial;
   const int64_t max_list = (c.mode == kModeSel ? c.k : (c.mode == kModeRange ? c.n_entries : 0)) + c.W;
   int len = 0;
-  a.nsplit = c.allow_split ? attn_nsplit(c.B, c.Tq, c.H, c.D, max_list, len) : 1;
+  const bool mfma = attn_mfma_eligible(c.q_fmt, c.H, c.D, c.ckv.rows ? c.ckv : c.win, c.prior_o != nullptr);
+  a.nsplit = c.allow_split ? attn_nsplit(c.B, c.Tq, c.H, c.D, max_list, mfma, len) : 1;
   a.split_len = len;
   a.ws = (float*)c.ws;
   if ((int64_t)c.B * c.Tq == 0) return hipSuccess;
-  if (attn_mfma_eligible(c.q_fmt, c.H, c.D, c.ckv.rows ? c.ckv : c.win, c.prior_o != nullptr)) {
+  if (mfma) {
     hipError_t e = launch_attn_mfma(c, a.nsplit, a.split_len, st);
     if (e != hipSuccess || a.nsplit == 1) return e;
     hipLaunchKernelGGL(attn_split_merge_kernel, dim3((unsigned)((int64_t)c.B * c.Tq), c.H), dim3(64), 0, st, a);
