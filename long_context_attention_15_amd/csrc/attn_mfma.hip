@@ -50,30 +50,6 @@ __device__ __forceinline__ int64_t m_visible(int64_t t, int m, int64_t n) {
   return v < n ? v : n;
 }
 
-// Index of list slot i that has to come from memory (the sel entry of a
-// top-k slot); other slots need no load.
-__device__ __forceinline__ int m_slot_sel(const MfmaArgs& a, int64_t bq, int64_t Lc, int64_t i, int64_t i1) {
-  return (a.mode == kModeSel && i < Lc && i < i1) ? a.sel[bq * a.k + i] : 0;
-}
-
-// Row of list slot i (jsel = its sel entry for top-k slots); src 0 = empty,
-// 1 = compressed store, 2 = window store.
-__device__ __forceinline__ int m_slot_row(const MfmaArgs& a, int b, int64_t t, int64_t Lc, int64_t i, int64_t i1,
-                                          int jsel, int64_t& row) {
-  row = 0;
-  if (i >= i1) return 0;
-  if (i < Lc) {
-    const int64_t j = a.mode == kModeSel ? (int64_t)jsel : i;
-    if (j < 0 || j >= a.n_entries) return 0;
-    row = (int64_t)b * a.ckv.cap + j;
-    return 1;
-  }
-  const int64_t p = t - a.W + 1 + (i - Lc);
-  if (p < 0 || (!a.ring && p >= a.win.cap)) return 0;
-  row = (int64_t)b * a.win.cap + (a.ring ? p % a.W : p);
-  return 2;
-}
-
 // 8 FP8 codes -> 8 BF16 values times s (exact for a power-of-two s).
 __device__ __forceinline__ u32x4 cvt8_fp8(u32x2 w, float s) {
   u32x4 r;
@@ -118,14 +94,29 @@ __device__ __forceinline__ int pv_entry(int G, int i) { return 16 * (i >> 2) + 4
 #define CSA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 #define CSA_WAIT_VMCNT0() CSA_WAIT_VMCNT(0)
 
-// Gathered rows come from HBM with microsecond latency: kStages tile buffers
-// keep kStages - 1 tiles of row loads in flight per workgroup.
+// Converted tile: 32 rows of 512 BF16 (FP8 dims times the row scale, exact
+// since row scales are powers of two; RoPE dims as stored), 1 KiB per row.
+// 16-byte unit u of row r sits at unit u ^ (r & 15): the sixteen rows that a
+// 128-bit S^T operand read gathers then hit sixteen different 16-byte bank
+// groups (measured on gfx950: 180 B/clk/CU, against 128 B/clk for a
+// stride-2 pattern and 199 B/clk for a plain contiguous read).
+__device__ __forceinline__ int kb_swz(int r) { return r & 15; }
+
+// Gathered rows come from HBM with microsecond latency.  Pipeline per
+// iteration it: products on converted tile it, conversion of raw tile it+1,
+// row DMA of tile it+4 into the raw buffer that tile it's conversion freed
+// (kStages buffers, three tiles of row loads in flight behind the one being
+// waited for), slot table of tile it+5.
 constexpr int kStages = 4;
-constexpr int kSlots = 8;                         // slot tables (>= kStages + 2, power of two)
-constexpr int kDmaPerWave = 5;                    // DMA loads per wave per tile (18 spread over 4 waves, padded)
+constexpr int kLead = kStages;                    // DMA distance in tiles
+constexpr int kSlots = 8;                         // slot tables (>= kLead + 2, power of two)
+constexpr int kDmaWaves = 3;                      // waves 0-2 issue the row DMA, wave 3 builds the slot tables
+constexpr int kDmaPerWave = kRawLoads / kDmaWaves; // 6 wave-wide loads each
+constexpr int kTblBase = kDmaWaves * 64;           // first thread of the table wave
 
 __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t Raw[kStages][kRawTile];
+  __shared__ __attribute__((aligned(16))) uint8_t Kb[2][kMT * 1024];   // converted tiles (bf16, scaled)
   __shared__ const uint8_t* Tptr[kSlots][kMT];    // per tile slot: row address (zero row if empty)
   __shared__ __attribute__((aligned(16))) float Tscl[kSlots][kMT];   // row scale, 0 if empty
   __shared__ int s_over;
@@ -143,37 +134,74 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
   const int64_t i1 = a.nsplit == 1 ? L : (i0 + a.split_len < L ? i0 + a.split_len : L);
   const int ntiles = i1 > i0 ? (int)((i1 - i0 + kMT - 1) / kMT) : 0;
 
-  // slot table of tile `tile` (threads < 32 own one slot each): the row
-  // address is stored now, the row scale is loaded now and returned, to be
-  // stored one iteration later so its latency never sits on the tile loop.
+  // Slot table of tile `tile`, built by the 32 table lanes of wave 3 (lane
+  // tl owns slot i0 + 32 tile + tl of the entry list: a top-k / visible
+  // compressed entry below Lc, a window row above).  The row address is
+  // stored now; the row scale is loaded now and returned, to be stored one
+  // iteration later so that its latency never sits on the tile loop.  Slot
+  // arithmetic is 32-bit (lists stay far below 2^31 entries); empty slots
+  // read the zero row and a zero scale.
+  const int tl = tid - kTblBase;
+  const int i0i = (int)i0, i1i = (int)i1, Lci = (int)Lc;
+  const int win_p0 = (int)(t - a.W + 1) - Lci;       // window position of slot Lc + x is win_p0 + Lc + x
+  const bool sel_mode = a.mode == kModeSel;
+  const int n_ent = (int)a.n_entries, win_cap = (int)a.win.cap;
+  const uint8_t* const ckv_base = a.ckv.rows + (size_t)b * a.ckv.cap * a.ckv.row_bytes;
+  const float* const ckv_sc = (const float*)a.ckv.scales + (size_t)b * a.ckv.cap;
+  const uint8_t* const win_base = a.win.rows + (size_t)b * a.win.cap * a.win.row_bytes;
+  const float* const win_sc = (const float*)a.win.scales + (size_t)b * a.win.cap;
+  const int32_t* const sel_row = sel_mode ? a.sel + bq * a.k : nullptr;
   auto table_ptr = [&](int tile, int jsel) -> float {
-    int64_t row;
-    const int64_t slot = i0 + (int64_t)tile * kMT + tid;
-    const int src = m_slot_row(a, b, t, Lc, slot, i1, jsel, row);
-    const Store& stv = src == 2 ? a.win : a.ckv;
-    Tptr[tile & (kSlots - 1)][tid] = src ? stv.rows + row * stv.row_bytes : g_zero_row;
-    return src ? ((const float*)stv.scales)[row] : 0.0f;
+    const int slot = i0i + tile * kMT + tl;
+    const uint8_t* ptr = g_zero_row;
+    const float* sp = (const float*)g_zero_row;
+    if (slot < i1i) {
+      if (slot < Lci) {
+        const int j = sel_mode ? jsel : slot;
+        if ((unsigned)j < (unsigned)n_ent) { ptr = ckv_base + (size_t)j * a.ckv.row_bytes; sp = ckv_sc + j; }
+      } else {
+        const int p = win_p0 + slot;
+        if (p >= 0 && (a.ring || p < win_cap)) {
+          const int r = a.ring ? p % a.W : p;
+          ptr = win_base + (size_t)r * a.win.row_bytes;
+          sp = win_sc + r;
+        }
+      }
+    }
+    Tptr[tile & (kSlots - 1)][tl] = ptr;
+    return *sp;
   };
+  // sel entry of the slot (top-k slots only; others read a zero)
   auto sel_of = [&](int tile) -> int {
-    return m_slot_sel(a, bq, Lc, i0 + (int64_t)tile * kMT + tid, i1);
+    const int slot = i0i + tile * kMT + tl;
+    return *(sel_mode && slot < Lci && slot < i1i ? sel_row + slot : (const int32_t*)g_zero_row);
   };
-  // DMA the raw rows of `tile` into Raw[tile % kStages]: 18 wave-wide loads
-  // of 1 KiB; lane l of load qd fills LDS unit 64 qd + l, i.e. the (row,
-  // unit) that unit_pos places there.  Every wave issues kDmaPerWave loads
-  // (waves 2 and 3 repeat one load of theirs, writing the same bytes again)
-  // so that all waves can wait on the same vmcnt.
-  auto dma_tile = [&](int tile) {
-    uint8_t* dst = Raw[tile % kStages];
+  // DMA of the raw rows of `tile` into Raw[tile % kStages]: 18 wave-wide
+  // loads of 1 KiB, kDmaPerWave on each of waves 0-2; lane l of load qd
+  // fills LDS unit 64 qd + l, i.e. the (row, unit) that unit_pos places
+  // there.  dma_src reads the slot table (early, so that its LDS latency is
+  // hidden), dma_issue starts the loads.
+  struct DmaSrc { const uint8_t* p[kDmaPerWave]; };
+  auto dma_src = [&](int tile) {
+    DmaSrc d;
     const uint8_t* const* tp = Tptr[tile & (kSlots - 1)];
 #pragma unroll
     for (int j = 0; j < kDmaPerWave; ++j) {
-      int qd = wave + 4 * j;
-      qd = qd < kRawLoads ? qd : qd - 4;
+      const int qd = (wave < kDmaWaves ? wave : 0) + kDmaWaves * j;
       const int u = qd * 64 + lane;
       const int r = u / kUnits, cc = u - r * kUnits;
       int c = cc - unit_rot(r);
       c = c < 0 ? c + kUnits : c;
-      __builtin_amdgcn_global_load_lds((const void*)(tp[r] + 16 * c), (lds_void*)(dst + 1024 * qd), 16, 0, 0);
+      d.p[j] = tp[r] + 16 * c;
+    }
+    return d;
+  };
+  auto dma_issue = [&](int tile, const DmaSrc& d) {
+    uint8_t* dst = Raw[tile % kStages];
+#pragma unroll
+    for (int j = 0; j < kDmaPerWave; ++j) {
+      const int qd = wave + kDmaWaves * j;
+      __builtin_amdgcn_global_load_lds((const void*)d.p[j], (lds_void*)(dst + 1024 * qd), 16, 0, 0);
     }
   };
 
@@ -186,33 +214,41 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 16; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qp + 32 * ks));
   }
-  // LDS byte offsets (within a tile) of this lane's reads.
-  // S^T A operand, row block eb: entry 16 eb + l16; FP8 K-step ks reads bytes
-  // 32 ks + 8 G .. +8 = unit 2 ks + (G >> 1), half G & 1; RoPE step 14 + j
-  // reads BF16 dims 32 j + 8 G = unit 28 + 4 j + G.
-  int s_fp8[2], s_rope[2][2];
+  // LDS byte offsets (within a converted tile) of this lane's reads.
+  // S^T A operand, row block eb, K-step ks: entry 16 eb + l16, unit 4 ks + G,
+  // i.e. byte 16384 eb + 256 (ks >> 2) + s_off[ks & 3].
+  int s_off[4];
+  {
+    const int x = 16 * (G ^ kb_swz(l16));
 #pragma unroll
-  for (int eb = 0; eb < 2; ++eb) {
-    const int e = 16 * eb + l16;
-    s_fp8[eb] = 16 * (kUnits * e + unit_rot(e) + (G >> 1)) + 8 * (G & 1);   // + 32 ks
-#pragma unroll
-    for (int j = 0; j < 2; ++j) s_rope[eb][j] = 16 * unit_pos(e, 28 + 4 * j + G);
+    for (int j = 0; j < 4; ++j) s_off[j] = l16 * 1024 + ((64 * j) ^ x);
   }
-  // V^T A operand, FP8 dim block db (dims 16 db .. +16, unit db): lane
-  // (16 G + l16) points at entry pv_entry(G, l16 >> 1), half l16 & 1.
-  const int ve = pv_entry(G, l16 >> 1);
-  const int v_fp8 = 16 * (kUnits * ve + unit_rot(ve)) + 8 * (l16 & 1);            // + 16 db
-  // V^T A operand, RoPE dim block 28 + j, j < 4 (bf16 dims 16 j .. +16), read hh:
-  // entry pv_entry(G, 4 hh + (l16 >> 2)), bf16 dims 16 j + 4 (l16 & 3).
-  int v_rope[4][2];                                                                 // [j][hh]
+  // V^T A operand, dim block db (dims 16 db .. +16), read hh: entry
+  // pv_entry(G, 4 hh + (l16 >> 2)) = 16 hh + 4 G + (l16 >> 2), dims
+  // 16 db + 4 (l16 & 3) .. +4, i.e. byte 16384 hh + 256 (db >> 3) + v_off[db & 7].
+  int v_off[8];
+  {
+    const int r = 4 * G + (l16 >> 2);
+    const int y = 16 * (((l16 >> 1) & 1) ^ kb_swz(r));
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 8; ++j) v_off[j] = r * 1024 + ((32 * j) ^ y) + 8 * (l16 & 1);
+  }
+  // conversion of a raw tile into Kb: thread -> row tid >> 3; FP8 chunks
+  // 7 (tid & 7) + j, j < 7 (8 dims each, one 16-byte BF16 unit), and RoPE
+  // unit 56 + (tid & 7)
+  const int cv_row = tid >> 3, cv_sub = tid & 7, cv_swz = kb_swz(cv_row);
+  auto convert_tile = [&](int tile) {
+    const uint8_t* raw = Raw[tile % kStages];
+    uint8_t* dst = Kb[tile & 1] + cv_row * 1024;
+    const float sc = Tscl[tile & (kSlots - 1)][cv_row];
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      const int e = pv_entry(G, 4 * hh + (l16 >> 2));
-      const int dbyte = 448 + 2 * (16 * j + 4 * (l16 & 3));
-      v_rope[j][hh] = 16 * unit_pos(e, dbyte >> 4) + (dbyte & 15);
+    for (int j = 0; j < 7; ++j) {
+      const int c = 7 * cv_sub + j;
+      const u32x2 w = *(const u32x2*)(raw + 16 * unit_pos(cv_row, c >> 1) + 8 * (c & 1));
+      *(u32x4*)(dst + 16 * (c ^ cv_swz)) = cvt8_fp8(w, sc);
     }
+    *(u32x4*)(dst + 16 * ((56 + cv_sub) ^ cv_swz)) = *(const u32x4*)(raw + 16 * unit_pos(cv_row, 28 + cv_sub));
+  };
 
   f32x4 acc[32];
 #pragma unroll
@@ -226,92 +262,126 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
   // the first pass tracks in mmax.
   constexpr float kMaxLift = 64.0f;
   float mref = -INFINITY, mmax = -INFINITY, lrun = 0.0f;
+  bool over = false;
   if (tid == 0) s_over = 0;
 
 #pragma nounroll
   for (int attempt = 0; attempt < 2; ++attempt) {
-    // ---- prologue: tables of tiles 0 .. kStages-1, rows of tiles 0 .. kStages-2
-    // (iteration it stores the scale of tile it + kStages - 1, computes the
-    // table of tile it + kStages and loads the sel of tile it + kStages + 1)
+    // ---- prologue: tables of tiles 0 .. kLead, rows of tiles 0 .. kLead-1,
+    // tile 0 converted.  Iteration it stores the scale of tile it + kLead,
+    // computes the table of tile it + kLead + 1 and loads the sel of tile
+    // it + kLead + 2.
     int selreg = 0;
     float scl_pending = 0.0f;
-    if (tid < kMT) {
+    const bool tbl = tid >= kTblBase && tid < kTblBase + kMT;
+    if (tbl) {
       int jn = sel_of(0);
 #pragma unroll
-      for (int tl = 0; tl < kStages; ++tl) {
+      for (int pt = 0; pt <= kLead; ++pt) {
         const int jcur = jn;
-        jn = sel_of(tl + 1);
-        const float sv = table_ptr(tl, jcur);
-        if (tl < kStages - 1) Tscl[tl][tid] = sv;
+        jn = sel_of(pt + 1);
+        const float sv = table_ptr(pt, jcur);
+        if (pt < kLead) Tscl[pt][tl] = sv;
         else scl_pending = sv;
       }
       selreg = jn;
     }
     __syncthreads();
+    if (wave < kDmaWaves) {
 #pragma unroll
-    for (int tl = 0; tl < kStages - 1; ++tl)
-      if (tl < ntiles) dma_tile(tl);
-    CSA_WAIT_VMCNT0();
+      for (int pt = 0; pt < kLead; ++pt)
+        if (pt < ntiles) dma_issue(pt, dma_src(pt));
+    }
+    // tiles 0 and 1 in (loads complete in order)
+    if (ntiles >= 4) CSA_WAIT_VMCNT(2 * kDmaPerWave);
+    else if (ntiles == 3) CSA_WAIT_VMCNT(kDmaPerWave);
+    else CSA_WAIT_VMCNT0();
+    __syncthreads();
+    if (ntiles > 0) convert_tile(0);
     __syncthreads();
 
     for (int it = 0; it < ntiles; ++it) {
-      if (tid < kMT) {
-        Tscl[(it + kStages - 1) & (kSlots - 1)][tid] = scl_pending;
-        if (it + kStages < ntiles) scl_pending = table_ptr(it + kStages, selreg);
-        if (it + kStages + 1 < ntiles) selreg = sel_of(it + kStages + 1);
-      }
-      // rows of tile it + kStages - 1 (its table was written one iteration ago)
-      if (it + kStages - 1 < ntiles) dma_tile(it + kStages - 1);
-      const uint8_t* raw = Raw[it % kStages];
+      // slot-table reads of this iteration go out first
+      const DmaSrc dsrc = dma_src(it + kLead);
       const float* tsc = Tscl[it & (kSlots - 1)];
+      const float tsv = tsc[lane & 31];
+      if (tbl) {
+        Tscl[(it + kLead) & (kSlots - 1)][tl] = scl_pending;
+        if (it + kLead + 1 < ntiles) scl_pending = table_ptr(it + kLead + 1, selreg);
+        if (it + kLead + 2 < ntiles) selreg = sel_of(it + kLead + 2);
+      }
+      const uint8_t* kb = Kb[it & 1];
 
-      // ---- S^T = K Q^T: two row blocks of 16 entries, this wave's 16 heads.
-      // All fragment reads are issued first so that their LDS latency
-      // overlaps the conversions and MFMAs.
-      u32x2 kf[2][14];
-      u32x4 kr[2][2];
+      // The three phases below are issued in a fixed order (scheduling
+      // barriers between groups): with one wavefront per SIMD the LDS reads
+      // must run kSD / kVD MFMAs ahead of their consumers, and the conversion
+      // of the next tile fills the issue slots between the S^T MFMAs.
+
+      // raw rows of the next tile for this thread's conversion share (tile
+      // it+1 < ntiles; past the end the stale buffer converts into a tile
+      // that is never read)
+      const uint8_t* craw = Raw[(it + 1) % kStages];
+      uint8_t* cdst = Kb[(it + 1) & 1] + cv_row * 1024;
+      const float csc = Tscl[(it + 1) & (kSlots - 1)][cv_row];
+      u32x2 cw[7];
 #pragma unroll
-      for (int ks = 0; ks < 14; ++ks)
-#pragma unroll
-        for (int eb = 0; eb < 2; ++eb) kf[eb][ks] = *(const u32x2*)(raw + s_fp8[eb] + 32 * ks);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int eb = 0; eb < 2; ++eb) kr[eb][j] = *(const u32x4*)(raw + s_rope[eb][j]);
-      __builtin_amdgcn_sched_barrier(0);            // keep the reads ahead of their uses
+      for (int j = 0; j < 7; ++j) {
+        const int c = 7 * cv_sub + j;
+        cw[j] = *(const u32x2*)(craw + 16 * unit_pos(cv_row, c >> 1) + 8 * (c & 1));
+      }
+      const u32x4 crope = *(const u32x4*)(craw + 16 * unit_pos(cv_row, 28 + cv_sub));
+
+      // ---- S^T = K Q^T: two row blocks of 16 entries, this wave's 16 heads
+      constexpr int kSD = 5;                        // K-step read distance
       f32x4 sa[2], sb[2];                           // even / odd K-step chains
 #pragma unroll
       for (int eb = 0; eb < 2; ++eb) { sa[eb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f}; sb[eb] = sa[eb]; }
-      const float srow0 = tsc[l16], srow1 = tsc[16 + l16];
+      u32x4 kq[16][2];
 #pragma unroll
-      for (int ks = 0; ks < 14; ++ks) {
-#pragma unroll
-        for (int eb = 0; eb < 2; ++eb) {
-          const u32x4 k = cvt8_fp8(kf[eb][ks], eb ? srow1 : srow0);
-          if (ks & 1) sb[eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k), qf[ks], sb[eb], 0, 0, 0);
-          else sa[eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k), qf[ks], sa[eb], 0, 0, 0);
-        }
+      for (int ks = 0; ks < kSD; ++ks) {
+        kq[ks][0] = *(const u32x4*)(kb + 256 * (ks >> 2) + s_off[ks & 3]);
+        kq[ks][1] = *(const u32x4*)(kb + 16384 + 256 * (ks >> 2) + s_off[ks & 3]);
       }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int eb = 0; eb < 2; ++eb) {
-          if (j) sb[eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[eb][j]), qf[14 + j], sb[eb], 0, 0, 0);
-          else sa[eb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr[eb][j]), qf[14 + j], sa[eb], 0, 0, 0);
+      for (int ks = 0; ks < 16; ++ks) {
+        if (ks + kSD < 16) {
+          const int kn = ks + kSD;
+          kq[kn][0] = *(const u32x4*)(kb + 256 * (kn >> 2) + s_off[kn & 3]);
+          kq[kn][1] = *(const u32x4*)(kb + 16384 + 256 * (kn >> 2) + s_off[kn & 3]);
         }
-      // V^T fragments for the PV product, read now so that the softmax below
-      // covers their latency
-      v2i32 vf[28];
+        if (ks & 1) {
+          sb[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kq[ks][0]), qf[ks], sb[0], 0, 0, 0);
+          sb[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kq[ks][1]), qf[ks], sb[1], 0, 0, 0);
+        } else {
+          sa[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kq[ks][0]), qf[ks], sa[0], 0, 0, 0);
+          sa[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kq[ks][1]), qf[ks], sa[1], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+
+      // ---- V^T reads for the first kVD dim blocks go out before the softmax
+      constexpr int kVD = 6;                        // dim-block read distance
+      u32x4 vq[32];
 #pragma unroll
-      for (int db = 0; db < 28; ++db) vf[db] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32*)(raw + v_fp8 + 16 * db));
-      v4i16 vr[4][2];
+      for (int db = 0; db < kVD; ++db) {
+        const uint8_t* vp = kb + 256 * (db >> 3) + v_off[db & 7];
+        const u32x2 x0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)vp));
+        const u32x2 x1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp + 16384)));
+        vq[db] = u32x4{x0.x, x0.y, x1.x, x1.y};
+      }
+      __builtin_amdgcn_sched_barrier(0);
+
+      // ---- conversion of the next tile, interleaved with the softmax below
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) vr[j][hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(raw + v_rope[j][hh]));
+      for (int j = 0; j < 7; ++j) {
+        const int c = 7 * cv_sub + j;
+        *(u32x4*)(cdst + 16 * (c ^ cv_swz)) = cvt8_fp8(cw[j], csc);
+      }
+      *(u32x4*)(cdst + 16 * ((56 + cv_sub) ^ cv_swz)) = crope;
 
       // ---- softmax; lane holds entries 16 (i >> 2) + 4 G + (i & 3), i = 0..7, of head h
-      const unsigned int vmask = (unsigned int)__ballot(lane < 32 && tsc[lane & 31] > 0.0f);
+      const unsigned int vmask = (unsigned int)__ballot(lane < 32 && tsv > 0.0f);
       float p[8];
       float mt = -INFINITY;
 #pragma unroll
@@ -321,59 +391,74 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
         p[i] = ((vmask >> e) & 1u) ? tot * sc2 : -INFINITY;
         mt = fmaxf(mt, p[i]);
       }
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
+      {
+        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+        mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
       {
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
         mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
       }
       mmax = fmaxf(mmax, mt);
       if (mref == -INFINITY) mref = mt;     // the head's first non-empty tile
-      if (__ballot(mt > mref + kMaxLift) != 0ull && lane == 0) s_over = 1;
+      over |= mt > mref + kMaxLift;
       float psum = 0.0f;
+      bf16x8 pb;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        p[i] = mref > -INFINITY ? exp2f(p[i] - mref) : 0.0f;
+        p[i] = mref > -INFINITY ? __builtin_amdgcn_exp2f(p[i] - mref) : 0.0f;
         psum += p[i];
+        pb[i] = (__bf16)p[i];
       }
-      psum += __shfl_xor(psum, 16);
+      {
+        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(psum), __float_as_uint(psum), false, false);
+        psum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      }
       {
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(psum), __float_as_uint(psum), false, false);
         psum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
       }
       lrun += psum;
-      // P^T operands: raw for the RoPE dims, times the row scale for the FP8 dims
-      bf16x8 pr, ps;
-      {
-        const float4 e0 = *(const float4*)(tsc + 4 * G), e1 = *(const float4*)(tsc + 16 + 4 * G);
-        const float es[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          pr[i] = (__bf16)p[i];
-          ps[i] = (__bf16)(p[i] * es[i]);
-        }
-      }
+      __builtin_amdgcn_sched_barrier(0);
 
       // ---- O^T += V^T P^T over 32 dim blocks of 16
 #pragma unroll
-      for (int db = 0; db < 28; ++db) {
-        const u32x4 v = cvt8_fp8(u32x2{(unsigned)vf[db].x, (unsigned)vf[db].y}, 1.0f);
-        acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), ps, acc[db], 0, 0, 0);
+      for (int db = 0; db < 32; ++db) {
+        if (db + kVD < 32) {
+          const int dn = db + kVD;
+          const uint8_t* vp = kb + 256 * (dn >> 3) + v_off[dn & 7];
+          const u32x2 x0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)vp));
+          const u32x2 x1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(vp + 16384)));
+          vq[dn] = u32x4{x0.x, x0.y, x1.x, x1.y};
+        }
+        acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vq[db]), pb, acc[db], 0, 0, 0);
+        // rows of tile it + kLead, one load every four dim blocks (its table
+        // was written one iteration ago, its raw buffer was last read by the
+        // conversion of tile it; issued after this iteration's conversion
+        // stores, since LDS stores behind an LDS DMA make the compiler wait
+        // for the DMA)
+        if ((db & 3) == 1 && (db >> 2) < kDmaPerWave && wave < kDmaWaves && it + kLead < ntiles) {
+          const int j = db >> 2;
+          __builtin_amdgcn_global_load_lds((const void*)dsrc.p[j],
+                                           (lds_void*)(Raw[(it + kLead) % kStages] + 1024 * (wave + kDmaWaves * j)), 16, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const u32x2 ux0 = __builtin_bit_cast(u32x2, vr[j][0]), ux1 = __builtin_bit_cast(u32x2, vr[j][1]);
-        const u32x4 v = u32x4{ux0.x, ux0.y, ux1.x, ux1.y};
-        acc[28 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, v), pr, acc[28 + j], 0, 0, 0);
-      }
-      // the rows of tile it+1 are in: loads complete in order, and after
-      // them this wave issued the DMA of the next kStages - 2 tiles (plus,
-      // on wave 0, some table loads), so allowing that many DMA loads to be
-      // outstanding is safe; near the end of the list fewer were issued, so
-      // wait for everything there
-      if (it + kStages - 1 < ntiles) CSA_WAIT_VMCNT((kStages - 2) * kDmaPerWave);
+      // the rows of tile it+2 are in before the barrier: loads complete in
+      // order, and after them this wave issued at most the DMA of tiles it+3
+      // and it+4 (plus, on wave 0, table loads, which only makes the wait
+      // stricter)
+      if (it + 4 < ntiles) CSA_WAIT_VMCNT(2 * kDmaPerWave);
+      else if (it + 3 < ntiles) CSA_WAIT_VMCNT(kDmaPerWave);
       else CSA_WAIT_VMCNT0();
-      __syncthreads();
+      // Workgroup barrier without the release fence of __syncthreads: the
+      // fence would also wait for every LDS DMA in flight (vmcnt(0)) and so
+      // drain the row pipeline each iteration.  LDS stores are completed by
+      // the lgkmcnt wait, the rows of tile it+2 by the vmcnt wait above; the
+      // memory clobber keeps the compiler from moving LDS accesses across.
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
+    if (__ballot(over) != 0ull && lane == 0) s_over = 1;
     __syncthreads();
     if (!s_over) break;                     // uniform
     // recompute with the exact per-head maximum (mref >= every logit now)
@@ -381,6 +466,7 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
     for (int db = 0; db < 32; ++db) acc[db] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     lrun = 0.0f;
     mref = mmax;
+    over = false;
     __syncthreads();
     if (tid == 0) s_over = 0;
   }
@@ -434,6 +520,8 @@ bool attn_mfma_eligible(int q_fmt, int H, int D, const csa_store& kv, bool has_p
 }
 
 hipError_t launch_attn_mfma(const AttnCall& c, int nsplit, int split_len, hipStream_t st) {
+  // slot arithmetic in the kernel is 32-bit
+  if (c.n_entries + c.W + kMT > INT32_MAX || c.ckv.cap > INT32_MAX || c.win.cap > INT32_MAX) return hipErrorInvalidValue;
   MfmaArgs a;
   a.q = (const uint16_t*)c.q; a.B = c.B; a.Tq = c.Tq; a.H = c.H;
   a.ckv = c.ckv.rows ? view(c.ckv) : view(c.win);
