@@ -317,7 +317,7 @@ hipError_t launch_attn(const AttnCall& c, hipStream_t st) {
   a.out = c.out; a.out_f32 = c.partial || c.q_fmt == CSA_F32; a.lse = c.lse; a.partial = c.partial;
   const int64_t max_list = (c.mode == kModeSel ? c.k : (c.mode == kModeRange ? c.n_entries : 0)) + c.W;
   int len = 0;
-  const bool mfma = attn_mfma_eligible(c.q_fmt, c.H, c.D, c.ckv.rows ? c.ckv : c.win, c.prior_o != nullptr);
+  const bool mfma = attn_mfma_eligible(c.q_fmt, c.H, c.D, c.ckv.rows ? c.ckv : c.win, c.prior_o != nullptr, c.tau);
   a.nsplit = c.allow_split ? attn_nsplit(c.B, c.Tq, c.H, c.D, max_list, mfma, len) : 1;
   a.split_len = len;
   a.ws = (float*)c.ws;

@@ -34,6 +34,7 @@ constexpr int kMT = 32;                  // entries per tile
 constexpr int kMThreads = 256;           // four wavefronts
 constexpr int kMHeads = 16;              // heads per wavefront
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kEmpty = -1.0e30f;          // logit of an empty slot
 constexpr float kLn2 = 0.6931471805599453f;
 
 struct MfmaArgs {
@@ -119,6 +120,7 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t Kb[2][kMT * 1024];   // converted tiles (bf16, scaled)
   __shared__ const uint8_t* Tptr[kSlots][kMT];    // per tile slot: row address (zero row if empty)
   __shared__ __attribute__((aligned(16))) float Tscl[kSlots][kMT];   // row scale, 0 if empty
+  __shared__ __attribute__((aligned(16))) float Tbias[kSlots][kMT];  // 0 for a filled slot, kEmpty for an empty one
   __shared__ int s_over;
 
   const int tid = threadIdx.x;
@@ -153,23 +155,18 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
   const int32_t* const sel_row = sel_mode ? a.sel + bq * a.k : nullptr;
   auto table_ptr = [&](int tile, int jsel) -> float {
     const int slot = i0i + tile * kMT + tl;
-    const uint8_t* ptr = g_zero_row;
-    const float* sp = (const float*)g_zero_row;
-    if (slot < i1i) {
-      if (slot < Lci) {
-        const int j = sel_mode ? jsel : slot;
-        if ((unsigned)j < (unsigned)n_ent) { ptr = ckv_base + (size_t)j * a.ckv.row_bytes; sp = ckv_sc + j; }
-      } else {
-        const int p = win_p0 + slot;
-        if (p >= 0 && (a.ring || p < win_cap)) {
-          const int r = a.ring ? p % a.W : p;
-          ptr = win_base + (size_t)r * a.win.row_bytes;
-          sp = win_sc + r;
-        }
-      }
-    }
-    Tptr[tile & (kSlots - 1)][tl] = ptr;
-    return *sp;
+    int p = win_p0 + slot;                         // window position (slots >= Lc)
+    const bool p_ok = p >= 0 && (a.ring || p < win_cap);
+    if (a.ring) p = p >= 0 ? p % a.W : 0;          // uniform branch
+    const bool in_list = slot < i1i, is_c = slot < Lci;
+    const int j = sel_mode ? jsel : slot;
+    const bool ok = in_list && (is_c ? (unsigned)j < (unsigned)n_ent : p_ok);
+    const int idx = is_c ? j : p;
+    const uint8_t* ptr = (is_c ? ckv_base : win_base) + (size_t)idx * (is_c ? a.ckv.row_bytes : a.win.row_bytes);
+    const float* sp = (is_c ? ckv_sc : win_sc) + idx;
+    Tptr[tile & (kSlots - 1)][tl] = ok ? ptr : g_zero_row;
+    Tbias[tile & (kSlots - 1)][tl] = ok ? 0.0f : kEmpty;
+    return *(ok ? sp : (const float*)g_zero_row);
   };
   // sel entry of the slot (top-k slots only; others read a zero)
   auto sel_of = [&](int tile) -> int {
@@ -181,19 +178,24 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
   // fills LDS unit 64 qd + l, i.e. the (row, unit) that unit_pos places
   // there.  dma_src reads the slot table (early, so that its LDS latency is
   // hidden), dma_issue starts the loads.
+  // Per load j: the slot-table row and the byte offset within the row of
+  // this lane's 16 bytes (fixed per lane); wave 3 mirrors wave 0's rows.
+  int dma_row[kDmaPerWave], dma_off[kDmaPerWave];
+#pragma unroll
+  for (int j = 0; j < kDmaPerWave; ++j) {
+    const int qd = (wave < kDmaWaves ? wave : 0) + kDmaWaves * j;
+    const int u = qd * 64 + lane;
+    const int r = u / kUnits, cc = u - r * kUnits;
+    int c = cc - unit_rot(r);
+    c = c < 0 ? c + kUnits : c;
+    dma_row[j] = r;
+    dma_off[j] = 16 * c;
+  }
   struct DmaSrc { const uint8_t* p[kDmaPerWave]; };
   auto dma_src = [&](int tile) {
     DmaSrc d;
-    const uint8_t* const* tp = Tptr[tile & (kSlots - 1)];
 #pragma unroll
-    for (int j = 0; j < kDmaPerWave; ++j) {
-      const int qd = (wave < kDmaWaves ? wave : 0) + kDmaWaves * j;
-      const int u = qd * 64 + lane;
-      const int r = u / kUnits, cc = u - r * kUnits;
-      int c = cc - unit_rot(r);
-      c = c < 0 ? c + kUnits : c;
-      d.p[j] = tp[r] + 16 * c;
-    }
+    for (int j = 0; j < kDmaPerWave; ++j) d.p[j] = Tptr[tile & (kSlots - 1)][dma_row[j]];
     return d;
   };
   auto dma_issue = [&](int tile, const DmaSrc& d) {
@@ -201,7 +203,7 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
 #pragma unroll
     for (int j = 0; j < kDmaPerWave; ++j) {
       const int qd = wave + kDmaWaves * j;
-      __builtin_amdgcn_global_load_lds((const void*)d.p[j], (lds_void*)(dst + 1024 * qd), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(d.p[j] + dma_off[j]), (lds_void*)(dst + 1024 * qd), 16, 0, 0);
     }
   };
 
@@ -259,10 +261,13 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
   // the O^T accumulators.  Probabilities relative to it stay below
   // 2^kMaxLift; if some logit climbs further (not seen with normalised
   // inputs) the whole query is recomputed once with the exact maximum, which
-  // the first pass tracks in mmax.
+  // the first pass tracks as xmax.
   constexpr float kMaxLift = 64.0f;
-  float mref = -INFINITY, mmax = -INFINITY, lrun = 0.0f;
-  bool over = false;
+  // mref: reference (log2 units) once mset; xmax: largest logit relative
+  // to it; lrun: this lane's share of the denominator (both reduced over the
+  // head's 4 lanes after the tile loop).
+  float mref = 0.0f, xmax = -INFINITY, lrun = 0.0f;
+  bool mset = false;
   if (tid == 0) s_over = 0;
 
 #pragma nounroll
@@ -303,8 +308,8 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
     for (int it = 0; it < ntiles; ++it) {
       // slot-table reads of this iteration go out first
       const DmaSrc dsrc = dma_src(it + kLead);
-      const float* tsc = Tscl[it & (kSlots - 1)];
-      const float tsv = tsc[lane & 31];
+      const float* tbs = Tbias[it & (kSlots - 1)];
+      const float4 eb0 = *(const float4*)(tbs + 4 * G), eb1 = *(const float4*)(tbs + 16 + 4 * G);
       if (tbl) {
         Tscl[(it + kLead) & (kSlots - 1)][tl] = scl_pending;
         if (it + kLead + 1 < ntiles) scl_pending = table_ptr(it + kLead + 1, selreg);
@@ -312,10 +317,9 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
       }
       const uint8_t* kb = Kb[it & 1];
 
-      // The three phases below are issued in a fixed order (scheduling
-      // barriers between groups): with one wavefront per SIMD the LDS reads
-      // must run kSD / kVD MFMAs ahead of their consumers, and the conversion
-      // of the next tile fills the issue slots between the S^T MFMAs.
+      // The phases below are issued in a fixed order (scheduling barriers
+      // between groups): with one wavefront per SIMD the LDS reads must run
+      // ahead of their MFMAs.
 
       // raw rows of the next tile for this thread's conversion share (tile
       // it+1 < ntiles; past the end the stale buffer converts into a tile
@@ -331,11 +335,15 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
       }
       const u32x4 crope = *(const u32x4*)(craw + 16 * unit_pos(cv_row, 28 + cv_sub));
 
-      // ---- S^T = K Q^T: two row blocks of 16 entries, this wave's 16 heads
+      // ---- S^T = K Q^T: two row blocks of 16 entries, this wave's 16 heads.
+      // The even chain starts at 0 for a filled slot and at kEmpty for an
+      // empty one, so empty slots drop out of the softmax by themselves.
       constexpr int kSD = 5;                        // K-step read distance
       f32x4 sa[2], sb[2];                           // even / odd K-step chains
-#pragma unroll
-      for (int eb = 0; eb < 2; ++eb) { sa[eb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f}; sb[eb] = sa[eb]; }
+      sa[0] = f32x4{eb0.x, eb0.y, eb0.z, eb0.w};
+      sa[1] = f32x4{eb1.x, eb1.y, eb1.z, eb1.w};
+      sb[0] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      sb[1] = sb[0];
       u32x4 kq[16][2];
 #pragma unroll
       for (int ks = 0; ks < kSD; ++ks) {
@@ -381,42 +389,37 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
       *(u32x4*)(cdst + 16 * ((56 + cv_sub) ^ cv_swz)) = crope;
 
       // ---- softmax; lane holds entries 16 (i >> 2) + 4 G + (i & 3), i = 0..7, of head h
-      const unsigned int vmask = (unsigned int)__ballot(lane < 32 && tsv > 0.0f);
-      float p[8];
-      float mt = -INFINITY;
+      float tot[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int e = pv_entry(G, i);
-        const float tot = sa[i >> 2][i & 3] + sb[i >> 2][i & 3];
-        p[i] = ((vmask >> e) & 1u) ? tot * sc2 : -INFINITY;
-        mt = fmaxf(mt, p[i]);
+      for (int i = 0; i < 8; ++i) tot[i] = sa[i >> 2][i & 3] + sb[i >> 2][i & 3];
+      if (!mset && __ballot(eb0.x == 0.0f || eb0.y == 0.0f || eb0.z == 0.0f || eb0.w == 0.0f ||
+                            eb1.x == 0.0f || eb1.y == 0.0f || eb1.z == 0.0f || eb1.w == 0.0f) != 0ull) {
+        // first tile with a filled slot (slots are shared by all heads, so
+        // this is wave-uniform): each head's reference is its maximum over
+        // the tile, reduced over the head's 4 lanes
+        float mt = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) mt = fmaxf(mt, tot[i] * sc2);
+        {
+          const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+          mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
+        {
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+          mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
+        mref = mt;
+        mset = true;
       }
-      {
-        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
-        mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-      }
-      {
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
-        mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-      }
-      mmax = fmaxf(mmax, mt);
-      if (mref == -INFINITY) mref = mt;     // the head's first non-empty tile
-      over |= mt > mref + kMaxLift;
       float psum = 0.0f;
       bf16x8 pb;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        p[i] = mref > -INFINITY ? __builtin_amdgcn_exp2f(p[i] - mref) : 0.0f;
-        psum += p[i];
-        pb[i] = (__bf16)p[i];
-      }
-      {
-        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(psum), __float_as_uint(psum), false, false);
-        psum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-      }
-      {
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(psum), __float_as_uint(psum), false, false);
-        psum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        const float x = fmaf(tot[i], sc2, -mref);
+        xmax = fmaxf(xmax, x);
+        const float pv = __builtin_amdgcn_exp2f(x);
+        psum += pv;
+        pb[i] = (__bf16)pv;
       }
       lrun += psum;
       __builtin_amdgcn_sched_barrier(0);
@@ -439,7 +442,7 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
         // for the DMA)
         if ((db & 3) == 1 && (db >> 2) < kDmaPerWave && wave < kDmaWaves && it + kLead < ntiles) {
           const int j = db >> 2;
-          __builtin_amdgcn_global_load_lds((const void*)dsrc.p[j],
+          __builtin_amdgcn_global_load_lds((const void*)(dsrc.p[j] + dma_off[j]),
                                            (lds_void*)(Raw[(it + kLead) % kStages] + 1024 * (wave + kDmaWaves * j)), 16, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -458,19 +461,30 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
       // memory clobber keeps the compiler from moving LDS accesses across.
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
-    if (__ballot(over) != 0ull && lane == 0) s_over = 1;
+    // head-wide maximum (relative to the reference) and sum over the 4 lanes of a head
+    {
+      auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(xmax), __float_as_uint(xmax), false, false);
+      xmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(xmax), __float_as_uint(xmax), false, false);
+      xmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(lrun), __float_as_uint(lrun), false, false);
+      lrun = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lrun), __float_as_uint(lrun), false, false);
+      lrun = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+    if (__ballot(mset && xmax > kMaxLift) != 0ull && lane == 0) s_over = 1;
     __syncthreads();
     if (!s_over) break;                     // uniform
-    // recompute with the exact per-head maximum (mref >= every logit now)
+    // recompute with the exact per-head maximum as the reference
 #pragma unroll
     for (int db = 0; db < 32; ++db) acc[db] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     lrun = 0.0f;
-    mref = mmax;
-    over = false;
+    if (mset) mref += xmax;
+    xmax = -INFINITY;
     __syncthreads();
     if (tid == 0) s_over = 0;
   }
-  const float mrun = mref;
+  const float mrun = mset ? mref : -INFINITY;
 
   // ---- epilogue: lane holds O^T rows (dims) 16 db + 4 G + (0..3) of head h
   const int64_t qoff = (bq * a.H + h) * (int64_t)kMD;
@@ -514,8 +528,10 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
   if (a.lse && G == 0) a.lse[bq * a.H + h] = lse;
 }
 
-bool attn_mfma_eligible(int q_fmt, int H, int D, const csa_store& kv, bool has_prior) {
-  return !has_prior && q_fmt == CSA_BF16 && D == kMD && H % 64 == 0 && kv.fmt == CSA_FP8_E4M3 &&
+// The MFMA kernel masks empty slots through a -1e30 logit, which needs a
+// positive softmax scale; other scales take the general kernel.
+bool attn_mfma_eligible(int q_fmt, int H, int D, const csa_store& kv, bool has_prior, float tau) {
+  return !has_prior && tau > 0.0f && q_fmt == CSA_BF16 && D == kMD && H % 64 == 0 && kv.fmt == CSA_FP8_E4M3 &&
          kv.row_bytes == kRawRow;
 }
 

@@ -49,7 +49,7 @@ enum { kModeNone = 0, kModeSel = 1, kModeRange = 2 };
 size_t attn_workspace(int B, int Tq, int H, int D, int64_t max_list);
 bool attn_supported(int H, int D);
 hipError_t launch_attn(const AttnCall& c, hipStream_t st);
-bool attn_mfma_eligible(int q_fmt, int H, int D, const csa_store& kv, bool has_prior);
+bool attn_mfma_eligible(int q_fmt, int H, int D, const csa_store& kv, bool has_prior, float tau);
 hipError_t launch_attn_mfma(const AttnCall& c, int nsplit, int split_len, hipStream_t st);
 
 }  // namespace csa
