@@ -115,12 +115,23 @@ constexpr int kDmaWaves = 3;                      // waves 0-2 issue the row DMA
 constexpr int kDmaPerWave = kRawLoads / kDmaWaves; // 6 wave-wide loads each
 constexpr int kTblBase = kDmaWaves * 64;           // first thread of the table wave
 
+// 16-byte-per-lane LDS DMA (global_load_lds_dwordx4: lane l's 16 bytes land
+// at LDS dst + 16 l), written as inline asm.  The compiler's own LDS-DMA
+// bookkeeping would otherwise put full LDS and vector-memory waits on the
+// next LDS accesses; completion is tracked here by explicit vmcnt waits
+// (the asm has no register result, only the address input).
+__device__ __forceinline__ void dma16(const void* src, void* dst) {
+  const unsigned lds = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)dst);
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+}
+
 __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t Raw[kStages][kRawTile];
   __shared__ __attribute__((aligned(16))) uint8_t Kb[2][kMT * 1024];   // converted tiles (bf16, scaled)
   __shared__ const uint8_t* Tptr[kSlots][kMT];    // per tile slot: row address (zero row if empty)
   __shared__ __attribute__((aligned(16))) float Tscl[kSlots][kMT];   // row scale, 0 if empty
   __shared__ __attribute__((aligned(16))) float Tbias[kSlots][kMT];  // 0 for a filled slot, kEmpty for an empty one
+  __shared__ __attribute__((aligned(16))) uint8_t DmaSink[1024];   // target of wave 3's stand-in loads
   __shared__ int s_over;
 
   const int tid = threadIdx.x;
@@ -191,6 +202,7 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
     dma_row[j] = r;
     dma_off[j] = 16 * c;
   }
+  const bool dma_sink = __builtin_amdgcn_readfirstlane(wave) >= kDmaWaves;
   struct DmaSrc { const uint8_t* p[kDmaPerWave]; };
   auto dma_src = [&](int tile) {
     DmaSrc d;
@@ -312,8 +324,9 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
       const float4 eb0 = *(const float4*)(tbs + 4 * G), eb1 = *(const float4*)(tbs + 16 + 4 * G);
       if (tbl) {
         Tscl[(it + kLead) & (kSlots - 1)][tl] = scl_pending;
-        if (it + kLead + 1 < ntiles) scl_pending = table_ptr(it + kLead + 1, selreg);
-        if (it + kLead + 2 < ntiles) selreg = sel_of(it + kLead + 2);
+        // past the end of the list the tables hold empty slots (zero rows)
+        scl_pending = table_ptr(it + kLead + 1, selreg);
+        selreg = sel_of(it + kLead + 2);
       }
       const uint8_t* kb = Kb[it & 1];
 
@@ -440,20 +453,22 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
         // conversion of tile it; issued after this iteration's conversion
         // stores, since LDS stores behind an LDS DMA make the compiler wait
         // for the DMA)
-        if ((db & 3) == 1 && (db >> 2) < kDmaPerWave && wave < kDmaWaves && it + kLead < ntiles) {
+        // Branch-free so that the LDS-read bookkeeping of the compiler stays
+        // exact: past the end of the list the rows are zero rows, and wave 3
+        // loads a zero row into a sink buffer.
+        if ((db & 3) == 1 && (db >> 2) < kDmaPerWave) {
           const int j = db >> 2;
-          __builtin_amdgcn_global_load_lds((const void*)(dsrc.p[j] + dma_off[j]),
-                                           (lds_void*)(Raw[(it + kLead) % kStages] + 1024 * (wave + kDmaWaves * j)), 16, 0, 0);
+          const uint8_t* src = dma_sink ? g_zero_row + 16 * lane : dsrc.p[j] + dma_off[j];
+          uint8_t* dst = dma_sink ? DmaSink : Raw[(it + kLead) % kStages] + 1024 * (wave + kDmaWaves * j);
+          dma16(src, dst);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
       // the rows of tile it+2 are in before the barrier: loads complete in
-      // order, and after them this wave issued at most the DMA of tiles it+3
-      // and it+4 (plus, on wave 0, table loads, which only makes the wait
-      // stricter)
-      if (it + 4 < ntiles) CSA_WAIT_VMCNT(2 * kDmaPerWave);
-      else if (it + 3 < ntiles) CSA_WAIT_VMCNT(kDmaPerWave);
-      else CSA_WAIT_VMCNT0();
+      // order, and after them every wave issued the kDmaPerWave loads of
+      // tiles it+3 and it+4 (wave 3 also its table loads, which only makes
+      // the wait stricter there)
+      CSA_WAIT_VMCNT(2 * kDmaPerWave);
       // Workgroup barrier without the release fence of __syncthreads: the
       // fence would also wait for every LDS DMA in flight (vmcnt(0)) and so
       // drain the row pipeline each iteration.  LDS stores are completed by
