@@ -125,12 +125,18 @@ __device__ __forceinline__ void dma16(const void* src, void* dst) {
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
 }
 
+__device__ __forceinline__ void dma4(const void* src, void* dst) {
+  const unsigned lds = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)dst);
+  asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+}
+
 __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t Raw[kStages][kRawTile];
   __shared__ __attribute__((aligned(16))) uint8_t Kb[2][kMT * 1024];   // converted tiles (bf16, scaled)
   __shared__ const uint8_t* Tptr[kSlots][kMT];    // per tile slot: row address (zero row if empty)
   __shared__ __attribute__((aligned(16))) float Tscl[kSlots][kMT];   // row scale, 0 if empty
   __shared__ __attribute__((aligned(16))) float Tbias[kSlots][kMT];  // 0 for a filled slot, kEmpty for an empty one
+  __shared__ __attribute__((aligned(16))) int32_t Tsel[kSlots][kMT];  // sel entries (top-k lists)
   __shared__ __attribute__((aligned(16))) uint8_t DmaSink[1024];   // target of wave 3's stand-in loads
   __shared__ int s_over;
 
@@ -149,11 +155,12 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
 
   // Slot table of tile `tile`, built by the 32 table lanes of wave 3 (lane
   // tl owns slot i0 + 32 tile + tl of the entry list: a top-k / visible
-  // compressed entry below Lc, a window row above).  The row address is
-  // stored now; the row scale is loaded now and returned, to be stored one
-  // iteration later so that its latency never sits on the tile loop.  Slot
-  // arithmetic is 32-bit (lists stay far below 2^31 entries); empty slots
-  // read the zero row and a zero scale.
+  // compressed entry below Lc, a window row above).  The row address and
+  // the softmax bias are stored now; the row scale goes to Tscl by LDS DMA,
+  // as the sel entries go to Tsel two tiles earlier, so no load result ever
+  // sits in a register of the tile loop.  Slot arithmetic is 32-bit (lists
+  // stay far below 2^31 entries); empty slots read the zero row and a zero
+  // scale.
   const int tl = tid - kTblBase;
   const int i0i = (int)i0, i1i = (int)i1, Lci = (int)Lc;
   const int win_p0 = (int)(t - a.W + 1) - Lci;       // window position of slot Lc + x is win_p0 + Lc + x
@@ -164,25 +171,27 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
   const uint8_t* const win_base = a.win.rows + (size_t)b * a.win.cap * a.win.row_bytes;
   const float* const win_sc = (const float*)a.win.scales + (size_t)b * a.win.cap;
   const int32_t* const sel_row = sel_mode ? a.sel + bq * a.k : nullptr;
-  auto table_ptr = [&](int tile, int jsel) -> float {
+  auto table_ptr = [&](int tile) {
     const int slot = i0i + tile * kMT + tl;
     int p = win_p0 + slot;                         // window position (slots >= Lc)
     const bool p_ok = p >= 0 && (a.ring || p < win_cap);
     if (a.ring) p = p >= 0 ? p % a.W : 0;          // uniform branch
     const bool in_list = slot < i1i, is_c = slot < Lci;
-    const int j = sel_mode ? jsel : slot;
+    const int j = sel_mode ? Tsel[tile & (kSlots - 1)][tl] : slot;
     const bool ok = in_list && (is_c ? (unsigned)j < (unsigned)n_ent : p_ok);
     const int idx = is_c ? j : p;
     const uint8_t* ptr = (is_c ? ckv_base : win_base) + (size_t)idx * (is_c ? a.ckv.row_bytes : a.win.row_bytes);
     const float* sp = (is_c ? ckv_sc : win_sc) + idx;
     Tptr[tile & (kSlots - 1)][tl] = ok ? ptr : g_zero_row;
     Tbias[tile & (kSlots - 1)][tl] = ok ? 0.0f : kEmpty;
-    return *(ok ? sp : (const float*)g_zero_row);
+    dma4(ok ? (const void*)sp : (const void*)g_zero_row, Tscl[tile & (kSlots - 1)]);
   };
-  // sel entry of the slot (top-k slots only; others read a zero)
-  auto sel_of = [&](int tile) -> int {
+  // sel entries of the tile's slots, DMA'd into Tsel (top-k slots only;
+  // others read a zero)
+  auto sel_dma = [&](int tile) {
     const int slot = i0i + tile * kMT + tl;
-    return *(sel_mode && slot < Lci && slot < i1i ? sel_row + slot : (const int32_t*)g_zero_row);
+    dma4(sel_mode && slot < Lci && slot < i1i ? (const void*)(sel_row + slot) : (const void*)g_zero_row,
+         Tsel[tile & (kSlots - 1)]);
   };
   // DMA of the raw rows of `tile` into Raw[tile % kStages]: 18 wave-wide
   // loads of 1 KiB, kDmaPerWave on each of waves 0-2; lane l of load qd
@@ -284,24 +293,19 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
 
 #pragma nounroll
   for (int attempt = 0; attempt < 2; ++attempt) {
-    // ---- prologue: tables of tiles 0 .. kLead, rows of tiles 0 .. kLead-1,
-    // tile 0 converted.  Iteration it stores the scale of tile it + kLead,
-    // computes the table of tile it + kLead + 1 and loads the sel of tile
-    // it + kLead + 2.
-    int selreg = 0;
-    float scl_pending = 0.0f;
+    // ---- prologue: sel entries of tiles 0 .. kLead+2, tables of tiles
+    // 0 .. kLead, rows of tiles 0 .. kLead-1, tile 0 converted.  Iteration
+    // it builds the table of tile it + kLead + 1 and DMAs the sel entries of
+    // tile it + kLead + 3.
     const bool tbl = tid >= kTblBase && tid < kTblBase + kMT;
     if (tbl) {
-      int jn = sel_of(0);
 #pragma unroll
-      for (int pt = 0; pt <= kLead; ++pt) {
-        const int jcur = jn;
-        jn = sel_of(pt + 1);
-        const float sv = table_ptr(pt, jcur);
-        if (pt < kLead) Tscl[pt][tl] = sv;
-        else scl_pending = sv;
-      }
-      selreg = jn;
+      for (int pt = 0; pt <= kLead + 2; ++pt) sel_dma(pt);
+      CSA_WAIT_VMCNT0();
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int pt = 0; pt <= kLead; ++pt) table_ptr(pt);
+      CSA_WAIT_VMCNT0();
     }
     __syncthreads();
     if (wave < kDmaWaves) {
@@ -323,10 +327,13 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
       const float* tbs = Tbias[it & (kSlots - 1)];
       const float4 eb0 = *(const float4*)(tbs + 4 * G), eb1 = *(const float4*)(tbs + 16 + 4 * G);
       if (tbl) {
-        Tscl[(it + kLead) & (kSlots - 1)][tl] = scl_pending;
-        // past the end of the list the tables hold empty slots (zero rows)
-        scl_pending = table_ptr(it + kLead + 1, selreg);
-        selreg = sel_of(it + kLead + 2);
+        // past the end of the list the tables hold empty slots (zero rows).
+        // The sel entries of tile it+kLead+1 came two iterations ago and its
+        // scale lands before the conversion in iteration it+kLead: wave 3
+        // issues 8 loads an iteration (2 table DMAs first, then its 6 sink
+        // loads) and waits for all but its newest 12 at the end of each.
+        table_ptr(it + kLead + 1);
+        sel_dma(it + kLead + 3);
       }
       const uint8_t* kb = Kb[it & 1];
 
@@ -476,6 +483,9 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
       // memory clobber keeps the compiler from moving LDS accesses across.
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
+    // every LDS DMA of this pass has landed (the compiler does not see the
+    // asm ones): nothing may write LDS behind the next pass or after exit
+    CSA_WAIT_VMCNT0();
     // head-wide maximum (relative to the reference) and sum over the 4 lanes of a head
     {
       auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(xmax), __float_as_uint(xmax), false, false);
