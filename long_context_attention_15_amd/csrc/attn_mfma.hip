@@ -153,11 +153,12 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
   const int64_t i1 = a.nsplit == 1 ? L : (i0 + a.split_len < L ? i0 + a.split_len : L);
   const int ntiles = i1 > i0 ? (int)((i1 - i0 + kMT - 1) / kMT) : 0;
 
-  // Slot table of tile `tile`, built by the 32 table lanes of wave 3 (lane
-  // tl owns slot i0 + 32 tile + tl of the entry list: a top-k / visible
-  // compressed entry below Lc, a window row above).  The row address and
+  // Slot tables of tiles `tile` and tile + 1 (tile even), built by wave 3
+  // every other iteration (lane tl owns slot i0 + 32 tile + tl of the entry
+  // list: a top-k / visible compressed entry below Lc, a window row above;
+  // lanes 32-63 fill slot row ts + 1 of the tables).  The row address and
   // the softmax bias are stored now; the row scale goes to Tscl by LDS DMA,
-  // as the sel entries go to Tsel two tiles earlier, so no load result ever
+  // as the sel entries go to Tsel two iterations earlier, so no load result ever
   // sits in a register of the tile loop.  Slot arithmetic is 32-bit (lists
   // stay far below 2^31 entries); empty slots read the zero row and a zero
   // scale.
@@ -171,27 +172,28 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
   const uint8_t* const win_base = a.win.rows + (size_t)b * a.win.cap * a.win.row_bytes;
   const float* const win_sc = (const float*)a.win.scales + (size_t)b * a.win.cap;
   const int32_t* const sel_row = sel_mode ? a.sel + bq * a.k : nullptr;
-  auto table_ptr = [&](int tile) {
-    const int slot = i0i + tile * kMT + tl;
+  auto table2 = [&](int tile) {
+    const int ts = tile & (kSlots - 1);            // even
+    const int slot = i0i + tile * kMT + tl;        // tl < 64 spans both tiles
     int p = win_p0 + slot;                         // window position (slots >= Lc)
     const bool p_ok = p >= 0 && (a.ring || p < win_cap);
     if (a.ring) p = p >= 0 ? p % a.W : 0;          // uniform branch
     const bool in_list = slot < i1i, is_c = slot < Lci;
-    const int j = sel_mode ? Tsel[tile & (kSlots - 1)][tl] : slot;
+    const int j = sel_mode ? (&Tsel[0][0])[ts * kMT + tl] : slot;
     const bool ok = in_list && (is_c ? (unsigned)j < (unsigned)n_ent : p_ok);
     const int idx = is_c ? j : p;
     const uint8_t* ptr = (is_c ? ckv_base : win_base) + (size_t)idx * (is_c ? a.ckv.row_bytes : a.win.row_bytes);
     const float* sp = (is_c ? ckv_sc : win_sc) + idx;
-    Tptr[tile & (kSlots - 1)][tl] = ok ? ptr : g_zero_row;
-    Tbias[tile & (kSlots - 1)][tl] = ok ? 0.0f : kEmpty;
-    dma4(ok ? (const void*)sp : (const void*)g_zero_row, Tscl[tile & (kSlots - 1)]);
+    (&Tptr[0][0])[ts * kMT + tl] = ok ? ptr : g_zero_row;
+    (&Tbias[0][0])[ts * kMT + tl] = ok ? 0.0f : kEmpty;
+    dma4(ok ? (const void*)sp : (const void*)g_zero_row, &Tscl[ts][0]);
   };
-  // sel entries of the tile's slots, DMA'd into Tsel (top-k slots only;
-  // others read a zero)
-  auto sel_dma = [&](int tile) {
+  // sel entries of tiles `tile` and tile + 1 (tile even), DMA'd into Tsel
+  // (top-k slots only; others read a zero)
+  auto sel_dma2 = [&](int tile) {
     const int slot = i0i + tile * kMT + tl;
     dma4(sel_mode && slot < Lci && slot < i1i ? (const void*)(sel_row + slot) : (const void*)g_zero_row,
-         Tsel[tile & (kSlots - 1)]);
+         &Tsel[tile & (kSlots - 1)][0]);
   };
   // DMA of the raw rows of `tile` into Raw[tile % kStages]: 18 wave-wide
   // loads of 1 KiB, kDmaPerWave on each of waves 0-2; lane l of load qd
@@ -293,18 +295,18 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
 
 #pragma nounroll
   for (int attempt = 0; attempt < 2; ++attempt) {
-    // ---- prologue: sel entries of tiles 0 .. kLead+2, tables of tiles
-    // 0 .. kLead, rows of tiles 0 .. kLead-1, tile 0 converted.  Iteration
-    // it builds the table of tile it + kLead + 1 and DMAs the sel entries of
-    // tile it + kLead + 3.
-    const bool tbl = tid >= kTblBase && tid < kTblBase + kMT;
+    // ---- prologue: sel entries of tiles 0 .. 7, tables of tiles 0 .. 5,
+    // rows of tiles 0 .. kLead-1, tile 0 converted.  Even iterations it
+    // build the tables of tiles it + 6, it + 7 and DMA the sel entries of
+    // tiles it + 8, it + 9.
+    const bool tbl = tid >= kTblBase;
     if (tbl) {
 #pragma unroll
-      for (int pt = 0; pt <= kLead + 2; ++pt) sel_dma(pt);
+      for (int pt = 0; pt < 8; pt += 2) sel_dma2(pt);
       CSA_WAIT_VMCNT0();
       asm volatile("" ::: "memory");
 #pragma unroll
-      for (int pt = 0; pt <= kLead; ++pt) table_ptr(pt);
+      for (int pt = 0; pt < 6; pt += 2) table2(pt);
       CSA_WAIT_VMCNT0();
     }
     __syncthreads();
@@ -326,14 +328,16 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
       const DmaSrc dsrc = dma_src(it + kLead);
       const float* tbs = Tbias[it & (kSlots - 1)];
       const float4 eb0 = *(const float4*)(tbs + 4 * G), eb1 = *(const float4*)(tbs + 16 + 4 * G);
-      if (tbl) {
+      if (tbl && (it & 1) == 0) {
         // past the end of the list the tables hold empty slots (zero rows).
-        // The sel entries of tile it+kLead+1 came two iterations ago and its
-        // scale lands before the conversion in iteration it+kLead: wave 3
-        // issues 8 loads an iteration (2 table DMAs first, then its 6 sink
-        // loads) and waits for all but its newest 12 at the end of each.
-        table_ptr(it + kLead + 1);
-        sel_dma(it + kLead + 3);
+        // The sel entries of tiles it+6, it+7 came two iterations ago and
+        // their scales land long before their conversion in iteration it+5:
+        // wave 3 issues its 2 table DMAs first, then its 6 sink loads, and
+        // waits for all but its newest 12 loads at the end of each
+        // iteration.  Slot rows: tile X's tables live from iteration X-7
+        // (odd X) to X, within kSlots = 8.
+        table2(it + 6);
+        sel_dma2(it + 8);
       }
       const uint8_t* kb = Kb[it & 1];
 
