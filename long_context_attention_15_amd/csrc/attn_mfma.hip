@@ -362,7 +362,7 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
       // ---- S^T = K Q^T: two row blocks of 16 entries, this wave's 16 heads.
       // The even chain starts at 0 for a filled slot and at kEmpty for an
       // empty one, so empty slots drop out of the softmax by themselves.
-      constexpr int kSD = 5;                        // K-step read distance
+      constexpr int kSD = 3;                        // K-step read distance (measured best)
       f32x4 sa[2], sb[2];                           // even / odd K-step chains
       sa[0] = f32x4{eb0.x, eb0.y, eb0.z, eb0.w};
       sa[1] = f32x4{eb1.x, eb1.y, eb1.z, eb1.w};
