@@ -507,6 +507,66 @@ __device__ __forceinline__ void score_chunk_mfma32(const IdxArgs& a, int b, int 
   }
 }
 
+// FP8 keys of dim 64 for at most 8 heads (the long-list and chunk paths):
+// v_mfma_f32_16x16x32_bf16 with heads as the A rows (8 used) and 16 entries
+// as the columns.  Lane (col, g) reads bytes [16 g, 16 g + 16) of entry
+// row col, so each wave-wide load covers 16 whole rows (1 KiB, contiguous):
+// a streaming read at close to the full HBM rate, which the 32-row layout
+// (every load touching half of each of 32 rows) does not reach.  Its 16
+// bytes feed two K-steps (bytes 8 s .. 8 s + 8 for step s); the q operand
+// takes the same byte order.  Heads 4 g .. 4 g + 3 sit in lane group g, so
+// the head-weighted ReLU sum is 4 FMAs and one row-pair swap (groups 2 and 3
+// carry zero weights).
+__device__ __forceinline__ void score_chunk_fp8_16(const IdxArgs& a, int b, int q, int64_t bq, int64_t c0, int cn,
+                                                   uint32_t* s_keys) {
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int col = lane & 15, g = lane >> 4;
+  const int64_t qrow0 = (int64_t)b * a.qidx.cap + (int64_t)q * a.H_I;
+  float wl[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * g + i;
+    wl[i] = h < a.H_I ? a.head_w[bq * a.H_I + h] * ((const float*)a.qidx.scales)[qrow0 + h] : 0.0f;
+  }
+  long long qa0 = 0, qa1 = 0;
+  if (col < a.H_I) {
+    const uint4 v = *(const uint4*)(a.qidx.rows + (qrow0 + col) * a.qidx.row_bytes + 16 * g);
+    qa0 = (long long)(((unsigned long long)v.y << 32) | v.x);
+    qa1 = (long long)(((unsigned long long)v.w << 32) | v.z);
+  }
+  const bf16x8v qb0 = fp8x8_bf16(qa0), qb1 = fp8x8_bf16(qa1);
+  const float* ksc = (const float*)a.keys.scales;
+  const int64_t krow0 = (int64_t)b * a.keys.cap + c0;
+  const int ngroups = (cn + 15) / 16;
+  constexpr int U = 8;                          // groups of 16 entries in flight per wave
+  for (int grp0 = wave * U; grp0 < ngroups; grp0 += kIdxWaves * U) {
+    uint4 kv[U];
+    float sk[U];
+    // every load is issued (rows past the chunk read its last row, their
+    // scores are never stored) so that all of them are in flight together
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      int e = (grp0 + u) * 16 + col;
+      e = e < cn ? e : cn - 1;
+      kv[u] = load_nt16(a.keys.rows + (krow0 + e) * a.keys.row_bytes + 16 * g);
+      sk[u] = __builtin_nontemporal_load(ksc + krow0 + e);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e = (grp0 + u) * 16 + col;
+      f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qb0, fp8x8_bf16((long long)(((unsigned long long)kv[u].y << 32) | kv[u].x)), c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qb1, fp8x8_bf16((long long)(((unsigned long long)kv[u].w << 32) | kv[u].z)), c, 0, 0, 0);
+      float v = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v = fmaf(wl[i], fmaxf(c[i], 0.0f), v);
+      const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+      v = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      if (g == 0 && e < cn) s_keys[e] = score_key(v * sk[u]);
+    }
+  }
+}
+
 // Keys of entries [c0, c0 + cn) for one query into s_keys (LDS): MFMA for
 // FP8 / MXFP4, float32 FMAs for F32.  Called by all kIdxThreads threads.
 template <int FMT, int DI>
@@ -533,7 +593,8 @@ __device__ __forceinline__ void score_chunk(const IdxArgs& a, int b, int q, int6
     }
   } else if constexpr (DI == 64) {
     if (a.H_I <= 8) {
-      score_chunk_mfma32<FMT>(a, b, q, bq, c0, cn, s_keys);
+      if constexpr (FMT == CSA_FP8_E4M3) score_chunk_fp8_16(a, b, q, bq, c0, cn, s_keys);
+      else score_chunk_mfma32<FMT>(a, b, q, bq, c0, cn, s_keys);
     } else {
       score_chunk_mfma<FMT, DI>(a, b, q, bq, c0, cn, s_keys, s_w);
     }
