@@ -315,6 +315,30 @@ def cpu_baseline(T=131072, n_sample=512, budget_s=15.0):
                       f"rows {t_rows:.1f} s, input generation {t_gen:.1f} s excluded)"}
 
 
+# ------------------------------------------------------------- HBM traffic
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "csa_hca_prefill_128k_hbm_traffic.md")
+KERNEL_SOURCE = os.path.join(ROOT, "long_context_attention_15_amd", "csrc", "attn_mfma.hip")
+
+
+def recorded_traffic(op):
+    """HBM bytes per launch of `op` from the rocprofv3 FETCH_SIZE / WRITE_SIZE
+    record under profiles/ (scaled by a plain copy's counters), or None when
+    there is none or the kernel source changed since the counters were taken
+    (the record carries the SHA-256 of the source it measured)."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_RECORD).read()
+        sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    for line in text.splitlines():
+        if line.startswith("traffic-record:"):
+            f = dict(kv.split("=", 1) for kv in line.split()[1:])
+            if f.get("op") == op and f.get("sha256") == sha:
+                return float(f["bytes"])
+    return None
+
+
 # -------------------------------------------------------------------- main
 def main():
     ap = argparse.ArgumentParser()
@@ -324,12 +348,23 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=20)
     ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (the reference for scaling HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the path is built and timed on a single MI355X; "
               "multi-GPU runs are not part of this build.", file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n}), flush=True)
+        return
     import long_context_attention_15_amd as csa
     csa.load()
     log(f"lib {csa.version()} on {torch.cuda.get_device_name(0)}")
@@ -353,7 +388,7 @@ def main():
         dom = max(alg, key=lambda n: per[n])
         ach = alg[dom]["flops"] / (per[dom] * 1e-3) / 1e12
         result["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": MFMA_BF16_TFLOPS,
-                              "unit": "TFLOP/s", "frac": ach / MFMA_BF16_TFLOPS, "traffic": None}
+                              "unit": "TFLOP/s", "frac": ach / MFMA_BF16_TFLOPS, "traffic": recorded_traffic(dom)}
         result["prefill_ops_tflops"] = {n: alg[n]["flops"] / (per[n] * 1e-3) / 1e12 for n in alg}
         del pf
         torch.cuda.empty_cache()
