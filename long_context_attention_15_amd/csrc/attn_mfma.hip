@@ -172,14 +172,14 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
   const uint8_t* const win_base = a.win.rows + (size_t)b * a.win.cap * a.win.row_bytes;
   const float* const win_sc = (const float*)a.win.scales + (size_t)b * a.win.cap;
   const int32_t* const sel_row = sel_mode ? a.sel + bq * a.k : nullptr;
-  auto table2 = [&](int tile) {
+  auto table2 = [&](int tile, int jsel) {
     const int ts = tile & (kSlots - 1);            // even
     const int slot = i0i + tile * kMT + tl;        // tl < 64 spans both tiles
     int p = win_p0 + slot;                         // window position (slots >= Lc)
     const bool p_ok = p >= 0 && (a.ring || p < win_cap);
     if (a.ring) p = p >= 0 ? p % a.W : 0;          // uniform branch
     const bool in_list = slot < i1i, is_c = slot < Lci;
-    const int j = sel_mode ? (&Tsel[0][0])[ts * kMT + tl] : slot;
+    const int j = sel_mode ? jsel : slot;
     const bool ok = in_list && (is_c ? (unsigned)j < (unsigned)n_ent : p_ok);
     const int idx = is_c ? j : p;
     const uint8_t* ptr = (is_c ? ckv_base : win_base) + (size_t)idx * (is_c ? a.ckv.row_bytes : a.win.row_bytes);
@@ -295,18 +295,23 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
 
 #pragma nounroll
   for (int attempt = 0; attempt < 2; ++attempt) {
-    // ---- prologue: sel entries of tiles 0 .. 7, tables of tiles 0 .. 5,
+    // ---- prologue: sel entries of tiles 0 .. 9, tables of tiles 0 .. 5,
     // rows of tiles 0 .. kLead-1, tile 0 converted.  Even iterations it
-    // build the tables of tiles it + 6, it + 7 and DMA the sel entries of
-    // tiles it + 8, it + 9.
+    // build the tables of tiles it + 6, it + 7 (from sel entries read into a
+    // register in the PV phase of the iteration before) and DMA the sel
+    // entries of tiles it + 10, it + 11.
     const bool tbl = tid >= kTblBase;
+    int selnext = 0;
     if (tbl) {
 #pragma unroll
       for (int pt = 0; pt < 8; pt += 2) sel_dma2(pt);
       CSA_WAIT_VMCNT0();
       asm volatile("" ::: "memory");
 #pragma unroll
-      for (int pt = 0; pt < 6; pt += 2) table2(pt);
+      for (int pt = 0; pt < 6; pt += 2) table2(pt, (&Tsel[0][0])[pt * kMT + tl]);
+      selnext = (&Tsel[0][0])[6 * kMT + tl];
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // slots 0, 1 read before they are refilled
+      sel_dma2(8);
       CSA_WAIT_VMCNT0();
     }
     __syncthreads();
@@ -330,14 +335,16 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
       const float4 eb0 = *(const float4*)(tbs + 4 * G), eb1 = *(const float4*)(tbs + 16 + 4 * G);
       if (tbl && (it & 1) == 0) {
         // past the end of the list the tables hold empty slots (zero rows).
-        // The sel entries of tiles it+6, it+7 came two iterations ago and
-        // their scales land long before their conversion in iteration it+5:
-        // wave 3 issues its 2 table DMAs first, then its 6 sink loads, and
-        // waits for all but its newest 12 loads at the end of each
-        // iteration.  Slot rows: tile X's tables live from iteration X-7
-        // (odd X) to X, within kSlots = 8.
-        table2(it + 6);
-        sel_dma2(it + 8);
+        // The sel entries of tiles it+6, it+7 were DMA'd four iterations ago
+        // and read into selnext in the previous iteration; their scales land
+        // long before their conversion in iteration it+5.  Wave 3 issues its
+        // 2 table DMAs first, then its 6 sink loads, and waits for all but its
+        // newest 12 loads at the end of each iteration, so table DMAs land by
+        // the end of the next one.  Slot rows: tile X's tables live from
+        // iteration X-7 (odd X) to X, its sel entries from X-10 to X-7, within
+        // kSlots = 8.
+        table2(it + 6, selnext);
+        sel_dma2(it + 10);
       }
       const uint8_t* kb = Kb[it & 1];
 
@@ -467,6 +474,7 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
         // Branch-free so that the LDS-read bookkeeping of the compiler stays
         // exact: past the end of the list the rows are zero rows, and wave 3
         // loads a zero row into a sink buffer.
+        if (db == 3 && tbl && (it & 1)) selnext = (&Tsel[0][0])[((it + 7) & (kSlots - 1)) * kMT + tl];
         if ((db & 3) == 1 && (db >> 2) < kDmaPerWave) {
           const int j = db >> 2;
           const uint8_t* src = dma_sink ? g_zero_row + 16 * lane : dsrc.p[j] + dma_off[j];
