@@ -298,6 +298,25 @@ def test_hca_prefill_parity(lib, H, D, R, T, m, W):
         assert np.all(got[: m - 1] == 0)                # no entries, no window, no sink
 
 
+@pytest.mark.parametrize("tau_mult", [60.0, 0.0, -1.0])
+def test_csa_prefill_extreme_and_nonpositive_scales(lib, tau_mult):
+    """A large softmax scale puts later logits far above the first tile's
+    maximum, which the MFMA kernel meets with its exact-maximum recompute; a
+    zero or negative scale takes the general kernel (the MFMA kernel masks
+    empty slots through a -1e30 logit).  Both must still match the oracle."""
+    import torch
+    H, D, R, T, m, k, W = 64, 512, 64, 400, 4, 64, 128
+    N = T // m
+    qd, qv, cst, cdeq, wst, wdeq, sink = _attn_inputs(1, T, H, D, R, "fp8", "bf16", N, T, layer=2)
+    sel = Hx.random_selection(T, m, N, k, seed=5)
+    out = torch.empty(qd.shape, dtype=qd.dtype, device=Hx.dev())
+    tau = tau_mult / math.sqrt(D)
+    lib.sparse_attn_prefill(qd, cst, N, Hx.to_dev(sel[None]), k, wst, W, Hx.to_dev(sink), tau, out)
+    _sync()
+    want, _ = O.csa_prefill(qv[0], cdeq[0], sel, wdeq[0], W, sink.astype(np.float64), tau)
+    Hx.check_attn(out.float().cpu().numpy()[0], want)
+
+
 def _decode_setup(B, H, D, R, N, W, layer):
     q = synth.tensor(0, "q", (B, H, D), rmsnorm=True, layer=layer)
     ckv = synth.tensor(0, "kv", (B, N, D), rmsnorm=True, layer=layer)
