@@ -270,11 +270,12 @@ bool attn_supported(int H, int D) { return H >= 1 && attn_shape(H, D).ok; }
 // (about 2 per CU) when the queries alone do not, each split a whole number
 // of 32-entry tiles and at least `min_len` entries.  hpw = heads per
 // workgroup of the kernel that runs.
-static int attn_nsplit_for(int B, int Tq, int H, int hpw, int64_t max_list, int min_len, int& split_len) {
+static int attn_nsplit_for(int B, int Tq, int H, int hpw, int64_t max_list, int min_len, int target,
+                           int& split_len) {
   const int64_t wgs = (int64_t)B * Tq * ((H + hpw - 1) / hpw);
   split_len = 0;
-  if (wgs >= 512 || max_list <= min_len) return 1;
-  const int64_t want = (512 + wgs - 1) / wgs;            // splits per query
+  if (wgs >= target || max_list <= min_len) return 1;
+  const int64_t want = (target + wgs - 1) / wgs;         // splits per query
   int64_t len = (max_list + want - 1) / want;
   len = ((len + 31) / 32) * 32;
   if (len < min_len) len = min_len;
@@ -287,10 +288,15 @@ static int attn_nsplit_for(int B, int Tq, int H, int hpw, int64_t max_list, int 
   return (int)ns;
 }
 
+// The MFMA kernel runs one workgroup per CU (its LDS tiles take most of the
+// 160 KB), so decode splits aim at one round of workgroups over the 256 CUs.
+constexpr int kMfmaTargetWgs = 256;
+constexpr int kMfmaMinSplit = 256;
+
 static int attn_nsplit(int B, int Tq, int H, int D, int64_t max_list, bool mfma, int& split_len) {
-  if (mfma) return attn_nsplit_for(B, Tq, H, 64, max_list, 256, split_len);
+  if (mfma) return attn_nsplit_for(B, Tq, H, 64, max_list, kMfmaMinSplit, kMfmaTargetWgs, split_len);
   const AttnShape s = attn_shape(H, D);
-  return attn_nsplit_for(B, Tq, H, s.hg ? s.hg : 1, max_list, 64, split_len);
+  return attn_nsplit_for(B, Tq, H, s.hg ? s.hg : 1, max_list, 64, 512, split_len);
 }
 
 size_t attn_workspace(int B, int Tq, int H, int D, int64_t max_list) {
