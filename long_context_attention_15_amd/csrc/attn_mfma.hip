@@ -110,10 +110,10 @@ __device__ __forceinline__ int kb_swz(int r) { return r & 15; }
 // waited for), slot table of tile it+5.
 constexpr int kStages = 4;
 constexpr int kLead = kStages;                    // DMA distance in tiles
-constexpr int kSlots = 8;                         // slot tables (>= kLead + 2, power of two)
+constexpr int kSlots = 16;                        // slot tables (two build batches of 8 tiles)
+constexpr int kBatch = 8;                         // tiles per table build (2 per wavefront)
 constexpr int kDmaWaves = 3;                      // waves 0-2 issue the row DMA, wave 3 builds the slot tables
 constexpr int kDmaPerWave = kRawLoads / kDmaWaves; // 6 wave-wide loads each
-constexpr int kTblBase = kDmaWaves * 64;           // first thread of the table wave
 
 // 16-byte-per-lane LDS DMA (global_load_lds_dwordx4: lane l's 16 bytes land
 // at LDS dst + 16 l), written as inline asm.  The compiler's own LDS-DMA
@@ -153,16 +153,18 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
   const int64_t i1 = a.nsplit == 1 ? L : (i0 + a.split_len < L ? i0 + a.split_len : L);
   const int ntiles = i1 > i0 ? (int)((i1 - i0 + kMT - 1) / kMT) : 0;
 
-  // Slot tables of tiles `tile` and tile + 1 (tile even), built by wave 3
-  // every other iteration (lane tl owns slot i0 + 32 tile + tl of the entry
-  // list: a top-k / visible compressed entry below Lc, a window row above;
-  // lanes 32-63 fill slot row ts + 1 of the tables).  The row address and
+  // Slot tables of tiles `tile` and tile + 1 (tile even), built by one
+  // wavefront (lane tl owns slot i0 + 32 tile + tl of the entry list: a
+  // top-k / visible compressed entry below Lc, a window row above; lanes
+  // 32-63 fill slot row ts + 1 of the tables).  All four wavefronts build
+  // together, 8 tiles every 8 iterations, so the work never leaves one
+  // wavefront behind at the tile barrier.  The row address and
   // the softmax bias are stored now; the row scale goes to Tscl by LDS DMA,
-  // as the sel entries go to Tsel two iterations earlier, so no load result ever
+  // as the sel entries go to Tsel one batch earlier, so no load result ever
   // sits in a register of the tile loop.  Slot arithmetic is 32-bit (lists
   // stay far below 2^31 entries); empty slots read the zero row and a zero
   // scale.
-  const int tl = tid - kTblBase;
+  const int tl = lane;
   const int i0i = (int)i0, i1i = (int)i1, Lci = (int)Lc;
   const int win_p0 = (int)(t - a.W + 1) - Lci;       // window position of slot Lc + x is win_p0 + Lc + x
   const bool sel_mode = a.mode == kModeSel;
@@ -295,23 +297,16 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
 
 #pragma nounroll
   for (int attempt = 0; attempt < 2; ++attempt) {
-    // ---- prologue: sel entries of tiles 0 .. 9, tables of tiles 0 .. 5,
-    // rows of tiles 0 .. kLead-1, tile 0 converted.  Even iterations it
-    // build the tables of tiles it + 6, it + 7 (from sel entries read into a
-    // register in the PV phase of the iteration before) and DMA the sel
-    // entries of tiles it + 10, it + 11.
-    const bool tbl = tid >= kTblBase;
-    int selnext = 0;
-    if (tbl) {
-#pragma unroll
-      for (int pt = 0; pt < 8; pt += 2) sel_dma2(pt);
+    // ---- prologue: sel entries of tiles 0 .. 15, tables of tiles 0 .. 7,
+    // rows of tiles 0 .. kLead-1, tile 0 converted.  Iterations it = 0 mod 8
+    // build the tables of tiles it + 8 .. it + 15 (wave w: it + 8 + 2 w and
+    // the next) and DMA the sel entries of tiles it + 16 .. it + 23.
+    {
+      sel_dma2(2 * wave);
       CSA_WAIT_VMCNT0();
       asm volatile("" ::: "memory");
-#pragma unroll
-      for (int pt = 0; pt < 6; pt += 2) table2(pt, (&Tsel[0][0])[pt * kMT + tl]);
-      selnext = (&Tsel[0][0])[6 * kMT + tl];
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // slots 0, 1 read before they are refilled
-      sel_dma2(8);
+      table2(2 * wave, (&Tsel[0][0])[2 * wave * kMT + tl]);
+      sel_dma2(kBatch + 2 * wave);
       CSA_WAIT_VMCNT0();
     }
     __syncthreads();
@@ -333,18 +328,16 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
       const DmaSrc dsrc = dma_src(it + kLead);
       const float* tbs = Tbias[it & (kSlots - 1)];
       const float4 eb0 = *(const float4*)(tbs + 4 * G), eb1 = *(const float4*)(tbs + 16 + 4 * G);
-      if (tbl && (it & 1) == 0) {
+      if ((it & (kBatch - 1)) == 0) {
         // past the end of the list the tables hold empty slots (zero rows).
-        // The sel entries of tiles it+6, it+7 were DMA'd four iterations ago
-        // and read into selnext in the previous iteration; their scales land
-        // long before their conversion in iteration it+5.  Wave 3 issues its
-        // 2 table DMAs first, then its 6 sink loads, and waits for all but its
-        // newest 12 loads at the end of each iteration, so table DMAs land by
-        // the end of the next one.  Slot rows: tile X's tables live from
-        // iteration X-7 (odd X) to X, its sel entries from X-10 to X-7, within
-        // kSlots = 8.
-        table2(it + 6, selnext);
-        sel_dma2(it + 10);
+        // Tile X's tables are built at iteration X-15 .. X-8 and last read at
+        // iteration X; its sel entries arrive at X-23 .. X-16 and are read at
+        // the build: 16 slot rows cover both.  Table DMAs (2 per wave) go out
+        // before the row loads of the iteration, so the wait at its end
+        // leaves them in flight and the next iteration's wait lands them,
+        // long before their first use.
+        table2(it + kBatch + 2 * wave, (&Tsel[0][0])[((it + kBatch + 2 * wave) & (kSlots - 1)) * kMT + tl]);
+        sel_dma2(it + 2 * kBatch + 2 * wave);
       }
       const uint8_t* kb = Kb[it & 1];
 
@@ -474,7 +467,6 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
         // Branch-free so that the LDS-read bookkeeping of the compiler stays
         // exact: past the end of the list the rows are zero rows, and wave 3
         // loads a zero row into a sink buffer.
-        if (db == 3 && tbl && (it & 1)) selnext = (&Tsel[0][0])[((it + 7) & (kSlots - 1)) * kMT + tl];
         if ((db & 3) == 1 && (db >> 2) < kDmaPerWave) {
           const int j = db >> 2;
           const uint8_t* src = dma_sink ? g_zero_row + 16 * lane : dsrc.p[j] + dma_off[j];
