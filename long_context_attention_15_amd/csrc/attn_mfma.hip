@@ -201,7 +201,7 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
   // loads of 1 KiB, kDmaPerWave on each of waves 0-2; lane l of load qd
   // fills LDS unit 64 qd + l, i.e. the (row, unit) that unit_pos places
   // there.  dma_src reads the slot table (early, so that its LDS latency is
-  // hidden), dma_issue starts the loads.
+  // hidden); the loads go out in the tile loop and the prologue.
   // Per load j: the slot-table row and the byte offset within the row of
   // this lane's 16 bytes (fixed per lane); wave 3 mirrors wave 0's rows.
   int dma_row[kDmaPerWave], dma_off[kDmaPerWave];
@@ -223,14 +223,7 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
     for (int j = 0; j < kDmaPerWave; ++j) d.p[j] = Tptr[tile & (kSlots - 1)][dma_row[j]];
     return d;
   };
-  auto dma_issue = [&](int tile, const DmaSrc& d) {
-    uint8_t* dst = Raw[tile % kStages];
-#pragma unroll
-    for (int j = 0; j < kDmaPerWave; ++j) {
-      const int qd = wave + kDmaWaves * j;
-      __builtin_amdgcn_global_load_lds((const void*)(d.p[j] + dma_off[j]), (lds_void*)(dst + 1024 * qd), 16, 0, 0);
-    }
-  };
+
 
   // Q^T operands: K-step ks covers dims [32 ks, 32 ks + 32); lane group G
   // takes dims 32 ks + 8 G .. +8.  Steps 0..13 are the FP8 dims, 14 and 15
@@ -301,27 +294,35 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
     // rows of tiles 0 .. kLead-1, tile 0 converted.  Iterations it = 0 mod 8
     // build the tables of tiles it + 8 .. it + 15 (wave w: it + 8 + 2 w and
     // the next) and DMA the sel entries of tiles it + 16 .. it + 23.
+    // Only the sel entries are waited for before the rows go out: the row
+    // loads need just the row addresses (LDS stores), and the scale and
+    // next sel loads issued before them complete before them.  Barriers
+    // without the release fence of __syncthreads (which would wait for
+    // every load in flight).
     {
       sel_dma2(2 * wave);
       CSA_WAIT_VMCNT0();
       asm volatile("" ::: "memory");
       table2(2 * wave, (&Tsel[0][0])[2 * wave * kMT + tl]);
       sel_dma2(kBatch + 2 * wave);
-      CSA_WAIT_VMCNT0();
     }
-    __syncthreads();
-    if (wave < kDmaWaves) {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // rows of tiles 0 .. kLead-1, branch-free like the loop's (zero rows
+    // past the end of the list, wave 3 into the sink)
 #pragma unroll
-      for (int pt = 0; pt < kLead; ++pt)
-        if (pt < ntiles) dma_issue(pt, dma_src(pt));
+    for (int pt = 0; pt < kLead; ++pt) {
+      const DmaSrc d = dma_src(pt);
+#pragma unroll
+      for (int j = 0; j < kDmaPerWave; ++j) {
+        const uint8_t* src = dma_sink ? g_zero_row + 16 * lane : d.p[j] + dma_off[j];
+        uint8_t* dst = dma_sink ? DmaSink : Raw[pt] + 1024 * (wave + kDmaWaves * j);
+        dma16(src, dst);
+      }
     }
-    // tiles 0 and 1 in (loads complete in order)
-    if (ntiles >= 4) CSA_WAIT_VMCNT(2 * kDmaPerWave);
-    else if (ntiles == 3) CSA_WAIT_VMCNT(kDmaPerWave);
-    else CSA_WAIT_VMCNT0();
-    __syncthreads();
-    if (ntiles > 0) convert_tile(0);
-    __syncthreads();
+    CSA_WAIT_VMCNT(2 * kDmaPerWave);           // tiles 0 and 1 in (loads complete in order)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    convert_tile(0);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
     for (int it = 0; it < ntiles; ++it) {
       // slot-table reads of this iteration go out first
