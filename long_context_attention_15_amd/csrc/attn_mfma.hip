@@ -154,9 +154,10 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
   const int ntiles = i1 > i0 ? (int)((i1 - i0 + kMT - 1) / kMT) : 0;
 
   // Slot tables of tiles `tile` and tile + 1 (tile even), built by one
-  // wavefront (lane tl owns slot i0 + 32 tile + tl of the entry list: a
-  // top-k / visible compressed entry below Lc, a window row above; lanes
-  // 32-63 fill slot row ts + 1 of the tables).  All four wavefronts build
+  // wavefront (lane tl owns slot i0 + 32 tile + tl of the entry list: the
+  // W window rows first, whose addresses need no sel entry, then the Lc
+  // top-k / visible compressed entries; lanes 32-63 fill slot row ts + 1 of
+  // the tables).  All four wavefronts build
   // together, 8 tiles every 8 iterations, so the work never leaves one
   // wavefront behind at the tile barrier.  The row address and
   // the softmax bias are stored now; the row scale goes to Tscl by LDS DMA,
@@ -165,8 +166,8 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
   // stay far below 2^31 entries); empty slots read the zero row and a zero
   // scale.
   const int tl = lane;
-  const int i0i = (int)i0, i1i = (int)i1, Lci = (int)Lc;
-  const int win_p0 = (int)(t - a.W + 1) - Lci;       // window position of slot Lc + x is win_p0 + Lc + x
+  const int i0i = (int)i0, i1i = (int)i1;
+  const int win_p0 = (int)(t - a.W + 1);             // window position of slot x < W
   const bool sel_mode = a.mode == kModeSel;
   const int n_ent = (int)a.n_entries, win_cap = (int)a.win.cap;
   const uint8_t* const ckv_base = a.ckv.rows + (size_t)b * a.ckv.cap * a.ckv.row_bytes;
@@ -177,11 +178,11 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
   auto table2 = [&](int tile, int jsel) {
     const int ts = tile & (kSlots - 1);            // even
     const int slot = i0i + tile * kMT + tl;        // tl < 64 spans both tiles
-    int p = win_p0 + slot;                         // window position (slots >= Lc)
+    int p = win_p0 + slot;                         // window position (slots < W)
     const bool p_ok = p >= 0 && (a.ring || p < win_cap);
     if (a.ring) p = p >= 0 ? p % a.W : 0;          // uniform branch
-    const bool in_list = slot < i1i, is_c = slot < Lci;
-    const int j = sel_mode ? jsel : slot;
+    const bool in_list = slot < i1i, is_c = slot >= a.W;
+    const int j = sel_mode ? jsel : slot - a.W;
     const bool ok = in_list && (is_c ? (unsigned)j < (unsigned)n_ent : p_ok);
     const int idx = is_c ? j : p;
     const uint8_t* ptr = (is_c ? ckv_base : win_base) + (size_t)idx * (is_c ? a.ckv.row_bytes : a.win.row_bytes);
@@ -194,7 +195,7 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
   // (top-k slots only; others read a zero)
   auto sel_dma2 = [&](int tile) {
     const int slot = i0i + tile * kMT + tl;
-    dma4(sel_mode && slot < Lci && slot < i1i ? (const void*)(sel_row + slot) : (const void*)g_zero_row,
+    dma4(sel_mode && slot >= a.W && slot < i1i ? (const void*)(sel_row + (slot - a.W)) : (const void*)g_zero_row,
          &Tsel[tile & (kSlots - 1)][0]);
   };
   // DMA of the raw rows of `tile` into Raw[tile % kStages]: 18 wave-wide
@@ -294,17 +295,24 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
     // rows of tiles 0 .. kLead-1, tile 0 converted.  Iterations it = 0 mod 8
     // build the tables of tiles it + 8 .. it + 15 (wave w: it + 8 + 2 w and
     // the next) and DMA the sel entries of tiles it + 16 .. it + 23.
-    // Only the sel entries are waited for before the rows go out: the row
-    // loads need just the row addresses (LDS stores), and the scale and
-    // next sel loads issued before them complete before them.  Barriers
-    // without the release fence of __syncthreads (which would wait for
-    // every load in flight).
-    {
-      sel_dma2(2 * wave);
+    // The first kLead tiles hold window rows when the split starts the list
+    // and the window spans them (or the list has no sel entries): their row
+    // loads then go out before the sel entries of the top-k tiles arrive,
+    // which waves 2 and 3 wait for to build tiles 4 .. 7.  Otherwise every
+    // wave waits for its sel entries first.  Scale and sel loads issued
+    // before a wave's row loads complete before them; barriers without the
+    // release fence of __syncthreads (which would wait for every load in
+    // flight).
+    const bool early = !sel_mode || (i0i == 0 && a.W >= kLead * kMT);
+    const bool need_sel = sel_mode && i0i + (2 * wave + 2) * kMT > a.W;   // wave-uniform
+    sel_dma2(2 * wave);
+    sel_dma2(kBatch + 2 * wave);
+    if (early) {
+      if (!need_sel) table2(2 * wave, 0);      // window rows / lists without sel entries
+    } else {
       CSA_WAIT_VMCNT0();
       asm volatile("" ::: "memory");
       table2(2 * wave, (&Tsel[0][0])[2 * wave * kMT + tl]);
-      sel_dma2(kBatch + 2 * wave);
     }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     // rows of tiles 0 .. kLead-1, branch-free like the loop's (zero rows
@@ -319,7 +327,17 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
         dma16(src, dst);
       }
     }
-    CSA_WAIT_VMCNT(2 * kDmaPerWave);           // tiles 0 and 1 in (loads complete in order)
+    if (early && need_sel) {
+      // sel entries of tiles 2 w, 2 w + 1 in (only the second sel load and
+      // the kLead kDmaPerWave row loads may still be in flight), then the
+      // tables and tiles 0, 1 (their scale load may stay in flight)
+      CSA_WAIT_VMCNT(kLead * kDmaPerWave + 1);
+      asm volatile("" ::: "memory");
+      table2(2 * wave, (&Tsel[0][0])[2 * wave * kMT + tl]);
+      CSA_WAIT_VMCNT(2 * kDmaPerWave + 1);
+    } else {
+      CSA_WAIT_VMCNT(2 * kDmaPerWave);         // tiles 0 and 1 in (loads complete in order)
+    }
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     convert_tile(0);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
