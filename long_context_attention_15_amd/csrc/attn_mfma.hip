@@ -534,46 +534,70 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
   }
   const float mrun = mset ? mref : -INFINITY;
 
-  // ---- epilogue: lane holds O^T rows (dims) 16 db + 4 G + (0..3) of head h
-  const int64_t qoff = (bq * a.H + h) * (int64_t)kMD;
-  if (a.nsplit > 1) {
-    // partial: m (natural log units), l, unnormalised o
-    float* wo = a.ws + ((bq * a.H + h) * a.nsplit + blockIdx.z) * (int64_t)kMD;
-    float* wml = a.ws + (int64_t)a.B * a.Tq * a.H * a.nsplit * kMD + ((bq * a.H + h) * a.nsplit + blockIdx.z) * 2;
+  // ---- epilogue: lane holds O^T rows (dims) 16 db + 4 G + (0..3) of head h.
+  // The output rows go out through LDS (the raw row buffers are free: every
+  // load has landed and every wave is past the tile loop), so that each
+  // store instruction writes one contiguous 1 KiB piece of a head's row;
+  // stored straight from the accumulators, every instruction would scatter
+  // 32-byte pieces over 16 rows, which the memory system absorbs far more
+  // slowly under the gather traffic of the other CUs.  Wave w stages its 16
+  // heads in 16 rows of kStageRow bytes (1 KiB of data, padded so that the
+  // row starts fall in different banks); FP32 rows go in two halves.
+  const bool split = a.nsplit > 1;
+  float scale = 1.0f, lse = -INFINITY;
+  if (!split) {
+    const float sig2 = (a.partial || !a.sink) ? -INFINITY : a.sink[h] * kLog2e;
+    const float M = fmaxf(mrun, sig2);
+    scale = 0.0f;
+    if (M > -INFINITY) {
+      const float fm = mrun > -INFINITY ? exp2f(mrun - M) : 0.0f;
+      const float Z = lrun * fm + (sig2 > -INFINITY ? exp2f(sig2 - M) : 0.0f);
+      scale = fm / Z;
+      lse = (M + log2f(Z)) * kLn2;
+    }
+  }
+  const bool f32 = split || a.out_f32;
+  constexpr int kStageRow = 1024 + 16;
+  uint8_t* const stg = &Raw[0][0] + wave * kMHeads * kStageRow;
+  const int64_t hrow0 = bq * a.H + blockIdx.y * 64 + wave * kMHeads;   // this wave's first head row
 #pragma unroll
-    for (int db = 0; db < 32; ++db)
-      *(float4*)(wo + 16 * db + 4 * G) = make_float4(acc[db][0], acc[db][1], acc[db][2], acc[db][3]);
+  for (int c = 0; c < 2; ++c) {
+    if (c == 1 && !f32) break;                   // uniform
+    if (f32) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const f32x4 v = acc[16 * c + k] * scale;
+        *(f32x4*)(stg + l16 * kStageRow + 64 * k + 16 * G) = v;
+      }
+    } else {
+#pragma unroll
+      for (int db = 0; db < 32; ++db) {
+        u32x2 w;
+        w.x = f32_to_bf16(acc[db][0] * scale) | (f32_to_bf16(acc[db][1] * scale) << 16);
+        w.y = f32_to_bf16(acc[db][2] * scale) | (f32_to_bf16(acc[db][3] * scale) << 16);
+        *(u32x2*)(stg + l16 * kStageRow + 32 * db + 8 * G) = w;
+      }
+    }
+    // (one wave writes and reads its own rows: its LDS accesses stay in order)
+#pragma unroll
+    for (int r = 0; r < kMHeads; ++r) {
+      const u32x4 x = *(const u32x4*)(stg + r * kStageRow + 16 * lane);
+      const int64_t hr = hrow0 + r;
+      uint8_t* dst = split ? (uint8_t*)(a.ws + (hr * a.nsplit + blockIdx.z) * (int64_t)kMD)
+                           : (f32 ? (uint8_t*)((float*)a.out + hr * kMD) : (uint8_t*)((uint16_t*)a.out + hr * kMD));
+      *(u32x4*)(dst + 1024 * c + 16 * lane) = x;
+    }
+  }
+  if (split) {
+    // partial: m (natural log units), l, unnormalised o
     if (G == 0) {
+      float* wml = a.ws + (int64_t)a.B * a.Tq * a.H * a.nsplit * kMD + ((bq * a.H + h) * a.nsplit + blockIdx.z) * 2;
       wml[0] = mrun > -INFINITY ? mrun * kLn2 : -INFINITY;
       wml[1] = lrun;
     }
-    return;
+  } else if (a.lse && G == 0) {
+    a.lse[bq * a.H + h] = lse;
   }
-  const float sig2 = (a.partial || !a.sink) ? -INFINITY : a.sink[h] * kLog2e;
-  const float M = fmaxf(mrun, sig2);
-  float scale = 0.0f, lse = -INFINITY;
-  if (M > -INFINITY) {
-    const float fm = mrun > -INFINITY ? exp2f(mrun - M) : 0.0f;
-    const float Z = lrun * fm + (sig2 > -INFINITY ? exp2f(sig2 - M) : 0.0f);
-    scale = fm / Z;
-    lse = (M + log2f(Z)) * kLn2;
-  }
-#pragma unroll
-  for (int db = 0; db < 32; ++db) {
-    const int d = 16 * db + 4 * G;
-    float v[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = acc[db][i] * scale;
-    if (a.out_f32) {
-      *(float4*)((float*)a.out + qoff + d) = make_float4(v[0], v[1], v[2], v[3]);
-    } else {
-      u32x2 w;
-      w.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
-      w.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
-      *(u32x2*)((uint16_t*)a.out + qoff + d) = w;
-    }
-  }
-  if (a.lse && G == 0) a.lse[bq * a.H + h] = lse;
 }
 
 // The MFMA kernel masks empty slots through a -1e30 logit, which needs a
