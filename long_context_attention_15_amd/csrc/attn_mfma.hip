@@ -226,6 +226,9 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
   };
 
 
+  // the head's sink logit (log2 units), loaded now so that the epilogue
+  // does not wait a memory round trip for it
+  const float sig2 = (a.nsplit > 1 || a.partial || !a.sink) ? -INFINITY : a.sink[h] * kLog2e;
   // Q^T operands: K-step ks covers dims [32 ks, 32 ks + 32); lane group G
   // takes dims 32 ks + 8 G .. +8.  Steps 0..13 are the FP8 dims, 14 and 15
   // the BF16 RoPE dims.
@@ -546,7 +549,6 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
   const bool split = a.nsplit > 1;
   float scale = 1.0f, lse = -INFINITY;
   if (!split) {
-    const float sig2 = (a.partial || !a.sink) ? -INFINITY : a.sink[h] * kLog2e;
     const float M = fmaxf(mrun, sig2);
     scale = 0.0f;
     if (M > -INFINITY) {
