@@ -1120,11 +1120,12 @@ static hipError_t launch_idx_stream(const IdxArgs& ia, hipStream_t st) {
 // Few queries over many entries (decode at long context).  Three kernels,
 // exact, reading each key once at full HBM rate:
 //   A  chunks of kLChunk entries: the keys of the chunk's scores go to the
-//      workspace, and so do the kLTop largest of the maxima of kLSets
-//      strided subsets of the chunk (each maximum is a real entry);
+//      workspace, and so does the m-th largest of the maxima of kLSets
+//      strided subsets of the chunk (each maximum is a real entry), m =
+//      ceil(k / #chunks whose subsets are all nonempty);
 //   B  per (query, segment of kLSeg entries): T = the smallest, over the
 //      chunks whose subsets are all nonempty, of their m-th largest subset
-//      maximum, m = ceil(k / #such chunks).  Each such chunk has at least m
+//      maximum.  Each such chunk has at least m
 //      entries >= T, so at least k entries have a key >= T: T is at most the
 //      k-th largest key and every member of the top-k has a key >= T.  The
 //      segment's entries with key >= T are compacted, in index order, into
@@ -1132,11 +1133,10 @@ static hipError_t launch_idx_stream(const IdxArgs& ia, hipStream_t st) {
 //   C  per query: the regions, concatenated in segment order (= index
 //      order), hold every candidate; the exact top-k (ties to the smaller
 //      index) is selected from them and emitted in ascending index order.
-constexpr int kLChunk = 4096;
+constexpr int kLChunk = 8192;
 constexpr int kLSeg = 16384;
 constexpr int kLPerWave = kLSeg / kIdxWaves;  // segment entries per wave in the compaction
 constexpr int kLSets = 128;                   // strided sets per chunk
-constexpr int kLTop = 32;                     // largest set maxima kept per chunk
 
 template <int FMT, int DI>
 __global__ __launch_bounds__(kIdxThreads) void idx_long_score_kernel(IdxArgs a) {
@@ -1154,14 +1154,17 @@ __global__ __launch_bounds__(kIdxThreads) void idx_long_score_kernel(IdxArgs a) 
   const int cn = cn64 < 0 ? 0 : (cn64 > kLChunk ? kLChunk : (int)cn64);
   uint8_t* wq = a.ws + bq * a.per_query;
   uint32_t* scores = (uint32_t*)(wq + a.off_scores);
-  uint32_t* uni = (uint32_t*)(wq + a.off_uni) + (int64_t)c * a.lm;
+  uint32_t* uni = (uint32_t*)(wq + a.off_uni) + c;
   if (cn == 0) return;                          // uniform (such chunks are never read)
   score_chunk<FMT, DI>(a, b, q, bq, c0, cn, s_keys, s_q, s_w);
   __syncthreads();
   for (int i = tid; i < cn; i += kIdxThreads) scores[c0 + i] = s_keys[i];
   // the largest key of each strided set {r + kLSets j} of the chunk (a real
-  // entry, 0 if the set is empty); the kLTop largest of these maxima, in
-  // descending order, go to the workspace
+  // entry, 0 if the set is empty); of these maxima, the one of rank m - 1
+  // (descending, ties to the smaller set) goes to the workspace when the
+  // chunk is full (every set nonempty: only full chunks are read), m =
+  // ceil(k / #full chunks) as the compaction uses it.  Ranks are counted in
+  // parallel, one set per thread.
   __shared__ uint32_t s_max[kLSets];
   for (int r = tid; r < kLSets; r += kIdxThreads) {
     uint32_t mx = 0u;
@@ -1169,19 +1172,17 @@ __global__ __launch_bounds__(kIdxThreads) void idx_long_score_kernel(IdxArgs a) 
     s_max[r] = mx;
   }
   __syncthreads();
-  if (tid < kWave) {
-    const int lane = tid;
-    uint32_t v0 = s_max[lane], v1 = s_max[lane + kWave];
-    for (int j = 0; j < kLTop; ++j) {
-      const uint32_t mx = wave_total<1>(v0 > v1 ? v0 : v1);
-      // remove one occurrence of mx
-      const uint64_t b0 = __ballot(v0 == mx), b1 = __ballot(v1 == mx);
-      if (b0 != 0ull) {
-        if (lane == __ffsll((unsigned long long)b0) - 1) v0 = 0u;
-      } else if (lane == __ffsll((unsigned long long)b1) - 1) {
-        v1 = 0u;
+  const int64_t nfull = nt >= kLSets ? (nt - kLSets) / kLChunk + 1 : 0;
+  if (cn >= kLSets && nfull > 0) {
+    const int64_t mm = ((int64_t)a.k + nfull - 1) / nfull;
+    if (mm <= kLSets && tid < kLSets) {
+      const uint32_t my = s_max[tid];
+      int rank = 0;
+      for (int r = 0; r < kLSets; ++r) {
+        const uint32_t v = s_max[r];
+        rank += (v > my || (v == my && r < tid)) ? 1 : 0;
       }
-      if (lane == 0) uni[j] = mx;
+      if (rank == (int)mm - 1) *uni = my;
     }
   }
 }
@@ -1208,16 +1209,19 @@ __global__ __launch_bounds__(kIdxThreads) void idx_long_compact_kernel(IdxArgs a
   // those (every entry when no such m exists)
   const int64_t nfull = nt >= kLSets ? (nt - kLSets) / kLChunk + 1 : 0;
   uint32_t T = 0u;
-  if (nfull > 0) {
-    const int64_t mm = ((int64_t)a.k + nfull - 1) / nfull;
-    if (mm <= kLTop) {
-      const uint32_t* uni = (const uint32_t*)(wq + a.off_uni);
-      T = 0xffffffffu;
-      for (int64_t c = 0; c < nfull; ++c) {
-        const uint32_t v = uni[c * a.lm + mm - 1];
-        T = v < T ? v : T;
-      }
+  if (nfull > 0 && ((int64_t)a.k + nfull - 1) / nfull <= kLSets) {   // uniform
+    // one load per thread (all in flight together), then a workgroup minimum
+    const uint32_t* uni = (const uint32_t*)(wq + a.off_uni);
+    uint32_t t = 0xffffffffu;
+    for (int64_t c = tid; c < nfull; c += kIdxThreads) {
+      const uint32_t v = uni[c];
+      t = v < t ? v : t;
     }
+    t = wave_total<2>(t);
+    if (lane == 0) sh.wtot[1][wave] = t;
+    __syncthreads();
+    T = 0xffffffffu;
+    for (int w = 0; w < kIdxWaves; ++w) T = sh.wtot[1][w] < T ? sh.wtot[1][w] : T;
   }
   // compaction in index order: wave w owns the contiguous range
   // [w * kLPerWave, +kLPerWave) of the segment; its scores are loaded once,
@@ -1257,6 +1261,7 @@ constexpr int kLFinalLds = 8192;
 
 __global__ __launch_bounds__(kIdxThreads) void idx_long_final_kernel(IdxArgs a) {
   __shared__ uint32_t s_cand[kLFinalLds];
+  __shared__ int32_t s_cidx[kLFinalLds];
   __shared__ SelShared sh;
   __shared__ uint32_t s_pre[kIdxThreads + 1];
   const int tid = threadIdx.x;
@@ -1270,9 +1275,9 @@ __global__ __launch_bounds__(kIdxThreads) void idx_long_final_kernel(IdxArgs a) 
   uint8_t* wq = a.ws + bq * a.per_query;
   const uint32_t* counts = (const uint32_t*)(wq + a.off_counts);
   const uint2* region = (const uint2*)(wq + a.off_region);
-  uint32_t* skey = (uint32_t*)(wq + a.off_skey);
-  int32_t* sidx = (int32_t*)(wq + a.off_sidx);
-  // segment offsets in the concatenated candidate list (nseg <= kIdxThreads)
+  // segment offsets in the concatenated candidate list (nseg <= kIdxThreads;
+  // s_pre[s] for every s <= kIdxThreads, so that segment s holds s_pre[s+1]
+  // - s_pre[s] candidates)
   const int lane = tid % kWave, wave = tid / kWave;
   const uint32_t cnt_mine = tid < a.nseg ? counts[tid] : 0u;
   const uint32_t incl = wave_scan<0>(cnt_mine);
@@ -1280,11 +1285,37 @@ __global__ __launch_bounds__(kIdxThreads) void idx_long_final_kernel(IdxArgs a) 
   __syncthreads();
   uint32_t wbase = 0;
   for (int w = 0; w < wave; ++w) wbase += sh.wtot[0][w];
-  if (tid < a.nseg) s_pre[tid] = wbase + incl - cnt_mine;
+  s_pre[tid] = wbase + incl - cnt_mine;
   if (tid == kIdxThreads - 1) s_pre[kIdxThreads] = wbase + incl;
   __syncthreads();
+  const int ncand = (int)s_pre[kIdxThreads];
+  const int kk = ncand < a.k ? ncand : a.k;
+  for (int i = kk + tid; i < a.k; i += kIdxThreads) out[i] = -1;
+  if (kk == 0) return;
+  uint32_t thr;
+  int need_eq;
+  if (ncand <= kLFinalLds) {
+    // the usual case (about k candidates): straight from the segment
+    // regions into LDS, 32 threads per segment, every load in flight together
+    for (int sg = tid >> 5; sg < a.nseg; sg += kIdxThreads >> 5) {
+      const uint32_t off = s_pre[sg], cnt = s_pre[sg + 1] - off;
+      const uint2* rg = region + (int64_t)sg * kLSeg;
+      for (uint32_t j = tid & 31; j < cnt; j += 32) {
+        const uint2 v = rg[j];
+        s_cand[off + j] = v.x;
+        s_cidx[off + j] = (int32_t)v.y;
+      }
+    }
+    __syncthreads();
+    radix_select(s_cand, ncand, kk, sh, thr, need_eq);
+    emit_selected(s_cand, ncand, thr, need_eq, sh, [&](int pos, int rank) { out[rank] = s_cidx[pos]; });
+    return;
+  }
+  // many candidates (heavy ties): concatenated in the workspace
+  uint32_t* skey = (uint32_t*)(wq + a.off_skey);
+  int32_t* sidx = (int32_t*)(wq + a.off_sidx);
   for (int sg = 0; sg < a.nseg; ++sg) {
-    const uint32_t cnt = counts[sg], off = s_pre[sg];
+    const uint32_t off = s_pre[sg], cnt = s_pre[sg + 1] - off;
     const uint2* rg = region + (int64_t)sg * kLSeg;
     for (uint32_t j = tid; j < cnt; j += kIdxThreads) {
       const uint2 v = rg[j];
@@ -1293,21 +1324,8 @@ __global__ __launch_bounds__(kIdxThreads) void idx_long_final_kernel(IdxArgs a) 
     }
   }
   __syncthreads();
-  const int ncand = (int)s_pre[kIdxThreads];
-  const int kk = ncand < a.k ? ncand : a.k;
-  for (int i = kk + tid; i < a.k; i += kIdxThreads) out[i] = -1;
-  if (kk == 0) return;
-  // select from an LDS copy when the candidates fit (the usual case: about k)
-  const uint32_t* keys = skey;
-  if (ncand <= kLFinalLds) {
-    for (int i = tid; i < ncand; i += kIdxThreads) s_cand[i] = skey[i];
-    __syncthreads();
-    keys = s_cand;
-  }
-  uint32_t thr;
-  int need_eq;
-  radix_select(keys, ncand, kk, sh, thr, need_eq);
-  emit_selected(keys, ncand, thr, need_eq, sh, [&](int pos, int rank) { out[rank] = sidx[pos]; });
+  radix_select(skey, ncand, kk, sh, thr, need_eq);
+  emit_selected(skey, ncand, thr, need_eq, sh, [&](int pos, int rank) { out[rank] = sidx[pos]; });
 }
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -1320,7 +1338,7 @@ IdxPlan indexer_plan(int B, int Tq, int64_t n_entries, int k) {
     // long lists: score / compact / final select
     p.mode = 1;
     p.nchunk = (int)((n_entries + kLChunk - 1) / kLChunk);
-    p.lm = kLTop;
+    p.lm = 1;
     p.nseg = (int)((n_entries + kLSeg - 1) / kLSeg);
     if (p.nseg > kIdxThreads) return p;                          // up to 8M entries per query
     const size_t npad = align256((size_t)p.nseg * kLSeg);
