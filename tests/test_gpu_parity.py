@@ -371,6 +371,55 @@ def test_hca_decode_parity(lib):
         Hx.check_attn(got[b], want)
 
 
+def test_decode_step_graph_replays_match_eager(lib):
+    """A decode step (indexer top-k over a long list, sparse attention with
+    split merge, HCA attention over a ring window) captured in one HIP graph:
+    every replay, with other work and synchronisations between replays,
+    equals the eager step bit for bit (the kernels are deterministic and the
+    library neither allocates, synchronises nor clears memory inside a call)."""
+    import torch
+    B, H, D, R, N, k, W, m, H_I, d_I = 4, 128, 512, 64, 20000, 1024, 128, 4, 8, 64
+    Nh = m * N // 128
+    qd, _, cst, _, rst, _, sink = _decode_setup(B, H, D, R, N, W, 4)
+    kst, _, qst, _, w = _indexer_inputs(B, 1, N, H_I, d_I, "fp8", seed_shift=6)
+    dev = Hx.dev()
+    pos = Hx.to_dev(np.array([m * N - 3 * b for b in range(B)], np.int64))
+    wt, sinkt = Hx.to_dev(w), Hx.to_dev(sink)
+    sel = torch.empty((B, 1, k), dtype=torch.int32, device=dev)
+    out = torch.empty(qd.shape, dtype=torch.bfloat16, device=dev)
+    out_h = torch.empty((B, 1, H, D), dtype=torch.bfloat16, device=dev)
+    iws = torch.empty(max(lib.indexer_topk_workspace(B, 1, N, k), 16), dtype=torch.uint8, device=dev)
+    aws = torch.empty(max(lib.attn_workspace(B, 1, H, D, k + W), 16), dtype=torch.uint8, device=dev)
+    hws = torch.empty(max(lib.attn_workspace(B, 1, H, D, Nh + W), 16), dtype=torch.uint8, device=dev)
+    tau = 1.0 / math.sqrt(D)
+
+    def step():
+        lib.indexer_topk(qst, wt, kst, N, pos, B, 1, H_I, m, k, sel, iws)
+        lib.sparse_attn_decode(qd, cst, N, sel, k, rst, pos, W, sinkt, tau, out, ws=aws)
+        lib.hca_attn(qd[:, None], cst, 128, Nh, pos[:, None], rst, W, sinkt, tau, out_h, flags=lib.WIN_RING, ws=hws)
+
+    step()
+    _sync()
+    ref = (sel.clone(), out.clone(), out_h.clone())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    _sync()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(3):
+        sel.fill_(-9)
+        out.zero_()
+        out_h.zero_()
+        _sync()
+        g.replay()
+        _sync()
+        assert torch.equal(sel, ref[0]) and torch.equal(out, ref[1]) and torch.equal(out_h, ref[2]), f"replay {r}"
+
+
 def test_partial_then_swa_merge_equals_fused(lib):
     import torch
     T, H, D, R, m, k, W = 400, 64, 512, 64, 4, 64, 128
