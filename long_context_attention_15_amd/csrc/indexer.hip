@@ -230,8 +230,8 @@ struct IdxArgs {
   int32_t* ws_idx;
   // long lists: per-query workspace block and the offsets inside it
   uint8_t* ws;
-  size_t per_query, off_scores, off_uni, off_region, off_counts, off_skey, off_sidx;
-  int lm, nseg;
+  size_t per_query, off_scores, off_uni, off_region, off_counts, off_skey, off_sidx, off_ctr;
+  int lm, nseg, rstride;   // rstride: entries between consecutive candidate regions
 };
 
 // visible entries of query bq
@@ -1119,7 +1119,11 @@ static hipError_t launch_idx_stream(const IdxArgs& ia, hipStream_t st) {
 //
 // Few queries over many entries (decode at long context).  Three kernels,
 // exact, reading each key once at full HBM rate:
-//   A  chunks of kLChunk entries: the keys of the chunk's scores go to the
+//   A  chunks of a.chunk entries (sized at plan time, between kLChunkMin
+//      and kLChunkMax, so that the (query, chunk) workgroups fill whole
+//      rounds of the resident workgroup slots: a partial last round leaves
+//      much of the chip idle while it streams):
+//      the keys of the chunk's scores go to the
 //      workspace, and so does the m-th largest of the maxima of kLSets
 //      strided subsets of the chunk (each maximum is a real entry), m =
 //      ceil(k / #chunks whose subsets are all nonempty);
@@ -1133,10 +1137,15 @@ static hipError_t launch_idx_stream(const IdxArgs& ia, hipStream_t st) {
 //   C  per query: the regions, concatenated in segment order (= index
 //      order), hold every candidate; the exact top-k (ties to the smaller
 //      index) is selected from them and emitted in ascending index order.
-constexpr int kLChunk = 8192;
+// When a query has at most kLFusedMaxChunks chunks, A and B run as one pass
+// (idx_long_fused_kernel below) and the scores never leave LDS.
+constexpr int kLChunkMin = 8192;             // smaller chunks only add per-chunk overhead
+constexpr int kLChunkMax = 12288;            // LDS keys per workgroup (3 resident per CU)
+constexpr int kLWgPerCu = 3;                  // resident score workgroups per CU (their registers allow 3)
 constexpr int kLSeg = 16384;
 constexpr int kLPerWave = kLSeg / kIdxWaves;  // segment entries per wave in the compaction
 constexpr int kLSets = 128;                   // strided sets per chunk
+constexpr int kLFusedMaxChunks = 128;         // one-pass path: at most this many chunks per query
 
 template <int FMT, int DI>
 __global__ __launch_bounds__(kIdxThreads) void idx_long_score_kernel(IdxArgs a) {
@@ -1149,9 +1158,9 @@ __global__ __launch_bounds__(kIdxThreads) void idx_long_score_kernel(IdxArgs a) 
   const int b = (int)(bq / a.Tq), q = (int)(bq % a.Tq);
   const int c = blockIdx.y;
   const int64_t nt = idx_visible(a, bq);
-  const int64_t c0 = (int64_t)c * kLChunk;
+  const int64_t c0 = (int64_t)c * a.chunk;
   const int64_t cn64 = nt - c0;
-  const int cn = cn64 < 0 ? 0 : (cn64 > kLChunk ? kLChunk : (int)cn64);
+  const int cn = cn64 < 0 ? 0 : (cn64 > a.chunk ? a.chunk : (int)cn64);
   uint8_t* wq = a.ws + bq * a.per_query;
   uint32_t* scores = (uint32_t*)(wq + a.off_scores);
   uint32_t* uni = (uint32_t*)(wq + a.off_uni) + c;
@@ -1172,7 +1181,7 @@ __global__ __launch_bounds__(kIdxThreads) void idx_long_score_kernel(IdxArgs a) 
     s_max[r] = mx;
   }
   __syncthreads();
-  const int64_t nfull = nt >= kLSets ? (nt - kLSets) / kLChunk + 1 : 0;
+  const int64_t nfull = nt >= kLSets ? (nt - kLSets) / a.chunk + 1 : 0;
   if (cn >= kLSets && nfull > 0) {
     const int64_t mm = ((int64_t)a.k + nfull - 1) / nfull;
     if (mm <= kLSets && tid < kLSets) {
@@ -1207,7 +1216,7 @@ __global__ __launch_bounds__(kIdxThreads) void idx_long_compact_kernel(IdxArgs a
   // m = ceil(k / #full), each full chunk holds at least m entries >= its
   // m-th largest set maximum, so at least k entries are >= the smallest of
   // those (every entry when no such m exists)
-  const int64_t nfull = nt >= kLSets ? (nt - kLSets) / kLChunk + 1 : 0;
+  const int64_t nfull = nt >= kLSets ? (nt - kLSets) / a.chunk + 1 : 0;
   uint32_t T = 0u;
   if (nfull > 0 && ((int64_t)a.k + nfull - 1) / nfull <= kLSets) {   // uniform
     // one load per thread (all in flight together), then a workgroup minimum
@@ -1257,6 +1266,130 @@ __global__ __launch_bounds__(kIdxThreads) void idx_long_compact_kernel(IdxArgs a
   if (wave == kIdxWaves - 1 && lane == 0) counts[seg] = base;
 }
 
+// One-pass variant of A + B: the chunk's keys stay in LDS.  The workgroups of
+// a query meet at an arrival counter in the workspace (zeroed by
+// idx_long_zero_kernel): each nonempty chunk publishes its m-th largest set
+// maximum, arrives once, and waits until every nonempty chunk of its query
+// has arrived; then T is formed as in B and the chunk compacts its own keys
+// >= T, in index order, into its region (regions one chunk apart).  The grid
+// puts the chunks of a query next to each other in dispatch order, and a
+// query has far fewer chunks than the chip has resident slots, so the wait
+// ends once the query's last chunk is scored.  The wait is bounded: a
+// workgroup that gives up takes T = 0 (all its keys become candidates),
+// which keeps the selection exact, only slower.
+constexpr int kLSpinMax = 1 << 16;   // polls of the arrival counter (tens of milliseconds)
+
+__global__ __launch_bounds__(256) void idx_long_zero_kernel(IdxArgs a, int64_t nq) {
+  const int64_t bq = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (bq < nq) *(uint32_t*)(a.ws + bq * a.per_query + a.off_ctr) = 0u;
+}
+
+template <int FMT, int DI>
+__global__ __launch_bounds__(kIdxThreads) void idx_long_fused_kernel(IdxArgs a) {
+  extern __shared__ uint32_t s_keys[];
+  __shared__ float s_q[kMaxHI * kMaxDI];
+  __shared__ float s_w[kMaxHI];
+  __shared__ uint32_t s_max[kLSets];
+  __shared__ uint32_t s_wt[kIdxWaves];
+  __shared__ uint32_t s_ok;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int c = blockIdx.x;
+  const int64_t bq = blockIdx.y;
+  const int b = (int)(bq / a.Tq), q = (int)(bq % a.Tq);
+  const int64_t nt = idx_visible(a, bq);
+  if (nt <= a.k) return;                        // uniform per query: no candidates needed
+  const int64_t c0 = (int64_t)c * a.chunk;
+  const int64_t cn64 = nt - c0;
+  const int cn = cn64 < 0 ? 0 : (cn64 > a.chunk ? a.chunk : (int)cn64);
+  uint8_t* wq = a.ws + bq * a.per_query;
+  uint32_t* uni = (uint32_t*)(wq + a.off_uni);
+  uint32_t* counts = (uint32_t*)(wq + a.off_counts);
+  uint32_t* ctr = (uint32_t*)(wq + a.off_ctr);
+  if (cn == 0) {                                // uniform; never waited for
+    if (tid == 0) counts[c] = 0u;
+    return;
+  }
+  score_chunk<FMT, DI>(a, b, q, bq, c0, cn, s_keys, s_q, s_w);
+  __syncthreads();
+  // the chunk's m-th largest strided-set maximum, as in A
+  for (int r = tid; r < kLSets; r += kIdxThreads) {
+    uint32_t mx = 0u;
+    for (int e = r; e < cn; e += kLSets) mx = s_keys[e] > mx ? s_keys[e] : mx;
+    s_max[r] = mx;
+  }
+  __syncthreads();
+  const int64_t nfull = nt >= kLSets ? (nt - kLSets) / a.chunk + 1 : 0;
+  const bool use_t = nfull > 0 && ((int64_t)a.k + nfull - 1) / nfull <= kLSets;   // uniform
+  if (cn >= kLSets && use_t && tid < kLSets) {
+    const int64_t mm = ((int64_t)a.k + nfull - 1) / nfull;
+    const uint32_t my = s_max[tid];
+    int rank = 0;
+    for (int r = 0; r < kLSets; ++r) {
+      const uint32_t v = s_max[r];
+      rank += (v > my || (v == my && r < tid)) ? 1 : 0;
+    }
+    if (rank == (int)mm - 1) {
+      const uint32_t old = __hip_atomic_exchange(uni + c, my, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      asm volatile("" ::"v"(old));              // a returning atomic: performed before the barrier
+    }
+  }
+  // arrive, then wait for the query's other nonempty chunks.  Publication,
+  // arrival, polling and the reads of the published statistics are all
+  // returning device-scope atomics, each performed before the next is
+  // issued: no cache write-back or invalidation is needed (those would stall
+  // the workgroups still streaming keys).
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t nact = (uint32_t)((nt + a.chunk - 1) / a.chunk);
+    uint32_t seen = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+    for (int it = 0; seen < nact && it < kLSpinMax; ++it) {
+      __builtin_amdgcn_s_sleep(16);
+      seen = __hip_atomic_fetch_add(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    s_ok = seen >= nact ? 1u : 0u;
+  }
+  __syncthreads();
+  uint32_t T = 0u;
+  if (use_t && s_ok) {                          // uniform
+    uint32_t t = 0xffffffffu;
+    for (int64_t j = tid; j < nfull; j += kIdxThreads) {
+      const uint32_t v = __hip_atomic_fetch_add(uni + j, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      t = v < t ? v : t;
+    }
+    t = wave_total<2>(t);
+    if (lane == 0) s_wt[wave] = t;
+    __syncthreads();
+    T = 0xffffffffu;
+    for (int w = 0; w < kIdxWaves; ++w) T = s_wt[w] < T ? s_wt[w] : T;
+    __syncthreads();
+  }
+  // compaction in index order: wave w owns [w * per, (w + 1) * per) of the
+  // chunk, counted in a first pass and written in a second
+  const int per = (cn + kIdxThreads - 1) / kIdxThreads * kWave;
+  const int p0 = wave * per;
+  const int p1 = p0 + per < cn ? p0 + per : cn;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  uint32_t n_mine = 0;
+  for (int p = p0; p < p1; p += kWave) {
+    const int pos = p + lane;
+    n_mine += (uint32_t)__popcll(__ballot(pos < p1 && s_keys[pos] >= T));
+  }
+  if (lane == 0) s_wt[wave] = n_mine;
+  __syncthreads();
+  uint32_t base = 0;
+  for (int w = 0; w < wave; ++w) base += s_wt[w];
+  uint2* region = (uint2*)(wq + a.off_region) + c0;
+  for (int p = p0; p < p1; p += kWave) {
+    const int pos = p + lane;
+    const uint32_t key = pos < p1 ? s_keys[pos] : 0u;
+    const bool take = pos < p1 && key >= T;
+    const uint64_t bt = __ballot(take);
+    if (take) region[base + __popcll(bt & lt)] = make_uint2(key, (uint32_t)(c0 + pos));
+    base += (uint32_t)__popcll(bt);
+  }
+  if (wave == kIdxWaves - 1 && lane == 0) counts[c] = base;
+}
+
 constexpr int kLFinalLds = 8192;
 
 __global__ __launch_bounds__(kIdxThreads) void idx_long_final_kernel(IdxArgs a) {
@@ -1299,7 +1432,7 @@ __global__ __launch_bounds__(kIdxThreads) void idx_long_final_kernel(IdxArgs a) 
     // regions into LDS, 32 threads per segment, every load in flight together
     for (int sg = tid >> 5; sg < a.nseg; sg += kIdxThreads >> 5) {
       const uint32_t off = s_pre[sg], cnt = s_pre[sg + 1] - off;
-      const uint2* rg = region + (int64_t)sg * kLSeg;
+      const uint2* rg = region + (int64_t)sg * a.rstride;
       for (uint32_t j = tid & 31; j < cnt; j += 32) {
         const uint2 v = rg[j];
         s_cand[off + j] = v.x;
@@ -1316,7 +1449,7 @@ __global__ __launch_bounds__(kIdxThreads) void idx_long_final_kernel(IdxArgs a) 
   int32_t* sidx = (int32_t*)(wq + a.off_sidx);
   for (int sg = 0; sg < a.nseg; ++sg) {
     const uint32_t off = s_pre[sg], cnt = s_pre[sg + 1] - off;
-    const uint2* rg = region + (int64_t)sg * kLSeg;
+    const uint2* rg = region + (int64_t)sg * a.rstride;
     for (uint32_t j = tid; j < cnt; j += kIdxThreads) {
       const uint2 v = rg[j];
       skey[off + j] = v.x;
@@ -1336,20 +1469,37 @@ IdxPlan indexer_plan(int B, int Tq, int64_t n_entries, int k) {
   if (n_entries <= 0) { p.chunk = 1024; p.nchunk = 1; p.ok = true; return p; }
   if (queries < 256 && n_entries > 8192) {
     // long lists: score / compact / final select
-    p.mode = 1;
-    p.nchunk = (int)((n_entries + kLChunk - 1) / kLChunk);
+    // chunk size: the (query, chunk) workgroups fill whole rounds of the
+    // resident slots (kLWgPerCu per CU), chunks of at most kLChunkMax entries
+    int n_cu = 0, dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu <= 0)
+      n_cu = 256;
+    const int64_t slots = (int64_t)kLWgPerCu * n_cu;
+    int64_t rounds = (queries * n_entries + slots * kLChunkMax - 1) / (slots * kLChunkMax);
+    rounds = rounds < 1 ? 1 : rounds;
+    const int64_t per_q = (slots * rounds + queries - 1) / queries;   // chunks per query
+    int64_t lchunk = (n_entries + per_q - 1) / per_q;
+    lchunk = (lchunk + 63) / 64 * 64;
+    lchunk = lchunk < kLChunkMin ? kLChunkMin : (lchunk > kLChunkMax ? kLChunkMax : lchunk);
+    p.nchunk = (int)((n_entries + lchunk - 1) / lchunk);
     p.lm = 1;
-    p.nseg = (int)((n_entries + kLSeg - 1) / kLSeg);
+    // one pass (mode 2) while a query's chunks are few next to the resident
+    // slots; its candidate regions are the chunks, else the kLSeg segments
+    const bool fused = p.nchunk <= kLFusedMaxChunks;
+    p.mode = fused ? 2 : 1;
+    p.rstride = fused ? (int)lchunk : kLSeg;
+    p.nseg = fused ? p.nchunk : (int)((n_entries + kLSeg - 1) / kLSeg);
     if (p.nseg > kIdxThreads) return p;                          // up to 8M entries per query
-    const size_t npad = align256((size_t)p.nseg * kLSeg);
+    const size_t npad = align256((size_t)p.nseg * p.rstride);
     p.off_scores = 0;
-    p.off_uni = align256(npad * 4);
+    p.off_uni = fused ? 0 : align256(npad * 4);                  // one pass keeps no scores
     p.off_region = p.off_uni + align256((size_t)p.nchunk * p.lm * 4);
     p.off_counts = p.off_region + npad * 8;
-    p.off_skey = p.off_counts + align256((size_t)p.nseg * 4);
+    p.off_ctr = p.off_counts + align256((size_t)p.nseg * 4);
+    p.off_skey = p.off_ctr + 256;
     p.off_sidx = p.off_skey + npad * 4;
     p.per_query = p.off_sidx + npad * 4;
-    p.chunk = kLChunk;
+    p.chunk = (int)lchunk;
     p.ws = (size_t)queries * p.per_query;
     p.ok = true;
     return p;
@@ -1368,10 +1518,22 @@ IdxPlan indexer_plan(int B, int Tq, int64_t n_entries, int k) {
 }
 
 template <int FMT, int DI>
-static hipError_t launch_idx_long(const IdxArgs& a, hipStream_t st) {
+static hipError_t launch_idx_long(const IdxArgs& a, bool fused, hipStream_t st) {
   const unsigned nq = (unsigned)((int64_t)a.B * a.Tq);
+  if (fused) {
+    hipLaunchKernelGGL(idx_long_zero_kernel, dim3((nq + 255) / 256), dim3(256), 0, st, a, (int64_t)nq);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // chunk index fastest: the chunks of a query are dispatched together
+    hipLaunchKernelGGL((idx_long_fused_kernel<FMT, DI>), dim3(a.nchunk, nq), dim3(kIdxThreads),
+                       (size_t)a.chunk * 4, st, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(idx_long_final_kernel, dim3(nq), dim3(kIdxThreads), 0, st, a);
+    return hipGetLastError();
+  }
   auto ka = idx_long_score_kernel<FMT, DI>;
-  hipLaunchKernelGGL(ka, dim3(nq, a.nchunk), dim3(kIdxThreads), kLChunk * 4, st, a);
+  hipLaunchKernelGGL(ka, dim3(nq, a.nchunk), dim3(kIdxThreads), (size_t)a.chunk * 4, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(idx_long_compact_kernel, dim3(nq, a.nseg), dim3(kIdxThreads), 0, st, a);
@@ -1411,7 +1573,8 @@ hipError_t launch_indexer(const csa_store& qidx, const float* head_w, const csa_
   a.ws = (uint8_t*)ws;
   a.per_query = plan.per_query; a.off_scores = plan.off_scores; a.off_uni = plan.off_uni;
   a.off_region = plan.off_region; a.off_counts = plan.off_counts; a.off_skey = plan.off_skey;
-  a.off_sidx = plan.off_sidx; a.lm = plan.lm; a.nseg = plan.nseg;
+  a.off_sidx = plan.off_sidx; a.off_ctr = plan.off_ctr; a.lm = plan.lm; a.nseg = plan.nseg;
+  a.rstride = plan.rstride;
   a.sel = sel;
   const size_t half = plan.ws / 2;
   a.ws_key = (uint32_t*)ws;
@@ -1419,12 +1582,13 @@ hipError_t launch_indexer(const csa_store& qidx, const float* head_w, const csa_
   if ((int64_t)B * Tq == 0) return hipSuccess;
   if (indexer_stream_ok(keys, H_I, B, Tq, n_entries, k)) return launch_idx_stream(a, st);
   const int d = keys.dim;
-  if (plan.mode == 1) {
+  if (plan.mode == 1 || plan.mode == 2) {
+    const bool f = plan.mode == 2;
     switch (keys.fmt) {
-      case CSA_F32: return d == 32 ? launch_idx_long<CSA_F32, 32>(a, st) : launch_idx_long<CSA_F32, 64>(a, st);
+      case CSA_F32: return d == 32 ? launch_idx_long<CSA_F32, 32>(a, f, st) : launch_idx_long<CSA_F32, 64>(a, f, st);
       case CSA_FP8_E4M3:
-        return d == 32 ? launch_idx_long<CSA_FP8_E4M3, 32>(a, st) : launch_idx_long<CSA_FP8_E4M3, 64>(a, st);
-      default: return d == 32 ? launch_idx_long<CSA_MXFP4, 32>(a, st) : launch_idx_long<CSA_MXFP4, 64>(a, st);
+        return d == 32 ? launch_idx_long<CSA_FP8_E4M3, 32>(a, f, st) : launch_idx_long<CSA_FP8_E4M3, 64>(a, f, st);
+      default: return d == 32 ? launch_idx_long<CSA_MXFP4, 32>(a, f, st) : launch_idx_long<CSA_MXFP4, 64>(a, f, st);
     }
   }
   switch (keys.fmt) {

@@ -20,9 +20,11 @@ struct IdxPlan {
   int nchunk;     // chunks per query
   size_t ws;      // workspace bytes
   bool ok;
-  int mode;       // 0: chunk(s) + merge, 1: long lists (score / compact / select)
-  int lm, nseg;   // long lists: union keys per chunk, segments per query
-  size_t per_query, off_scores, off_uni, off_region, off_counts, off_skey, off_sidx;
+  int mode;       // 0: chunk(s) + merge, 1: long lists (score / compact / select),
+                  // 2: long lists (score and compact in one pass / select)
+  int lm, nseg;   // long lists: union keys per chunk, candidate regions per query
+  int rstride;    // long lists: entries between consecutive candidate regions
+  size_t per_query, off_scores, off_uni, off_region, off_counts, off_skey, off_sidx, off_ctr;
 };
 IdxPlan indexer_plan(int B, int Tq, int64_t n_entries, int k);
 // Many queries over FP8 keys of 64 dims: the single-pass streaming top-k,

@@ -211,12 +211,15 @@ def test_indexer_stream_exact_ties(lib, k):
         assert np.array_equal(sel[0, i], want), f"query {i} at {pos[0][i]}"
 
 
-@pytest.mark.parametrize("N,k", [(20000, 512), (50000, 1024)])
+@pytest.mark.parametrize("N,k", [(20000, 512), (50000, 1024), (1100000, 512)])
 def test_indexer_long_list_exact_ties(lib, N, k):
     """Few queries over many entries (the decode path: chunk scores, union
     threshold, compaction, final select) with integer-valued inputs: exact
     scores, massive ties including exact zeros; the sets must equal the
-    oracle's, smaller index first."""
+    oracle's, smaller index first.  The smaller lists take the one-pass
+    score-and-compact path (a few chunks per query); 1.1M entries give more
+    chunks per query than it takes, so the separate score and compaction
+    kernels run."""
     B, Tq, H_I, d_I, m = 2, 3, 8, 64, 4
     rng = np.random.default_rng(13)
     keys = rng.integers(-2, 3, (B, N, d_I)).astype(np.float64)
