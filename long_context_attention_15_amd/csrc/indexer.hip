@@ -538,31 +538,41 @@ __device__ __forceinline__ void score_chunk_fp8_16(const IdxArgs& a, int b, int 
   const float* ksc = (const float*)a.keys.scales;
   const int64_t krow0 = (int64_t)b * a.keys.cap + c0;
   const int ngroups = (cn + 15) / 16;
-  constexpr int U = 8;                          // groups of 16 entries in flight per wave
-  for (int grp0 = wave * U; grp0 < ngroups; grp0 += kIdxWaves * U) {
-    uint4 kv[U];
-    float sk[U];
-    // every load is issued (rows past the chunk read its last row, their
-    // scores are never stored) so that all of them are in flight together
+  // double-buffered: the next batch of U groups of 16 entries is in flight
+  // while the current one is scored (the last batch re-reads the chunk's
+  // last row, so every issue is unconditional and the wait counts stay exact)
+  constexpr int U = 4;
+  uint4 kv[U];
+  float sk[U];
+  auto issue = [&](int g0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      int e = (grp0 + u) * 16 + col;
+      int e = (g0 + u) * 16 + col;
       e = e < cn ? e : cn - 1;
       kv[u] = load_nt16(a.keys.rows + (krow0 + e) * a.keys.row_bytes + 16 * g);
       sk[u] = __builtin_nontemporal_load(ksc + krow0 + e);
     }
+  };
+  int grp0 = wave * U;
+  issue(grp0);
+  for (; grp0 < ngroups; grp0 += kIdxWaves * U) {
+    uint4 cv[U];
+    float cs[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) { cv[u] = kv[u]; cs[u] = sk[u]; }
+    issue(grp0 + kIdxWaves * U);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int e = (grp0 + u) * 16 + col;
       f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
-      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qb0, fp8x8_bf16((long long)(((unsigned long long)kv[u].y << 32) | kv[u].x)), c, 0, 0, 0);
-      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qb1, fp8x8_bf16((long long)(((unsigned long long)kv[u].w << 32) | kv[u].z)), c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qb0, fp8x8_bf16((long long)(((unsigned long long)cv[u].y << 32) | cv[u].x)), c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qb1, fp8x8_bf16((long long)(((unsigned long long)cv[u].w << 32) | cv[u].z)), c, 0, 0, 0);
       float v = 0.0f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) v = fmaf(wl[i], fmaxf(c[i], 0.0f), v);
       const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
       v = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-      if (g == 0 && e < cn) s_keys[e] = score_key(v * sk[u]);
+      if (g == 0 && e < cn) s_keys[e] = score_key(v * cs[u]);
     }
   }
 }
@@ -1119,10 +1129,8 @@ static hipError_t launch_idx_stream(const IdxArgs& ia, hipStream_t st) {
 //
 // Few queries over many entries (decode at long context).  Three kernels,
 // exact, reading each key once at full HBM rate:
-//   A  chunks of a.chunk entries (sized at plan time, between kLChunkMin
-//      and kLChunkMax, so that the (query, chunk) workgroups fill whole
-//      rounds of the resident workgroup slots: a partial last round leaves
-//      much of the chip idle while it streams):
+//   A  chunks of a.chunk = kLChunk entries (of the sizes measured at 262144
+//      entries per query, from 4096 to 16384, this one streamed fastest):
 //      the keys of the chunk's scores go to the
 //      workspace, and so does the m-th largest of the maxima of kLSets
 //      strided subsets of the chunk (each maximum is a real entry), m =
@@ -1139,9 +1147,7 @@ static hipError_t launch_idx_stream(const IdxArgs& ia, hipStream_t st) {
 //      index) is selected from them and emitted in ascending index order.
 // When a query has at most kLFusedMaxChunks chunks, A and B run as one pass
 // (idx_long_fused_kernel below) and the scores never leave LDS.
-constexpr int kLChunkMin = 8192;             // smaller chunks only add per-chunk overhead
-constexpr int kLChunkMax = 12288;            // LDS keys per workgroup (3 resident per CU)
-constexpr int kLWgPerCu = 3;                  // resident score workgroups per CU (their registers allow 3)
+constexpr int kLChunk = 8192;                 // entries per chunk (32 KiB of keys in LDS, 3 workgroups per CU)
 constexpr int kLSeg = 16384;
 constexpr int kLPerWave = kLSeg / kIdxWaves;  // segment entries per wave in the compaction
 constexpr int kLSets = 128;                   // strided sets per chunk
@@ -1469,18 +1475,7 @@ IdxPlan indexer_plan(int B, int Tq, int64_t n_entries, int k) {
   if (n_entries <= 0) { p.chunk = 1024; p.nchunk = 1; p.ok = true; return p; }
   if (queries < 256 && n_entries > 8192) {
     // long lists: score / compact / final select
-    // chunk size: the (query, chunk) workgroups fill whole rounds of the
-    // resident slots (kLWgPerCu per CU), chunks of at most kLChunkMax entries
-    int n_cu = 0, dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu <= 0)
-      n_cu = 256;
-    const int64_t slots = (int64_t)kLWgPerCu * n_cu;
-    int64_t rounds = (queries * n_entries + slots * kLChunkMax - 1) / (slots * kLChunkMax);
-    rounds = rounds < 1 ? 1 : rounds;
-    const int64_t per_q = (slots * rounds + queries - 1) / queries;   // chunks per query
-    int64_t lchunk = (n_entries + per_q - 1) / per_q;
-    lchunk = (lchunk + 63) / 64 * 64;
-    lchunk = lchunk < kLChunkMin ? kLChunkMin : (lchunk > kLChunkMax ? kLChunkMax : lchunk);
+    const int64_t lchunk = kLChunk;
     p.nchunk = (int)((n_entries + lchunk - 1) / lchunk);
     p.lm = 1;
     // one pass (mode 2) while a query's chunks are few next to the resident
