@@ -167,6 +167,134 @@ __global__ __launch_bounds__(kWave * kCompressWaves) void compress_kernel(
   }
 }
 
+// Blocks of one token (m = 1): the softmax weight of a single logit is
+// exactly 1, so the entry is the token row itself and only the quantisation
+// remains.  Rows are packed LPR lanes to a row, 8 contiguous values per lane
+// (one 16-byte load of BF16), 64 / LPR rows per wavefront; the row maxima are
+// reductions over the row's lane group.  Codes and scales are the ones the
+// general kernel stores for m = 1.
+template <typename TIn>
+__device__ __forceinline__ void load8(const TIn* p, float (&v)[8]);
+template <>
+__device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float (&v)[8]) { load_vals<uint16_t, 8>(p, v); }
+template <>
+__device__ __forceinline__ void load8<float>(const float* p, float (&v)[8]) { load_vals<float, 8>(p, v); }
+
+template <typename TIn, int LPR>
+__global__ __launch_bounds__(kWave * kCompressWaves) void quant_rows_kernel(
+    const TIn* __restrict__ tok, int B, int64_t bstride, StoreW out, int64_t row0, int64_t N) {
+  constexpr int RPW = kWave / LPR;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int li = lane % LPR;
+  int64_t e = ((int64_t)blockIdx.x * kCompressWaves + wave) * RPW + lane / LPR;
+  // lanes of rows past the end compute on row 0 (they take part in the
+  // group reductions) and store nothing
+  const bool valid = e < (int64_t)B * N;
+  if (!valid) e = 0;
+  const int b = (int)(e / N);
+  const int64_t j = e % N;
+  constexpr int D = LPR * 8;
+  const int d0 = li * 8;
+  float x[8];
+  load8<TIn>(tok + (int64_t)b * bstride + j * D + d0, x);
+  const int64_t row = (int64_t)b * out.cap + row0 + j;
+  uint8_t* dst = out.rows + row * out.row_bytes;
+  if (out.fmt == CSA_F32) {
+    if (valid) {
+      float4* o = (float4*)((float*)dst + d0);
+      o[0] = make_float4(x[0], x[1], x[2], x[3]);
+      o[1] = make_float4(x[4], x[5], x[6], x[7]);
+    }
+  } else if (out.fmt == CSA_FP8_E4M3) {
+    const int nb = D - out.rope;                // bulk dims; the rest is the BF16 tail
+    float am = 0.0f;
+#pragma unroll
+    for (int v = 0; v < 8; ++v)
+      if (d0 + v < nb) am = fmaxf(am, fabsf(x[v]));
+    am = wave_max<LPR>(am);
+    const float s = fp8_row_scale(am);
+    const int es = ilogbf(s);
+    if (valid) {
+      if (d0 + 8 <= nb) {
+        uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          lo |= f32_to_e4m3(ldexpf(x[v], -es)) << (8 * v);
+          hi |= f32_to_e4m3(ldexpf(x[v + 4], -es)) << (8 * v);
+        }
+        *(uint2*)(dst + d0) = make_uint2(lo, hi);
+      } else if (d0 >= nb) {
+        uint32_t w[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) w[v] = f32_to_bf16(x[2 * v]) | (f32_to_bf16(x[2 * v + 1]) << 16);
+        *(uint4*)(dst + nb + 2 * (d0 - nb)) = make_uint4(w[0], w[1], w[2], w[3]);
+      } else {
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          const int d = d0 + v;
+          if (d < nb) dst[d] = (uint8_t)f32_to_e4m3(ldexpf(x[v], -es));
+          else ((uint16_t*)(dst + nb))[d - nb] = (uint16_t)f32_to_bf16(x[v]);
+        }
+      }
+      if (li == 0) ((float*)out.scales)[row] = s;
+    }
+  } else {  // CSA_MXFP4, D in {32, 64}: blocks of 32 values = 4 lanes
+    float am = 0.0f;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) am = fmaxf(am, fabsf(x[v]));
+    am = wave_max<4>(am);
+    const int E = mx_block_exp(am);
+    uint32_t pk = 0u;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) pk |= f32_to_e2m1(ldexpf(x[v], -E)) << (4 * v);
+    if (valid) {
+      *(uint32_t*)(dst + d0 / 2) = pk;
+      if ((li & 3) == 0) ((uint8_t*)out.scales)[row * (D / 32) + li / 4] = (uint8_t)(E + 127);
+    }
+  }
+}
+
+template <typename TIn, int LPR>
+static hipError_t launch_quant_t(const void* tok, int B, int64_t T, int64_t bstride, const csa_store& out,
+                                 int64_t row0, hipStream_t st) {
+  const int64_t items = (int64_t)B * T;
+  if (items == 0) return hipSuccess;
+  constexpr int rows_per_block = kCompressWaves * (kWave / LPR);
+  const int64_t blocks = (items + rows_per_block - 1) / rows_per_block;
+  hipLaunchKernelGGL((quant_rows_kernel<TIn, LPR>), dim3((unsigned)blocks), dim3(kWave * kCompressWaves), 0, st,
+                     (const TIn*)tok, B, bstride, wview(out), row0, T);
+  return hipGetLastError();
+}
+
+template <typename TIn>
+static hipError_t launch_quant(const void* tok, int B, int64_t T, int64_t bstride, const csa_store& out,
+                               int64_t row0, hipStream_t st) {
+  switch (out.dim / 8) {
+    case 4: return launch_quant_t<TIn, 4>(tok, B, T, bstride, out, row0, st);
+    case 8: return launch_quant_t<TIn, 8>(tok, B, T, bstride, out, row0, st);
+    case 16: return launch_quant_t<TIn, 16>(tok, B, T, bstride, out, row0, st);
+    case 32: return launch_quant_t<TIn, 32>(tok, B, T, bstride, out, row0, st);
+    default: return launch_quant_t<TIn, 64>(tok, B, T, bstride, out, row0, st);
+  }
+}
+
+// What the m = 1 path assumes: 8 | dim with a power-of-two lane group of 4
+// to 64 lanes, 16-byte aligned token rows and batch stride, 16-byte aligned
+// store rows, an FP8 bulk that ends on a 16-byte boundary, MXFP4 rows of 32
+// or 64 values.  Every store the entry point accepts meets it (dims 32 to
+// 512); the check keeps the kernel's assumptions next to it.
+static bool quant_rows_ok(const void* tok, int tok_fmt, int64_t bstride, const csa_store& out) {
+  const int D = out.dim, lpr = D / 8;
+  if (D % 8 != 0 || lpr < 4 || lpr > 64 || (lpr & (lpr - 1)) != 0) return false;
+  if (out.fmt == CSA_MXFP4 && (D > 64 || out.rope_dim != 0)) return false;
+  const int esz = tok_fmt == CSA_F32 ? 4 : 2;
+  if ((uintptr_t)tok % 16 != 0 || (bstride * esz) % 16 != 0) return false;
+  if ((uintptr_t)out.rows % 16 != 0) return false;
+  if (out.fmt != CSA_MXFP4 && out.row_bytes % 16 != 0) return false;
+  if (out.fmt == CSA_FP8_E4M3 && (D - out.rope_dim) % 16 != 0) return false;
+  return true;
+}
+
 template <typename TIn, int VPL>
 static hipError_t launch_compress_t(const void* tok, int B, int64_t T, int64_t bstride, int m,
                                     const float* gate, const float* bias, const csa_store& out,
@@ -183,6 +311,9 @@ static hipError_t launch_compress_t(const void* tok, int B, int64_t T, int64_t b
 hipError_t launch_compress(const void* tok, int tok_fmt, int B, int64_t T, int64_t bstride, int m,
                            const float* gate, const float* bias, const csa_store& out, int64_t row0,
                            hipStream_t st) {
+  if (m == 1 && quant_rows_ok(tok, tok_fmt, bstride, out))
+    return tok_fmt == CSA_F32 ? launch_quant<float>(tok, B, T, bstride, out, row0, st)
+                              : launch_quant<uint16_t>(tok, B, T, bstride, out, row0, st);
   const int vpl = out.dim >= 64 ? out.dim / 64 : 1;
 #define CSA_CMP(TT, V) return launch_compress_t<TT, V>(tok, B, T, bstride, m, gate, bias, out, row0, st)
   if (tok_fmt == CSA_F32) {

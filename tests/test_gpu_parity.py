@@ -57,10 +57,13 @@ def test_compress_parity(lib, name, tf, sf, D, R, m, T, B):
 
 
 @pytest.mark.parametrize("tf,sf,D,R", [("bf16", "fp8", 512, 64), ("f32", "fp8", 64, 16), ("bf16", "fp8", 64, 0),
-                                       ("bf16", "mxfp4", 64, 0), ("f32", "mxfp4", 32, 0), ("f32", "f32", 64, 0)])
+                                       ("bf16", "mxfp4", 64, 0), ("f32", "mxfp4", 32, 0), ("f32", "f32", 64, 0),
+                                       ("bf16", "fp8", 128, 0), ("f32", "fp8", 256, 64), ("bf16", "f32", 32, 0)])
 def test_compress_m1_quantisation_is_bit_exact(lib, tf, sf, D, R):
     """m = 1 stores the token itself (alpha = 1 exactly), so the stored bytes
-    are the plain quantisation: identical to the oracle codec's."""
+    are the plain quantisation: identical to the oracle codec's.  The rows go
+    through the packed quantise-only kernel at every supported width (4 to 64
+    lanes per row); T = 777 leaves a partly filled last wavefront."""
     T = 777
     x = synth.tensor(0, "kv", (1, T, D), rmsnorm=True) * 3.0
     x[0, 5] = 0.0                       # an all-zero row
