@@ -1152,6 +1152,7 @@ constexpr int kLSeg = 16384;
 constexpr int kLPerWave = kLSeg / kIdxWaves;  // segment entries per wave in the compaction
 constexpr int kLSets = 128;                   // strided sets per chunk
 constexpr int kLFusedMaxChunks = 128;         // one-pass path: at most this many chunks per query
+static_assert(kLFusedMaxChunks <= 2 * kWave, "one wavefront polls the chunk slots, two per lane");
 
 template <int FMT, int DI>
 __global__ __launch_bounds__(kIdxThreads) void idx_long_score_kernel(IdxArgs a) {
@@ -1273,21 +1274,25 @@ __global__ __launch_bounds__(kIdxThreads) void idx_long_compact_kernel(IdxArgs a
 }
 
 // One-pass variant of A + B: the chunk's keys stay in LDS.  The workgroups of
-// a query meet at an arrival counter in the workspace (zeroed by
+// a query meet through per-chunk slots in the workspace (cleared by
 // idx_long_zero_kernel): each nonempty chunk publishes its m-th largest set
-// maximum, arrives once, and waits until every nonempty chunk of its query
-// has arrived; then T is formed as in B and the chunk compacts its own keys
-// >= T, in index order, into its region (regions one chunk apart).  The grid
+// maximum (or "not full") in its slot and waits until every nonempty chunk
+// of its query has published; the smallest statistic is T as B forms it, and
+// the chunk compacts its own keys >= T, in index order, into its region
+// (regions one chunk apart).  The grid
 // puts the chunks of a query next to each other in dispatch order, and a
 // query has far fewer chunks than the chip has resident slots, so the wait
 // ends once the query's last chunk is scored.  The wait is bounded: a
 // workgroup that gives up takes T = 0 (all its keys become candidates),
-// which keeps the selection exact, only slower.
+// which keeps the selection exact, only slower.  kLFusedMaxChunks <= 2 x 64
+// (one polling wavefront, two slots per lane).
 constexpr int kLSpinMax = 1 << 16;   // polls of the arrival counter (tens of milliseconds)
+constexpr int kLParts = kIdxThreads / kLSets;   // threads per strided set in the set maxima
+static_assert(kLParts * kLSets == kIdxThreads && kLSets == 2 * kWave, "set maxima layout");
 
 __global__ __launch_bounds__(256) void idx_long_zero_kernel(IdxArgs a, int64_t nq) {
-  const int64_t bq = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (bq < nq) *(uint32_t*)(a.ws + bq * a.per_query + a.off_ctr) = 0u;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < nq * a.nchunk) ((uint64_t*)(a.ws + (i / a.nchunk) * a.per_query + a.off_ctr))[i % a.nchunk] = 0ull;
 }
 
 template <int FMT, int DI>
@@ -1295,9 +1300,9 @@ __global__ __launch_bounds__(kIdxThreads) void idx_long_fused_kernel(IdxArgs a) 
   extern __shared__ uint32_t s_keys[];
   __shared__ float s_q[kMaxHI * kMaxDI];
   __shared__ float s_w[kMaxHI];
-  __shared__ uint32_t s_max[kLSets];
+  __shared__ uint32_t s_part[kLParts][kLSets];
   __shared__ uint32_t s_wt[kIdxWaves];
-  __shared__ uint32_t s_ok;
+  __shared__ uint32_t s_T;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int c = blockIdx.x;
   const int64_t bq = blockIdx.y;
@@ -1308,67 +1313,81 @@ __global__ __launch_bounds__(kIdxThreads) void idx_long_fused_kernel(IdxArgs a) 
   const int64_t cn64 = nt - c0;
   const int cn = cn64 < 0 ? 0 : (cn64 > a.chunk ? a.chunk : (int)cn64);
   uint8_t* wq = a.ws + bq * a.per_query;
-  uint32_t* uni = (uint32_t*)(wq + a.off_uni);
   uint32_t* counts = (uint32_t*)(wq + a.off_counts);
-  uint32_t* ctr = (uint32_t*)(wq + a.off_ctr);
+  // one slot per chunk: 0 until published, then bit 32 set and the chunk's
+  // statistic (all ones when the chunk is not full) in the low word
+  uint64_t* slots = (uint64_t*)(wq + a.off_ctr);
+  auto publish = [&](uint64_t val) {
+    const uint64_t old = __hip_atomic_exchange(slots + c, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("" ::"v"(old));
+  };
   if (cn == 0) {                                // uniform; never waited for
     if (tid == 0) counts[c] = 0u;
     return;
   }
   score_chunk<FMT, DI>(a, b, q, bq, c0, cn, s_keys, s_q, s_w);
   __syncthreads();
-  // the chunk's m-th largest strided-set maximum, as in A
-  for (int r = tid; r < kLSets; r += kIdxThreads) {
-    uint32_t mx = 0u;
-    for (int e = r; e < cn; e += kLSets) mx = s_keys[e] > mx ? s_keys[e] : mx;
-    s_max[r] = mx;
-  }
-  __syncthreads();
   const int64_t nfull = nt >= kLSets ? (nt - kLSets) / a.chunk + 1 : 0;
   const bool use_t = nfull > 0 && ((int64_t)a.k + nfull - 1) / nfull <= kLSets;   // uniform
-  if (cn >= kLSets && use_t && tid < kLSets) {
-    const int64_t mm = ((int64_t)a.k + nfull - 1) / nfull;
-    const uint32_t my = s_max[tid];
-    int rank = 0;
-    for (int r = 0; r < kLSets; ++r) {
-      const uint32_t v = s_max[r];
-      rank += (v > my || (v == my && r < tid)) ? 1 : 0;
+  if (cn >= kLSets && use_t) {                  // uniform: a full chunk publishes its statistic
+    // the maximum of each strided set {r + kLSets j}: four threads per set,
+    // each over every fourth member, then one wavefront holds the kLSets
+    // maxima (two per lane) and finds the m-th largest by building it bit by
+    // bit from the top: the largest v with #(maxima >= v) >= m
+    {
+      const int r = tid % kLSets, part = tid / kLSets;
+      uint32_t mx = 0u;
+      for (int e = r + part * kLSets; e < cn; e += kIdxThreads) mx = s_keys[e] > mx ? s_keys[e] : mx;
+      s_part[part][r] = mx;
     }
-    if (rank == (int)mm - 1) {
-      const uint32_t old = __hip_atomic_exchange(uni + c, my, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      asm volatile("" ::"v"(old));              // a returning atomic: performed before the barrier
-    }
-  }
-  // arrive, then wait for the query's other nonempty chunks.  Publication,
-  // arrival, polling and the reads of the published statistics are all
-  // returning device-scope atomics, each performed before the next is
-  // issued: no cache write-back or invalidation is needed (those would stall
-  // the workgroups still streaming keys).
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t nact = (uint32_t)((nt + a.chunk - 1) / a.chunk);
-    uint32_t seen = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
-    for (int it = 0; seen < nact && it < kLSpinMax; ++it) {
-      __builtin_amdgcn_s_sleep(16);
-      seen = __hip_atomic_fetch_add(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    s_ok = seen >= nact ? 1u : 0u;
-  }
-  __syncthreads();
-  uint32_t T = 0u;
-  if (use_t && s_ok) {                          // uniform
-    uint32_t t = 0xffffffffu;
-    for (int64_t j = tid; j < nfull; j += kIdxThreads) {
-      const uint32_t v = __hip_atomic_fetch_add(uni + j, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      t = v < t ? v : t;
-    }
-    t = wave_total<2>(t);
-    if (lane == 0) s_wt[wave] = t;
     __syncthreads();
-    T = 0xffffffffu;
-    for (int w = 0; w < kIdxWaves; ++w) T = s_wt[w] < T ? s_wt[w] : T;
-    __syncthreads();
+    if (wave == 0) {
+      uint32_t va = 0u, vb = 0u;
+#pragma unroll
+      for (int part = 0; part < kLParts; ++part) {
+        va = s_part[part][lane] > va ? s_part[part][lane] : va;
+        vb = s_part[part][lane + kWave] > vb ? s_part[part][lane + kWave] : vb;
+      }
+      const int mm = (int)(((int64_t)a.k + nfull - 1) / nfull);
+      uint32_t v = 0u;
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t t = v | (1u << bit);
+        const int cnt = __popcll(__ballot(va >= t)) + __popcll(__ballot(vb >= t));
+        v = cnt >= mm ? t : v;
+      }
+      if (lane == 0) publish(((uint64_t)1 << 32) | v);
+    }
+  } else if (use_t && tid == 0) {
+    publish(((uint64_t)1 << 32) | 0xffffffffu); // a nonempty chunk that is not full: arrived, no statistic
   }
+  // wait for the query's other nonempty chunks: one wavefront polls all
+  // their slots (two per lane) and forms T as the smallest statistic once
+  // every slot is published.  Publication is an atomic exchange and the polls
+  // are device-scope atomic loads, so no cache write-back or invalidation is
+  // needed (those would stall the workgroups still streaming keys).  When T
+  // is 0 anyway (no usable statistic) nothing is waited for.
+  if (use_t && wave == 0) {                     // uniform per workgroup
+    const int nact = (int)((nt + a.chunk - 1) / a.chunk);
+    uint32_t t = 0u;
+    bool all = false;
+    for (int it = 0; !all && it < kLSpinMax; ++it) {
+      const uint64_t s0 = lane < nact ? __hip_atomic_load(slots + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                      : ((uint64_t)1 << 32) | 0xffffffffu;
+      const uint64_t s1 = lane + kWave < nact
+                              ? __hip_atomic_load(slots + lane + kWave, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                              : ((uint64_t)1 << 32) | 0xffffffffu;
+      all = __ballot((s0 >> 32) == 0 || (s1 >> 32) == 0) == 0ull;
+      if (all) {
+        const uint32_t l0 = (uint32_t)s0, l1 = (uint32_t)s1;
+        t = wave_total<2>(l0 < l1 ? l0 : l1);
+      } else {
+        __builtin_amdgcn_s_sleep(16);
+      }
+    }
+    if (lane == 0) s_T = all ? t : 0u;
+  }
+  __syncthreads();
+  const uint32_t T = use_t ? s_T : 0u;
   // compaction in index order: wave w owns [w * per, (w + 1) * per) of the
   // chunk, counted in a first pass and written in a second
   const int per = (cn + kIdxThreads - 1) / kIdxThreads * kWave;
@@ -1491,7 +1510,7 @@ IdxPlan indexer_plan(int B, int Tq, int64_t n_entries, int k) {
     p.off_region = p.off_uni + align256((size_t)p.nchunk * p.lm * 4);
     p.off_counts = p.off_region + npad * 8;
     p.off_ctr = p.off_counts + align256((size_t)p.nseg * 4);
-    p.off_skey = p.off_ctr + 256;
+    p.off_skey = p.off_ctr + align256((size_t)p.nchunk * 8);    // one-pass: a slot per chunk
     p.off_sidx = p.off_skey + npad * 4;
     p.per_query = p.off_sidx + npad * 4;
     p.chunk = (int)lchunk;
@@ -1516,7 +1535,8 @@ template <int FMT, int DI>
 static hipError_t launch_idx_long(const IdxArgs& a, bool fused, hipStream_t st) {
   const unsigned nq = (unsigned)((int64_t)a.B * a.Tq);
   if (fused) {
-    hipLaunchKernelGGL(idx_long_zero_kernel, dim3((nq + 255) / 256), dim3(256), 0, st, a, (int64_t)nq);
+    hipLaunchKernelGGL(idx_long_zero_kernel, dim3((unsigned)(((int64_t)nq * a.nchunk + 255) / 256)), dim3(256), 0, st,
+                       a, (int64_t)nq);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     // chunk index fastest: the chunks of a query are dispatched together
