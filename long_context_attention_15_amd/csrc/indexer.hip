@@ -703,19 +703,25 @@ __global__ __launch_bounds__(kIdxThreads) void idx_merge_kernel(IdxArgs a) {
 // radix select over the list gives the top-k, emitted in list order =
 // ascending index.  No workspace, no barriers, one pass over the keys.
 constexpr int kSQW = 4;                   // queries per wavefront (= workgroup)
-constexpr int kSCap = 992;                // candidate slots per query
-constexpr int kSSlots = (kSCap + kWave - 1) / kWave;   // list slots per lane when a list is in registers
 constexpr int kSStep = 64;                // entries per iteration (two MFMA column blocks)
 constexpr int kSSlack = 96;               // a compaction keeps at most k + kSSlack entries
-constexpr int kStreamMaxK = kSCap - kSSlack - 2 * kSStep;
+// Candidate slots per query.  The kernel is bound by how many wavefronts a
+// CU holds, and the lists set that (one wavefront per workgroup): 736 slots
+// leave room for 8 workgroups per CU, 992 for 6, so lists are kept as short
+// as k allows (more frequent compactions cost less than the lost occupancy).
+constexpr int kSCapSmall = 736;
+constexpr int kSCapLarge = 992;
+template <int CAP>
+constexpr int stream_max_k() { return CAP - kSSlack - 2 * kSStep; }
+constexpr int kStreamMaxK = stream_max_k<kSCapLarge>();
 constexpr int64_t kStreamMaxN = 65536;    // candidate indices are 16-bit
 constexpr int64_t kStreamMinQueries = 2048;
 
-constexpr int kSRowCap = kSCap + kWave;   // list slots + one spare slot per lane
-
+// list slots + one spare slot per lane
+template <int CAP>
 struct StreamLds {
-  uint32_t ckey[kSQW][kSRowCap];
-  uint16_t cidx[kSQW][kSRowCap];
+  uint32_t ckey[kSQW][CAP + kWave];
+  uint16_t cidx[kSQW][CAP + kWave];
   uint32_t hist[256];
 };
 
@@ -758,25 +764,28 @@ __device__ __forceinline__ float thr_float(uint32_t thr) {
 
 // A candidate list held in registers: lane l owns positions 64 j + l; key 0
 // marks an empty slot (every real key is nonzero).
+template <int NS>
 struct RegList {
-  uint32_t key[kSSlots];
-  uint32_t id[kSSlots];
+  uint32_t key[NS];
+  uint32_t id[NS];
 };
 
-__device__ __forceinline__ void list_load(const uint32_t* keys, const uint16_t* ids, int n, RegList& r) {
+template <int NS>
+__device__ __forceinline__ void list_load(const uint32_t* keys, const uint16_t* ids, int n, RegList<NS>& r) {
   const int lane = threadIdx.x % kWave;
 #pragma unroll
-  for (int j = 0; j < kSSlots; ++j) {
+  for (int j = 0; j < NS; ++j) {
     const int pos = kWave * j + lane;
     r.key[j] = pos < n ? keys[pos] : 0u;
     r.id[j] = pos < n ? (uint32_t)ids[pos] : 0u;
   }
 }
 
-__device__ __forceinline__ void list_minmax(const RegList& r, uint32_t& kmin, uint32_t& kmax) {
+template <int NS>
+__device__ __forceinline__ void list_minmax(const RegList<NS>& r, uint32_t& kmin, uint32_t& kmax) {
   uint32_t lo = 0xffffffffu, hi = 0u;
 #pragma unroll
-  for (int j = 0; j < kSSlots; ++j) {
+  for (int j = 0; j < NS; ++j) {
     const uint32_t k = r.key[j];
     lo = (k != 0u && k < lo) ? k : lo;
     hi = k > hi ? k : hi;
@@ -788,13 +797,14 @@ __device__ __forceinline__ void list_minmax(const RegList& r, uint32_t& kmin, ui
 // One 8-bit radix digit over the list's keys restricted to (key & mask) ==
 // prefix: the digit value `bin` holding the need-th largest key, the number
 // of keys in higher digits (`above`) and in that digit (`inbin`).
-__device__ void list_digit(const RegList& r, uint32_t prefix, uint32_t mask, int shift, int need, uint32_t* hist,
+template <int NS>
+__device__ void list_digit(const RegList<NS>& r, uint32_t prefix, uint32_t mask, int shift, int need, uint32_t* hist,
                            int& bin, int& above, int& inbin) {
   const int lane = threadIdx.x % kWave;
   *(uint4*)(hist + 4 * lane) = make_uint4(0u, 0u, 0u, 0u);
   lds_wave_sync();
 #pragma unroll
-  for (int j = 0; j < kSSlots; ++j) {
+  for (int j = 0; j < NS; ++j) {
     const uint32_t k = r.key[j];
     if (k != 0u && (k & mask) == prefix) atomicAdd(&hist[(k >> shift) & 255u], 1u);
   }
@@ -828,9 +838,10 @@ __device__ void list_digit(const RegList& r, uint32_t prefix, uint32_t mask, int
 // to at most kk + slack (then T = bin lower bound - 1 and need_eq = 0: all
 // keys >= the bound stay); otherwise it runs to the last bit and the cut is
 // exact (kept == kk).  1 <= kk <= length.
-__device__ void list_cut(const RegList& r, int kk, int slack, uint32_t* hist, uint32_t& T, int& need_eq) {
+template <int NS>
+__device__ void list_cut(const RegList<NS>& r, int kk, int slack, uint32_t* hist, uint32_t& T, int& need_eq) {
   uint32_t kmin, kmax;
-  list_minmax(r, kmin, kmax);
+  list_minmax<NS>(r, kmin, kmax);
   if (kmin == kmax) { T = kmin; need_eq = kk; return; }
   int hb = 31 - __builtin_clz(kmin ^ kmax);           // highest differing bit
   uint32_t mask = hb == 31 ? 0u : ~((2u << hb) - 1u);
@@ -839,7 +850,7 @@ __device__ void list_cut(const RegList& r, int kk, int slack, uint32_t* hist, ui
   while (true) {
     const int shift = hb >= 7 ? hb - 7 : 0;
     int bin, above, inbin;
-    list_digit(r, prefix, mask, shift, need, hist, bin, above, inbin);
+    list_digit<NS>(r, prefix, mask, shift, need, hist, bin, above, inbin);
     above_all += above;
     const uint32_t lo = prefix | ((uint32_t)bin << shift);
     if (lo > 0u && above_all + inbin <= kk + slack) { T = lo - 1u; need_eq = 0; return; }
@@ -855,12 +866,13 @@ __device__ void list_cut(const RegList& r, int kk, int slack, uint32_t* hist, ui
 
 // Rewrite the list with the entries of key > T plus the first need_eq of
 // key == T, in order; returns the new length.
-__device__ int list_store_kept(const RegList& r, uint32_t T, int need_eq, uint32_t* keys, uint16_t* ids) {
+template <int NS>
+__device__ int list_store_kept(const RegList<NS>& r, uint32_t T, int need_eq, uint32_t* keys, uint16_t* ids) {
   const int lane = threadIdx.x % kWave;
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int out = 0, eqs = 0;
 #pragma unroll
-  for (int j = 0; j < kSSlots; ++j) {
+  for (int j = 0; j < NS; ++j) {
     const uint32_t k = r.key[j];
     const bool eq = k != 0u && k == T;
     const uint64_t beq = __ballot(eq);
@@ -882,15 +894,16 @@ __device__ int list_store_kept(const RegList& r, uint32_t T, int need_eq, uint32
 // and raises thr (a strict bound: later entries need key > thr; every kept
 // entry has key > T, or key == T and a smaller index, so an entry with key
 // <= T ranks below at least k kept ones).
+template <int NS>
 __device__ int list_shrink(uint32_t* keys, uint16_t* ids, int n, int k, uint32_t* hist, uint32_t& thr) {
-  RegList r;
-  list_load(keys, ids, n, r);
+  RegList<NS> r;
+  list_load<NS>(keys, ids, n, r);
   uint32_t T;
   int need_eq;
-  list_cut(r, k, kSSlack, hist, T, need_eq);
+  list_cut<NS>(r, k, kSSlack, hist, T, need_eq);
   const uint32_t bound = need_eq == 0 ? T + 1u : T;
   thr = bound > thr ? bound : thr;
-  return list_store_kept(r, T, need_eq, keys, ids);
+  return list_store_kept<NS>(r, T, need_eq, keys, ids);
 }
 
 struct StreamArgs {
@@ -909,8 +922,11 @@ struct KeyRegs {
   float sc[2];
 };
 
+template <int CAP>
 __global__ __launch_bounds__(kWave) void idx_stream_kernel(StreamArgs a) {
-  __shared__ StreamLds S;
+  constexpr int NS = (CAP + kWave - 1) / kWave;   // list slots per lane when a list is in registers
+  constexpr int kSRowCap = CAP + kWave;
+  __shared__ StreamLds<CAP> S;
   const int lane = threadIdx.x;
   const int g = lane >> 5, l32 = lane & 31;
   // heaviest groups (latest queries) first
@@ -1025,8 +1041,8 @@ __global__ __launch_bounds__(kWave) void idx_stream_kernel(StreamArgs a) {
     const uint64_t mA = __ballot(pA), mB = __ballot(pB);
     const int a_lo = __popcll(mA & 0xffffffffull), a_hi = __popcll(mA >> 32);
     const int b_lo = __popcll(mB & 0xffffffffull), b_hi = __popcll(mB >> 32);
-    const int dA = pA ? lane_rank(mA, g ? cnt[1] - a_lo : cnt[0]) : kSCap + lane;
-    const int dB = pB ? lane_rank(mB, g ? cnt[3] - b_lo : cnt[2]) : kSCap + lane;
+    const int dA = pA ? lane_rank(mA, g ? cnt[1] - a_lo : cnt[0]) : CAP + lane;
+    const int dB = pB ? lane_rank(mB, g ? cnt[3] - b_lo : cnt[2]) : CAP + lane;
     ck[qA * kSRowCap + dA] = key_of(sA);
     ci[qA * kSRowCap + dA] = (uint16_t)e;
     ck[qB * kSRowCap + dB] = key_of(sB);
@@ -1041,8 +1057,8 @@ __global__ __launch_bounds__(kWave) void idx_stream_kernel(StreamArgs a) {
     bool shrunk = false;
 #pragma unroll
     for (int qq = 0; qq < kSQW; ++qq) {
-      if (cnt[qq] > kSCap - kSStep) {                              // uniform
-        cnt[qq] = list_shrink(ck + qq * kSRowCap, ci + qq * kSRowCap, cnt[qq], a.k, S.hist, thr[qq]);
+      if (cnt[qq] > CAP - kSStep) {                              // uniform
+        cnt[qq] = list_shrink<NS>(ck + qq * kSRowCap, ci + qq * kSRowCap, cnt[qq], a.k, S.hist, thr[qq]);
         shrunk = true;
       }
     }
@@ -1091,14 +1107,14 @@ __global__ __launch_bounds__(kWave) void idx_stream_kernel(StreamArgs a) {
       for (int i = lane; i < n; i += kWave) out[i] = (int32_t)ids[i];
       continue;
     }
-    RegList r;
-    list_load(keys, ids, n, r);
+    RegList<NS> r;
+    list_load<NS>(keys, ids, n, r);
     uint32_t T;
     int need_eq;
-    list_cut(r, kk, 0, S.hist, T, need_eq);
+    list_cut<NS>(r, kk, 0, S.hist, T, need_eq);
     int outn = 0, eqs = 0;
 #pragma unroll
-    for (int j = 0; j < kSSlots; ++j) {
+    for (int j = 0; j < NS; ++j) {
       const uint32_t k = r.key[j];
       const bool eq = k != 0u && k == T;
       const uint64_t beq = __ballot(eq);
@@ -1121,7 +1137,9 @@ static hipError_t launch_idx_stream(const IdxArgs& ia, hipStream_t st) {
   a.qidx = ia.qidx; a.keys = ia.keys; a.head_w = ia.head_w; a.n_entries = ia.n_entries; a.q_pos = ia.q_pos;
   a.B = ia.B; a.Tq = ia.Tq; a.H_I = ia.H_I; a.m = ia.m; a.k = ia.k; a.sel = ia.sel;
   a.ngroups = (ia.Tq + kSQW - 1) / kSQW;
-  hipLaunchKernelGGL(idx_stream_kernel, dim3((unsigned)((int64_t)a.B * a.ngroups)), dim3(kWave), 0, st, a);
+  const dim3 grid((unsigned)((int64_t)a.B * a.ngroups));
+  if (a.k <= stream_max_k<kSCapSmall>()) hipLaunchKernelGGL(idx_stream_kernel<kSCapSmall>, grid, dim3(kWave), 0, st, a);
+  else hipLaunchKernelGGL(idx_stream_kernel<kSCapLarge>, grid, dim3(kWave), 0, st, a);
   return hipGetLastError();
 }
 
