@@ -115,6 +115,35 @@ csa_status csa_compress_kv(const void* tok, int tok_fmt, int B, int64_t T, int64
                            csa_store out, int64_t out_row0, hipStream_t stream);
 
 /*
+ * csa_decode_append -- cache maintenance for one decoded token per sequence
+ * (the window keeps the latest raw tokens: llm-tech overview, HCA section;
+ * only whole compression blocks enter the compressed cache, the incomplete
+ * tail block stays raw: kenelite analysis 16, inference infrastructure).
+ *
+ * For each b < B with position p = pos[b] (device int64; p < 0: nothing):
+ *   1. tail[b][p mod tail_rows] = tok[b]  (raw copy; tail is the caller's
+ *      [B][tail_rows][dim] ring of tok_fmt, tail_rows a positive multiple of
+ *      m, so a block's m rows are contiguous in it);
+ *   2. if win.rows != NULL: row p mod W of win for b = tok[b] quantised to
+ *      win.fmt (the bytes csa_compress_kv stores with m = 1);
+ *   3. if (p + 1) mod m == 0: entry j = (p + 1)/m - 1 of out for b = the
+ *      compression of tail rows for positions p+1-m .. p, with the gate,
+ *      bias and arithmetic of csa_compress_kv (its bytes are identical to
+ *      what csa_compress_kv stores for block j of the same tokens).  An entry
+ *      at or past out.cap is not written (pos is only known on the device).
+ * A decode step calls this once per cache: CSA KV (m = 4, with the window
+ * store), CSA indexer keys (m = 4, win.rows = NULL), HCA KV (m' = 128).
+ * Positions advance by one per call; the tail must hold the sequence's raw
+ * tokens of its current block (from prefill, or earlier calls).
+ * tok: [B][dim] (CSA_F32 or CSA_BF16), 16-byte aligned, as is tail.
+ * dim, formats and rope_dim as for csa_compress_kv; win.dim == out.dim,
+ * 1 <= W <= win.cap.
+ */
+csa_status csa_decode_append(const void* tok, int tok_fmt, int B, const int64_t* pos, void* tail, int tail_rows,
+                             int m, const float* gate, const float* bias, csa_store out, csa_store win, int W,
+                             hipStream_t stream);
+
+/*
  * csa_indexer_topk -- Lightning Indexer scores and top-k selection
  * (llm-tech overview, CSA section: the indexer picks the top-k compressed
  * entries; kenelite analysis 5.3: top-512 Flash, top-1024 Pro).

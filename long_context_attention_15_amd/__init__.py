@@ -42,6 +42,7 @@ _SIGS = {
     "csa_status_string": ([_I], ctypes.c_char_p),
     "csa_last_error": ([], ctypes.c_char_p),
     "csa_compress_kv": ([_P, _I, _I, _I64, _I64, _I, _P, _P, _CStore, _I64, _P], _I),
+    "csa_decode_append": ([_P, _I, _I, _P, _P, _I, _I, _P, _P, _CStore, _CStore, _I, _P], _I),
     "csa_indexer_topk_workspace": ([_I, _I, _I64, _I], _SZ),
     "csa_indexer_topk": ([_CStore, _P, _CStore, _I64, _P, _I, _I, _I, _I, _I, _P, _P, _SZ, _P], _I),
     "csa_attn_workspace": ([_I, _I, _I, _I, _I64], _SZ),
@@ -152,6 +153,19 @@ def compress_kv(tok, m: int, gate, bias, out: Store, out_row0: int = 0, stream=N
     assert tok.stride(2) == 1 and tok.stride(1) == D, "token rows must be contiguous"
     _check(load().csa_compress_kv(_ptr(tok), _fmt_of(tok), B, T, tok.stride(0), m, _ptr(gate), _ptr(bias),
                                   out.c(), out_row0, _stream(stream)), "csa_compress_kv")
+
+
+def decode_append(tok, pos, tail, m: int, gate, bias, out: Store, win: Optional[Store] = None, W: int = 0,
+                  stream=None):
+    """csa_decode_append: tok [B][dim] float32 or bfloat16, pos [B] int64, tail [B][R][dim] (tok's dtype,
+    R a multiple of m); window row pos mod W of `win` when given, entry (pos+1)/m - 1 of `out` when a
+    block closes."""
+    B, D = tok.shape
+    assert tok.is_contiguous() and tail.is_contiguous() and tail.dtype == tok.dtype and tail.shape[0] == B
+    assert tail.shape[2] == D and pos.dtype.itemsize == 8 and pos.numel() == B
+    wc = win.c() if win is not None else _CStore(None, None, 0, 0, 0, 0, 0)
+    _check(load().csa_decode_append(_ptr(tok), _fmt_of(tok), B, _ptr(pos), _ptr(tail), int(tail.shape[1]), m,
+                                    _ptr(gate), _ptr(bias), out.c(), wc, W, _stream(stream)), "csa_decode_append")
 
 
 def indexer_topk_workspace(B: int, Tq: int, n_entries: int, k: int) -> int:

@@ -120,6 +120,32 @@ csa_status csa_compress_kv(const void* tok, int tok_fmt, int B, int64_t T, int64
                     "csa_compress_kv launch");
 }
 
+csa_status csa_decode_append(const void* tok, int tok_fmt, int B, const int64_t* pos, void* tail, int tail_rows,
+                             int m, const float* gate, const float* bias, csa_store out, csa_store win, int W,
+                             hipStream_t stream) {
+  g_err[0] = 0;
+  if (B < 0) return fail(CSA_EINVAL, "B must be >= 0");
+  if (m < 1 || m > csa::compress_max_m()) return fail(CSA_EINVAL, "m = %d outside [1, %d]", m, csa::compress_max_m());
+  if (!tok || !pos || !tail || !gate || !bias) return fail(CSA_EINVAL, "tok, pos, tail, gate and bias must be non-NULL");
+  if (tok_fmt != CSA_F32 && tok_fmt != CSA_BF16) return fail(CSA_EUNSUPPORTED, "tok_fmt must be CSA_F32 or CSA_BF16");
+  if (!aligned(tok, 16) || !aligned(tail, 16)) return fail(CSA_EINVAL, "tok and tail must be 16-byte aligned");
+  if (!aligned(pos, 8)) return fail(CSA_EINVAL, "pos must be 8-byte aligned");
+  if (tail_rows < m || tail_rows % m != 0) return fail(CSA_EINVAL, "tail_rows = %d is not a positive multiple of m", tail_rows);
+  CSA_TRY(check_store(out, "out"));
+  const int vpl = out.dim >= 64 ? out.dim / 64 : 1;
+  if (out.fmt == CSA_FP8_E4M3 && out.rope_dim % vpl != 0)
+    return fail(CSA_EUNSUPPORTED, "rope_dim must be a multiple of dim / 64");
+  if (win.rows) {
+    CSA_TRY(check_store(win, "win"));
+    if (win.dim != out.dim) return fail(CSA_EINVAL, "win.dim != out.dim");
+    if (W < 1 || W > win.cap) return fail(CSA_EINVAL, "W = %d outside [1, win.cap]", W);
+    if (win.fmt == CSA_FP8_E4M3 && win.rope_dim % vpl != 0)
+      return fail(CSA_EUNSUPPORTED, "win.rope_dim must be a multiple of dim / 64");
+  }
+  return hip_status(csa::launch_decode_append(tok, tok_fmt, B, pos, tail, tail_rows, m, gate, bias, out, win, W, stream),
+                    "csa_decode_append launch");
+}
+
 size_t csa_indexer_topk_workspace(int B, int Tq, int64_t n_entries, int k) {
   if (B < 0 || Tq < 0 || k < 1) return 0;
   csa::IdxPlan p = csa::indexer_plan(B, Tq, n_entries, k);

@@ -54,23 +54,66 @@ __device__ __forceinline__ void load_vals<uint16_t, 8>(const uint16_t* p, float 
   for (int i = 0; i < 4; ++i) { v[2 * i] = bf16_to_f32(w[i] & 0xffffu); v[2 * i + 1] = bf16_to_f32(w[i] >> 16); }
 }
 
-template <typename TIn, int VPL>
-__global__ __launch_bounds__(kWave * kCompressWaves) void compress_kernel(
-    const TIn* __restrict__ tok, int B, int64_t T, int64_t bstride, int m,
-    const float* __restrict__ gate, const float* __restrict__ bias, StoreW out, int64_t row0,
-    int64_t N) {
-  __shared__ float s_alpha[kCompressWaves][kMaxM];
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  int64_t e = (int64_t)blockIdx.x * kCompressWaves + wave;
-  // waves past the end idle through the block barriers below
-  const bool valid = e < (int64_t)B * N;
-  if (!valid) e = 0;
-  const int b = (int)(e / N);
-  const int64_t j = e % N;
+// Quantise one entry (lane l holds dims [l*VPL, l*VPL + VPL) in acc; lanes
+// with active == false hold none) into row `row_out` of `out`.  Called by
+// the whole wavefront (row maxima are wavefront reductions).
+template <int VPL>
+__device__ __forceinline__ void store_entry(const float (&acc)[VPL], bool active, StoreW out, int64_t row_out) {
+  const int lane = threadIdx.x % kWave;
+  const int D = out.dim;
+  uint8_t* dst = out.rows + row_out * out.row_bytes;
+  if (out.fmt == CSA_F32) {
+    if (active) {
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) ((float*)dst)[lane * VPL + v] = acc[v];
+    }
+  } else if (out.fmt == CSA_FP8_E4M3) {
+    const int nb = D - out.rope;          // bulk dims
+    const bool bulk = active && lane * VPL < nb;
+    float am = 0.0f;
+    if (bulk) {
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) am = fmaxf(am, fabsf(acc[v]));
+    }
+    am = wave_max(am);
+    const float s = fp8_row_scale(am);
+    const int es = ilogbf(s);
+    if (bulk) {
+      uint8_t c[VPL];
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) c[v] = (uint8_t)f32_to_e4m3(ldexpf(acc[v], -es));
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) dst[lane * VPL + v] = c[v];
+    } else if (active) {
+      uint16_t* r = (uint16_t*)(dst + nb);
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) r[lane * VPL + v - nb] = (uint16_t)f32_to_bf16(acc[v]);
+    }
+    if (lane == 0) ((float*)out.scales)[row_out] = s;
+  } else {  // CSA_MXFP4, VPL == 1, D in {32, 64}
+    float am = active ? fabsf(acc[0]) : 0.0f;
+    am = wave_max<32>(am);                // lanes 0-31 = block 0, 32-63 = block 1
+    const int E = mx_block_exp(am);
+    uint32_t c = active ? f32_to_e2m1(ldexpf(acc[0], -E)) : 0u;
+    uint32_t hi = __shfl_xor(c, 1);
+    if (active && (lane & 1) == 0) dst[lane >> 1] = (uint8_t)(c | (hi << 4));
+    if (active && (lane & 31) == 0)
+      ((uint8_t*)out.scales)[row_out * (D / 32) + (lane >> 5)] = (uint8_t)(E + 127);
+  }
+}
+
+// One output entry per wavefront: the m token rows are row(0) .. row(m-1)
+// (lane l owns dims [l*VPL, l*VPL + VPL)); the entry goes to row `row_out`
+// of `out`.  Called by every wavefront of the workgroup (the block
+// barriers); a wavefront with valid == false computes on row(0) = some
+// readable row and stores nothing.
+template <typename TIn, int VPL, typename RowFn>
+__device__ __forceinline__ void compress_entry(RowFn row, int m, const float* __restrict__ gate,
+                                               const float* __restrict__ bias, StoreW out, int64_t row_out,
+                                               bool valid, float* alpha) {
+  const int lane = threadIdx.x % kWave;
   const int D = out.dim;
   const bool active = valid && lane * VPL < D;
-  const TIn* base = tok + (int64_t)b * bstride + j * m * (int64_t)D + lane * VPL;
-  float* alpha = s_alpha[wave];
 
   float g[VPL];
 #pragma unroll
@@ -81,7 +124,7 @@ __global__ __launch_bounds__(kWave * kCompressWaves) void compress_kernel(
     float x[VPL];
     float p = 0.0f;
     if (active) {
-      load_vals<TIn, VPL>(base + (int64_t)i * D, x);
+      load_vals<TIn, VPL>(row(i) + lane * VPL, x);
 #pragma unroll
       for (int v = 0; v < VPL; ++v) p = fmaf(x[v], g[v], p);
     }
@@ -111,12 +154,12 @@ __global__ __launch_bounds__(kWave * kCompressWaves) void compress_kernel(
     // the sum starts from the first term (not from +0), so m = 1 stores x
     // itself, signed zeros included
     float x0[VPL];
-    load_vals<TIn, VPL>(base, x0);
+    load_vals<TIn, VPL>(row(0) + lane * VPL, x0);
 #pragma unroll
     for (int v = 0; v < VPL; ++v) acc[v] = alpha[0] * x0[v];
     for (int i = 1; i < m; ++i) {
       float x[VPL];
-      load_vals<TIn, VPL>(base + (int64_t)i * D, x);
+      load_vals<TIn, VPL>(row(i) + lane * VPL, x);
       const float a = alpha[i];
 #pragma unroll
       for (int v = 0; v < VPL; ++v) acc[v] = fmaf(a, x[v], acc[v]);
@@ -124,47 +167,94 @@ __global__ __launch_bounds__(kWave * kCompressWaves) void compress_kernel(
   }
 
   if (!valid) return;
-  // quantise + store
-  const int64_t row = (int64_t)b * out.cap + row0 + j;
-  uint8_t* dst = out.rows + row * out.row_bytes;
-  if (out.fmt == CSA_F32) {
-    if (active) {
+  store_entry<VPL>(acc, active, out, row_out);
+}
+
+template <typename TIn, int VPL>
+__global__ __launch_bounds__(kWave * kCompressWaves) void compress_kernel(
+    const TIn* __restrict__ tok, int B, int64_t T, int64_t bstride, int m,
+    const float* __restrict__ gate, const float* __restrict__ bias, StoreW out, int64_t row0,
+    int64_t N) {
+  __shared__ float s_alpha[kCompressWaves][kMaxM];
+  const int wave = threadIdx.x / kWave;
+  int64_t e = (int64_t)blockIdx.x * kCompressWaves + wave;
+  // waves past the end idle through the block barriers
+  const bool valid = e < (int64_t)B * N;
+  if (!valid) e = 0;
+  const int b = (int)(e / N);
+  const int64_t j = e % N;
+  const int D = out.dim;
+  const TIn* base = tok + (int64_t)b * bstride + j * m * (int64_t)D;
+  compress_entry<TIn, VPL>([&](int i) { return base + (int64_t)i * D; }, m, gate, bias, out,
+                           (int64_t)b * out.cap + row0 + j, valid, s_alpha[wave]);
+}
+
+// Decode-time cache maintenance, one wavefront per sequence b at position
+// p = pos[b] (p < 0: nothing): the raw token goes to slot p mod R of the
+// sequence's tail ring, its quantised row to window slot p mod W (when a
+// window store is given), and when p closes a block ((p + 1) mod m == 0)
+// the block's m raw tokens, read back from the tail ring in position order,
+// are compressed into entry (p + 1) / m - 1 by the same code as
+// compress_kernel (entries at or past out.cap are not written).  Each lane
+// writes and reads back only its own dims of the tail row.
+template <typename TIn, int VPL>
+__global__ __launch_bounds__(kWave * kCompressWaves) void decode_append_kernel(
+    const TIn* __restrict__ tok, int B, const int64_t* __restrict__ pos, TIn* tail, int R, int m,
+    const float* __restrict__ gate, const float* __restrict__ bias, StoreW out, StoreW win, int W) {
+  __shared__ float s_alpha[kCompressWaves][kMaxM];
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  int b = (int)blockIdx.x * kCompressWaves + wave;
+  const bool in_batch = b < B;
+  if (!in_batch) b = 0;
+  const int64_t p = pos[b];
+  const bool live = in_batch && p >= 0;
+  const int D = out.dim;
+  const TIn* x = tok + (int64_t)b * D;
+  TIn* tb = tail + (int64_t)b * R * D;
+  if (live && lane * VPL < D) {
 #pragma unroll
-      for (int v = 0; v < VPL; ++v) ((float*)dst)[lane * VPL + v] = acc[v];
-    }
-  } else if (out.fmt == CSA_FP8_E4M3) {
-    const int nb = D - out.rope;          // bulk dims
-    const bool bulk = active && lane * VPL < nb;
-    float am = 0.0f;
-    if (bulk) {
-#pragma unroll
-      for (int v = 0; v < VPL; ++v) am = fmaxf(am, fabsf(acc[v]));
-    }
-    am = wave_max(am);
-    const float s = fp8_row_scale(am);
-    const int es = ilogbf(s);
-    if (bulk) {
-      uint8_t c[VPL];
-#pragma unroll
-      for (int v = 0; v < VPL; ++v) c[v] = (uint8_t)f32_to_e4m3(ldexpf(acc[v], -es));
-#pragma unroll
-      for (int v = 0; v < VPL; ++v) dst[lane * VPL + v] = c[v];
-    } else if (active) {
-      uint16_t* r = (uint16_t*)(dst + nb);
-#pragma unroll
-      for (int v = 0; v < VPL; ++v) r[lane * VPL + v - nb] = (uint16_t)f32_to_bf16(acc[v]);
-    }
-    if (lane == 0) ((float*)out.scales)[row] = s;
-  } else {  // CSA_MXFP4, VPL == 1, D in {32, 64}
-    float am = active ? fabsf(acc[0]) : 0.0f;
-    am = wave_max<32>(am);                // lanes 0-31 = block 0, 32-63 = block 1
-    const int E = mx_block_exp(am);
-    uint32_t c = active ? f32_to_e2m1(ldexpf(acc[0], -E)) : 0u;
-    uint32_t hi = __shfl_xor(c, 1);
-    if (active && (lane & 1) == 0) dst[lane >> 1] = (uint8_t)(c | (hi << 4));
-    if (active && (lane & 31) == 0)
-      ((uint8_t*)out.scales)[row * (D / 32) + (lane >> 5)] = (uint8_t)(E + 127);
+    for (int v = 0; v < VPL; ++v) tb[(p % R) * D + lane * VPL + v] = x[lane * VPL + v];
   }
+  if (win.rows && live) {                              // the window row: the token quantised
+    float xv[VPL];
+    const bool act = lane * VPL < D;
+    if (act) load_vals<TIn, VPL>(x + lane * VPL, xv);
+    else {
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) xv[v] = 0.0f;
+    }
+    store_entry<VPL>(xv, act, win, (int64_t)b * win.cap + p % W);
+  }
+  const bool close = live && (p + 1) % m == 0 && (p + 1) / m - 1 < out.cap;
+  const int64_t j = close ? (p + 1) / m - 1 : 0;
+  const int64_t r0 = close ? (p + 1 - m) % R : 0;      // first row of the block in the ring
+  compress_entry<TIn, VPL>([&](int i) { return (const TIn*)tb + ((r0 + i) % R) * D; }, m, gate, bias, out,
+                           (int64_t)b * out.cap + j, close, s_alpha[wave]);
+}
+
+template <typename TIn, int VPL>
+static hipError_t launch_append_t(const void* tok, int B, const int64_t* pos, void* tail, int R, int m,
+                                  const float* gate, const float* bias, const csa_store& out, const csa_store& win,
+                                  int W, hipStream_t st) {
+  if (B == 0) return hipSuccess;
+  const StoreW w = win.rows ? wview(win) : StoreW{nullptr, nullptr, 0, out.dim, 0, out.fmt, 0};
+  hipLaunchKernelGGL((decode_append_kernel<TIn, VPL>), dim3((unsigned)((B + kCompressWaves - 1) / kCompressWaves)),
+                     dim3(kWave * kCompressWaves), 0, st, (const TIn*)tok, B, pos, (TIn*)tail, R, m, gate, bias,
+                     wview(out), w, W);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_append(const void* tok, int tok_fmt, int B, const int64_t* pos, void* tail, int R, int m,
+                                const float* gate, const float* bias, const csa_store& out, const csa_store& win,
+                                int W, hipStream_t st) {
+  const int vpl = out.dim >= 64 ? out.dim / 64 : 1;
+#define CSA_APP(TT, V) return launch_append_t<TT, V>(tok, B, pos, tail, R, m, gate, bias, out, win, W, st)
+  if (tok_fmt == CSA_F32) {
+    switch (vpl) { case 1: CSA_APP(float, 1); case 2: CSA_APP(float, 2); case 4: CSA_APP(float, 4); default: CSA_APP(float, 8); }
+  } else {
+    switch (vpl) { case 1: CSA_APP(uint16_t, 1); case 2: CSA_APP(uint16_t, 2); case 4: CSA_APP(uint16_t, 4); default: CSA_APP(uint16_t, 8); }
+  }
+#undef CSA_APP
 }
 
 // Blocks of one token (m = 1): the softmax weight of a single logit is

@@ -13,6 +13,9 @@ hipError_t launch_compress(const void* tok, int tok_fmt, int B, int64_t T, int64
                            const float* gate, const float* bias, const csa_store& out, int64_t row0,
                            hipStream_t st);
 int compress_max_m();
+hipError_t launch_decode_append(const void* tok, int tok_fmt, int B, const int64_t* pos, void* tail, int R, int m,
+                                const float* gate, const float* bias, const csa_store& out, const csa_store& win,
+                                int W, hipStream_t st);
 
 // Indexer: chunk size and chunk count chosen for a call; workspace bytes.
 struct IdxPlan {

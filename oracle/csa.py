@@ -69,6 +69,32 @@ def compress(x: np.ndarray, gate: np.ndarray, bias: np.ndarray, m: int) -> np.nd
     return np.einsum("nm,nmd->nd", alpha, blocks)
 
 
+def decode_append(x: np.ndarray, gate: np.ndarray, bias: np.ndarray, m: int, W: int, p0: int, p1: int):
+    """Decode-time cache maintenance of one sequence (kenelite analysis 16,
+    inference infrastructure: only whole compression blocks enter the
+    compressed cache, an incomplete tail block stays raw; llm-tech overview,
+    HCA section: the sliding window holds the latest raw tokens).
+
+    x [T, D] the sequence's tokens.  Positions < p0 were handled before, so
+    the raw tail holds the tokens of the current block up to p0; positions
+    p0 .. p1-1 arrive one per step.  Each step puts its token in window slot
+    p mod W and in the tail; when the tail holds m tokens the block is
+    compressed (as in `compress`) into entry p // m = (p+1)/m - 1 and the
+    tail restarts.  Returns (entries {j: c_j [D]} for the blocks closed by
+    these steps, window {slot: position} of the slots they wrote).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    tail = [x[q] for q in range((p0 // m) * m, p0)]
+    entries, window = {}, {}
+    for p in range(p0, p1):
+        tail.append(x[p])
+        window[p % W] = p
+        if len(tail) == m:
+            entries[p // m] = compress(np.stack(tail), gate, bias, m)[0]
+            tail = []
+    return entries, window
+
+
 # ------------------------------------------------------------- storage rows
 def row_bytes(fmt: str, D: int, R: int = 0) -> int:
     if fmt == "f32":

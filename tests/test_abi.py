@@ -54,6 +54,22 @@ def _store(ptr=16, cap=8, dim=64, rope=0, fmt=csa.F32, scales=0):
 P = 1 << 20
 
 
+def test_decode_append_rejects_bad_arguments(lib):
+    out = _store(P, 8, 64)
+    nowin = csa._CStore(None, None, 0, 0, 0, 0, 0)
+    # null pos, tail rows not a multiple of m, m out of range, unaligned tail
+    assert lib.csa_decode_append(P, csa.F32, 2, 0, P, 8, 4, P, P, out, nowin, 0, None) == 1
+    assert lib.csa_decode_append(P, csa.F32, 2, P, P, 6, 4, P, P, out, nowin, 0, None) == 1
+    assert "multiple of m" in lib.csa_last_error().decode()
+    assert lib.csa_decode_append(P, csa.F32, 2, P, P, 8, 0, P, P, out, nowin, 0, None) == 1
+    assert lib.csa_decode_append(P, csa.F32, 2, P, P + 4, 8, 4, P, P, out, nowin, 0, None) == 1
+    # unsupported token format, window of another dim, W beyond the window store
+    assert lib.csa_decode_append(P, csa.MXFP4, 2, P, P, 8, 4, P, P, out, nowin, 0, None) == 2
+    assert lib.csa_decode_append(P, csa.F32, 2, P, P, 8, 4, P, P, out, _store(P, 8, 128), 4, None) == 1
+    assert lib.csa_decode_append(P, csa.F32, 2, P, P, 8, 4, P, P, out, _store(P, 8, 64), 9, None) == 1
+    assert "W = 9" in lib.csa_last_error().decode()
+
+
 def test_compress_rejects_bad_arguments(lib):
     out = _store(P, 8, 64)
     # m out of range

@@ -56,6 +56,89 @@ def test_compress_parity(lib, name, tf, sf, D, R, m, T, B):
             assert frac <= 2e-3, f"{frac:.2e} of codes differ from the oracle's packing"
 
 
+APPEND_CASES = [
+    # name, tok fmt, store fmt, D, R, m, tail rows, window slots (0 = no window store), steps
+    ("csa_kv_bf16_fp8_D512_m4_window", "bf16", "fp8", 512, 64, 4, 4, 128, 150),
+    ("csa_idx_bf16_mxfp4_D64_m4_tail8", "bf16", "mxfp4", 64, 0, 4, 8, 0, 150),
+    ("hca_kv_bf16_fp8_D512_m128", "bf16", "fp8", 512, 64, 128, 128, 0, 150),
+    ("f32_f32_D32_m3_tail6_window16", "f32", "f32", 32, 0, 3, 6, 16, 60),
+]
+
+
+@pytest.mark.parametrize("name,tf,sf,D,R,m,Rt,W,steps", APPEND_CASES)
+def test_decode_append_matches_prefill_compression(lib, name, tf, sf, D, R, m, Rt, W, steps):
+    """Tokens appended one per step (sequences at different positions, one
+    with negative positions that must write nothing) leave the caches that
+    prefill builds: every entry closed by the steps has the bytes
+    csa_compress_kv stores for that block and lies within the compressor's
+    error bound of the oracle's entry; every window slot written holds the
+    oracle's packing of its token; rows not closed keep their old bytes."""
+    import torch
+    p0s = [0, 5, m + 2, -10 ** 6]
+    B = len(p0s)
+    Tmax = max(p0s) + steps
+    x = synth.tensor(0, "kv", (B, Tmax, D), rmsnorm=(tf == "bf16"))
+    g = synth.tensor(0, "gate", (D,), std=0.02)
+    bb = synth.tensor(0, "bias", (m,), std=0.02)
+    xd, xv = Hx.act(x, tf)
+    gd, bd = Hx.to_dev(g.astype(np.float32)), Hx.to_dev(bb.astype(np.float32))
+    ncap = Tmax // m + 2
+    out = lib.alloc_store(B, ncap, D, sf, R, device=Hx.dev())
+    out.rows.fill_(0xAB)
+    win = None
+    if W:
+        win = lib.alloc_store(B, W, D, sf, R, device=Hx.dev())
+        win.rows.fill_(0xCD)
+    tail = torch.zeros((B, Rt, D), dtype=xd.dtype, device=Hx.dev())
+    for b, p0 in enumerate(p0s):                 # the raw tokens of each sequence's current block
+        for q in range(max(0, (p0 // m) * m), max(0, p0)):
+            tail[b, q % Rt] = xd[b, q]
+    pos = torch.empty(B, dtype=torch.int64, device=Hx.dev())
+    tok = torch.zeros((B, D), dtype=xd.dtype, device=Hx.dev())
+    for st in range(steps):
+        ps = [p0 + st for p0 in p0s]
+        pos.copy_(torch.tensor(ps, dtype=torch.int64))
+        for b, p in enumerate(ps):
+            if p >= 0:
+                tok[b] = xd[b, p]
+        lib.decode_append(tok, pos, tail, m, gd, bd, out, win, W)
+    ref = lib.alloc_store(B, ncap, D, sf, R, device=Hx.dev())
+    lib.compress_kv(xd, m, gd, bd, ref)
+    _sync()
+    g32 = g.astype(np.float32).astype(np.float64)
+    b32 = bb.astype(np.float32).astype(np.float64)
+    for b, p0 in enumerate(p0s):
+        rows = out.rows[b].cpu().numpy()
+        if p0 < 0:
+            assert np.all(rows == 0xAB) and not bool(tail[b].any())
+            if W:
+                assert bool((win.rows[b] == 0xCD).all())
+            continue
+        entries, window = O.decode_append(xv[b], g32, b32, m, max(W, 1), p0, p0 + steps)
+        js = sorted(entries)
+        assert js == list(range(p0 // m, (p0 + steps) // m))
+        keep = np.ones(ncap, bool)
+        if js:
+            j0, j1 = js[0], js[-1] + 1
+            keep[j0:j1] = False
+            assert torch.equal(out.rows[b, j0:j1], ref.rows[b, j0:j1]), "entry bytes differ from csa_compress_kv"
+            sc = None
+            if out.scales is not None:
+                assert torch.equal(out.scales[b, j0:j1], ref.scales[b, j0:j1])
+                sc = out.scales[b, j0:j1].cpu().numpy()
+            c = np.stack([entries[j] for j in js])
+            eps = Hx.compress_error_bound(xv[b][j0 * m: j1 * m], g32, b32, m)
+            frac = Hx.check_compress(rows[j0:j1], sc, sf, D, R, c, eps)
+            if sf != "f32":
+                assert frac <= 2e-3
+        assert np.all(rows[keep] == 0xAB), "rows outside the closed blocks were written"
+        if W:
+            slots = sorted(window)
+            got = win.rows[b].cpu().numpy()[slots]
+            gsc = None if win.scales is None else win.scales[b].cpu().numpy()[slots]
+            Hx.check_compress(got, gsc, sf, D, R, xv[b][[window[s_] for s_ in slots]], None, exact_codes=True)
+
+
 @pytest.mark.parametrize("tf,sf,D,R", [("bf16", "fp8", 512, 64), ("f32", "fp8", 64, 16), ("bf16", "fp8", 64, 0),
                                        ("bf16", "mxfp4", 64, 0), ("f32", "mxfp4", 32, 0), ("f32", "f32", 64, 0),
                                        ("bf16", "fp8", 128, 0), ("f32", "fp8", 256, 64), ("bf16", "f32", 32, 0)])

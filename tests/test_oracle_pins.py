@@ -414,3 +414,25 @@ def test_generator_slices_are_consistent():
     assert np.array_equal(synth.normal(3, 7, (40,), start=33), full[33:73])
     z = synth.normal(0, 1, (200000,))
     assert abs(z.mean()) < 0.01 and abs(z.std() - 1) < 0.01
+
+
+def test_decode_append_equals_prefill_compression_and_keeps_the_last_window():
+    """Appending tokens one by one must leave the caches prefill builds: each
+    closed block's entry equals the entry `compress` gives for the whole
+    prefix (the block's tokens only), and the window slots hold the latest W
+    positions, position p in slot p mod W."""
+    rng = np.random.default_rng(21)
+    T, D, m, W = 61, 16, 4, 8
+    x = rng.standard_normal((T, D))
+    g = rng.standard_normal(D) * 0.3
+    b = rng.standard_normal(m) * 0.3
+    p0, p1 = 6, 58                      # starts inside block 1, stops inside block 14
+    entries, window = O.decode_append(x, g, b, m, W, p0, p1)
+    full = O.compress(x[:p1], g, b, m)
+    assert sorted(entries) == list(range(p0 // m, p1 // m))   # blocks closed by the steps: 1 .. 13
+    for j, c in entries.items():
+        np.testing.assert_allclose(c, full[j], rtol=1e-13, atol=1e-13)
+    assert window == {p % W: p for p in range(p1 - W, p1)}
+    # m' = 128 blocks: none closes before position 127; the window is the last W of the steps
+    e2, w2 = O.decode_append(x, g, b, 128, W, 0, T)
+    assert e2 == {} and sorted(w2.values()) == list(range(T - W, T))
