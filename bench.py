@@ -54,11 +54,12 @@ class Gen:
         return x if dtype is None else x.to(dtype)
 
 
-def quantised_rows(csa, gen, B, n, D, fmt, R, chunk_rows=1 << 18):
-    """A store of n RMS-normalised N(0,1) rows per batch element, quantised by
-    the library's own m = 1 compressor (as a prefill would have stored them)."""
+def quantised_rows(csa, gen, B, n, D, fmt, R, chunk_rows=1 << 18, cap=None):
+    """A store of n RMS-normalised N(0,1) rows per batch element (cap >= n
+    rows allocated), quantised by the library's own m = 1 compressor (as a
+    prefill would have stored them)."""
     import torch
-    st = csa.alloc_store(B, n, D, fmt, R)
+    st = csa.alloc_store(B, cap or n, D, fmt, R)
     zero = torch.zeros(D, device="cuda")
     one = torch.ones(1, device="cuda")
     for b in range(B):
@@ -171,8 +172,9 @@ class Decode1M:
         g = Gen(1 if hybrid else 2)
         bf = torch.bfloat16
         ifmt = "mxfp4" if hybrid else "fp8"
-        self.ckv = quantised_rows(csa, g, B, self.N, D, "fp8", R)
-        self.keys = quantised_rows(csa, g, B, self.N, dI, ifmt, 0)
+        # one spare entry each: the step that closes the next block writes it
+        self.ckv = quantised_rows(csa, g, B, self.N, D, "fp8", R, cap=self.N + 1)
+        self.keys = quantised_rows(csa, g, B, self.N, dI, ifmt, 0, cap=self.N + 1)
         self.ring = quantised_rows(csa, g, B, W, D, "fp8", R)
         self.qi = g.normal((B, HI, dI), rms=True, dtype=bf)
         self.qst = csa.alloc_store(B, HI, dI, ifmt)
@@ -190,12 +192,43 @@ class Decode1M:
         self.aws = torch.empty(max(aws, 16), dtype=torch.uint8, device="cuda")
         self.tau = 1.0 / math.sqrt(D)
         if hybrid:
-            self.hkv = quantised_rows(csa, g, B, self.Nh, D, "fp8", R)
+            self.hkv = quantised_rows(csa, g, B, self.Nh, D, "fp8", R, cap=self.Nh + 1)
             self.ring_h = quantised_rows(csa, g, B, W, D, "fp8", R)
             self.q_h = g.normal((B, 1, H, D), rms=True, dtype=bf)
             self.sink_h = g.normal((H,))
             self.out_h = torch.empty_like(self.q_h)
         self.flush = torch.empty(1 << 29, dtype=torch.uint8, device="cuda")   # 512 MiB > the 256 MB MALL
+        # cache maintenance of the step: the new token's KV and indexer key,
+        # raw tails of the current blocks, compressor weights
+        self.kv_tok = g.normal((B, D), rms=True, dtype=bf)
+        self.ik_tok = g.normal((B, dI), rms=True, dtype=bf)
+        self.kv_tail = g.normal((B, m, D), rms=True, dtype=bf)
+        self.ik_tail = g.normal((B, m, dI), rms=True, dtype=bf)
+        self.g_kv, self.b_kv = g.normal((D,), std=0.02), g.normal((m,), std=0.02)
+        self.g_ik, self.b_ik = g.normal((dI,), std=0.02), g.normal((m,), std=0.02)
+        if hybrid:
+            self.hkv_tok = g.normal((B, D), rms=True, dtype=bf)
+            self.h_tail = g.normal((B, mh, D), rms=True, dtype=bf)
+            self.g_h, self.b_h = g.normal((D,), std=0.02), g.normal((mh,), std=0.02)
+        # positions at which the step closes a block (CSA every m tokens, HCA every m')
+        self.pos_close_m = torch.full((B,), ctx + m - 1, dtype=torch.int64, device="cuda")
+        self.pos_close_mh = torch.full((B,), ctx + mh - 1, dtype=torch.int64, device="cuda")
+
+    def append_ops(self, pos, pos_h):
+        """Cache maintenance of the step's new token (window slot, tails, and
+        the compressed entry when a block closes at that position)."""
+        c = self.csa
+        o = [
+            ("csa_decode_append(kv)", lambda: c.decode_append(self.kv_tok, pos, self.kv_tail, self.m, self.g_kv,
+                                                              self.b_kv, self.ckv, self.ring, self.W)),
+            ("csa_decode_append(idx keys)", lambda: c.decode_append(self.ik_tok, pos, self.ik_tail, self.m,
+                                                                    self.g_ik, self.b_ik, self.keys)),
+        ]
+        if self.hybrid:
+            o.append(("hca_decode_append(kv)", lambda: c.decode_append(self.hkv_tok, pos_h, self.h_tail, self.mh,
+                                                                       self.g_h, self.b_h, self.hkv, self.ring_h,
+                                                                       self.W)))
+        return o
 
     def ops(self):
         c = self.csa
@@ -444,6 +477,14 @@ def main():
                          "hbm_gbs": {n: ab[n] / (per[n] * 1e-3) / 1e9 for n in ab},
                          "hbm_frac": {n: ab[n] / (per[n] * 1e-3) / 1e9 / HBM_PEAK_GBS for n in ab}}
             kernels.update({f"{name}/{n}": v for n, v in per.items()})
+            # cache maintenance of the new token (outside the step, whose caches
+            # are given): at the step's position, and at positions that close a
+            # block (every m-th token for CSA, every m'-th for HCA), where the
+            # compressed entry is written too
+            _, per_app = time_ops(d.append_ops(d.pos, d.pos), args.decode_steps, 2, flush=d.flush)
+            _, per_close = time_ops(d.append_ops(d.pos_close_m, d.pos_close_mh), args.decode_steps, 2, flush=d.flush)
+            dec[name]["append_us"] = {n: v * 1e3 for n, v in per_app.items()}
+            dec[name]["append_block_close_us"] = {n: v * 1e3 for n, v in per_close.items()}
             del d
             torch.cuda.empty_cache()
         result["decode"] = dec

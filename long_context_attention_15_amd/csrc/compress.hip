@@ -13,6 +13,7 @@ namespace csa {
 
 constexpr int kCompressWaves = 4;
 constexpr int kMaxM = 1024;
+constexpr int kRowBatch = 8;   // token rows whose loads are in flight together
 
 template <typename TIn, int VPL>
 __device__ __forceinline__ void load_vals(const TIn* p, float (&v)[VPL]);
@@ -119,17 +120,26 @@ __device__ __forceinline__ void compress_entry(RowFn row, int m, const float* __
 #pragma unroll
   for (int v = 0; v < VPL; ++v) g[v] = active ? gate[lane * VPL + v] : 0.0f;
 
-  // pass 1: logits
-  for (int i = 0; i < m; ++i) {
-    float x[VPL];
-    float p = 0.0f;
-    if (active) {
-      load_vals<TIn, VPL>(row(i) + lane * VPL, x);
+  // pass 1: logits, the rows loaded kRowBatch at a time, all in flight
+  // together: the loads are unconditional (past the block's end they re-read
+  // its last row, lanes past the row's dims re-read dims 0 .., all ignored),
+  // so nothing waits between them.  Each row's dot product keeps its order.
+  const int lo = lane * VPL < D ? lane * VPL : 0;
+  for (int i0 = 0; i0 < m; i0 += kRowBatch) {
+    float x[kRowBatch][VPL];
 #pragma unroll
-      for (int v = 0; v < VPL; ++v) p = fmaf(x[v], g[v], p);
+    for (int u = 0; u < kRowBatch; ++u) load_vals<TIn, VPL>(row(i0 + u < m ? i0 + u : m - 1) + lo, x[u]);
+#pragma unroll
+    for (int u = 0; u < kRowBatch; ++u) {
+      if (i0 + u >= m) break;                    // uniform
+      float p = 0.0f;
+      if (active) {
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) p = fmaf(x[u][v], g[v], p);
+      }
+      p = wave_sum(p);
+      if (lane == 0) alpha[i0 + u] = p + bias[i0 + u];
     }
-    p = wave_sum(p);
-    if (lane == 0) alpha[i] = p + bias[i];
   }
   __syncthreads();
   float mx = -INFINITY;
@@ -157,12 +167,17 @@ __device__ __forceinline__ void compress_entry(RowFn row, int m, const float* __
     load_vals<TIn, VPL>(row(0) + lane * VPL, x0);
 #pragma unroll
     for (int v = 0; v < VPL; ++v) acc[v] = alpha[0] * x0[v];
-    for (int i = 1; i < m; ++i) {
-      float x[VPL];
-      load_vals<TIn, VPL>(row(i) + lane * VPL, x);
-      const float a = alpha[i];
+    for (int i0 = 1; i0 < m; i0 += kRowBatch) {
+      float x[kRowBatch][VPL];
 #pragma unroll
-      for (int v = 0; v < VPL; ++v) acc[v] = fmaf(a, x[v], acc[v]);
+      for (int u = 0; u < kRowBatch; ++u) load_vals<TIn, VPL>(row(i0 + u < m ? i0 + u : m - 1) + lo, x[u]);
+#pragma unroll
+      for (int u = 0; u < kRowBatch; ++u) {
+        if (i0 + u >= m) break;
+        const float a = alpha[i0 + u];
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) acc[v] = fmaf(a, x[u][v], acc[v]);
+      }
     }
   }
 
@@ -226,6 +241,7 @@ __global__ __launch_bounds__(kWave * kCompressWaves) void decode_append_kernel(
     store_entry<VPL>(xv, act, win, (int64_t)b * win.cap + p % W);
   }
   const bool close = live && (p + 1) % m == 0 && (p + 1) / m - 1 < out.cap;
+  if (!__syncthreads_or(close)) return;               // no block closes in this workgroup
   const int64_t j = close ? (p + 1) / m - 1 : 0;
   const int64_t r0 = close ? (p + 1 - m) % R : 0;      // first row of the block in the ring
   compress_entry<TIn, VPL>([&](int i) { return (const TIn*)tb + ((r0 + i) % R) * D; }, m, gate, bias, out,
