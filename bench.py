@@ -246,6 +246,19 @@ class Decode1M:
                                                              flags=c.WIN_RING, ws=self.aws)))
         return o
 
+    def invariant_ops(self):
+        """The step's attention with CSA_BATCH_INVARIANT (no split lists)."""
+        c = self.csa
+        f = c.BATCH_INVARIANT
+        o = [("csa_sparse_attn_decode", lambda: c.sparse_attn_decode(self.q, self.ckv, self.N, self.sel, self.k,
+                                                                     self.ring, self.pos, self.W, self.sink,
+                                                                     self.tau, self.out, flags=f, ws=self.aws))]
+        if self.hybrid:
+            o.append(("hca_attn(decode)", lambda: c.hca_attn(self.q_h, self.hkv, self.mh, self.Nh, self.pos[:, None],
+                                                             self.ring_h, self.W, self.sink_h, self.tau, self.out_h,
+                                                             flags=c.WIN_RING | f, ws=self.aws)))
+        return o
+
     def algorithmic_bytes(self):
         """HBM bytes the method must move per step (no implementation overheads)."""
         B, N, k, W, H, D = self.B, self.N, self.k, self.W, self.H, self.D
@@ -485,6 +498,9 @@ def main():
             _, per_close = time_ops(d.append_ops(d.pos_close_m, d.pos_close_mh), args.decode_steps, 2, flush=d.flush)
             dec[name]["append_us"] = {n: v * 1e3 for n, v in per_app.items()}
             dec[name]["append_block_close_us"] = {n: v * 1e3 for n, v in per_close.items()}
+            # the attention with batch-invariant results (no split lists)
+            _, per_inv = time_ops(d.invariant_ops(), args.decode_steps, 2, flush=d.flush)
+            dec[name]["batch_invariant_attn_us"] = {n: v * 1e3 for n, v in per_inv.items()}
             del d
             torch.cuda.empty_cache()
         result["decode"] = dec

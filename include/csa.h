@@ -87,6 +87,12 @@ typedef struct {
                                entries, lse = ln sum_e exp(l_e) (-inf if none)  */
 #define CSA_WIN_RING 2      /* the window store is a ring of W slots per batch
                                element; position p lives in slot p mod W      */
+#define CSA_BATCH_INVARIANT 4  /* one workgroup per (query row, 64 heads) over
+                               the whole entry list, never a split list: a
+                               row's result bits depend on its own inputs
+                               only, whatever else is in the batch (the
+                               default splits few-query calls to fill the
+                               chip, and the split count follows B)          */
 
 const char* csa_version(void);
 const char* csa_status_string(int status);

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(PKG, "libcsa.so")
 F32, BF16, FP8_E4M3, MXFP4 = 0, 1, 2, 3
 ATTN_PARTIAL = 1
 WIN_RING = 2
+BATCH_INVARIANT = 4
 FMT_NAMES = {"f32": F32, "bf16": BF16, "fp8": FP8_E4M3, "mxfp4": MXFP4}
 
 

@@ -185,7 +185,8 @@ size_t csa_attn_workspace(int B, int Tq, int H, int dim, int64_t max_list) {
 }
 
 static csa_status run_attn(csa::AttnCall& c, int flags, hipStream_t stream, const char* what) {
-  if (flags & ~(CSA_ATTN_PARTIAL | CSA_WIN_RING)) return fail(CSA_EINVAL, "unknown flags 0x%x", flags);
+  if (flags & ~(CSA_ATTN_PARTIAL | CSA_WIN_RING | CSA_BATCH_INVARIANT))
+    return fail(CSA_EINVAL, "unknown flags 0x%x", flags);
   if (!std::isfinite(c.tau)) return fail(CSA_EINVAL, "sm_scale must be finite");
   if (c.W < 0 || c.W > 65536) return fail(CSA_EINVAL, "W outside [0, 65536]");
   c.partial = (flags & CSA_ATTN_PARTIAL) != 0;
@@ -198,7 +199,7 @@ static csa_status run_attn(csa::AttnCall& c, int flags, hipStream_t stream, cons
   if (need > 0 && c.ws && c.ws_bytes < need)
     return fail(CSA_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, c.ws_bytes);
   if (need > 0 && c.ws && !aligned(c.ws, 16)) return fail(CSA_EINVAL, "ws must be 16-byte aligned");
-  c.allow_split = need > 0 && c.ws != nullptr;
+  c.allow_split = need > 0 && c.ws != nullptr && !(flags & CSA_BATCH_INVARIANT);
   return hip_status(csa::launch_attn(c, stream), what);
 }
 

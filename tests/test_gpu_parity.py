@@ -460,6 +460,57 @@ def test_hca_decode_parity(lib):
         Hx.check_attn(got[b], want)
 
 
+def _seq_store(st, b):
+    """Sequence b of a store as a store of one sequence (same cap)."""
+    import long_context_attention_15_amd as csa
+    return csa.Store(st.rows[b:b + 1], None if st.scales is None else st.scales[b:b + 1], st.cap, st.dim, st.rope,
+                     st.fmt)
+
+
+def test_batch_invariant_decode_is_independent_of_the_batch(lib):
+    """With CSA_BATCH_INVARIANT a sequence's decode output (CSA sparse and
+    HCA dense attention) has the same bits whether it is decoded alone or in
+    a batch of 5 at other positions, and it agrees with the oracle."""
+    import torch
+    B, H, D, R, N, k, W, m = 5, 128, 512, 64, 3000, 1024, 128, 4
+    qd, qv, cst, cdeq, rst, rdeq, sink = _decode_setup(B, H, D, R, N, W, 4)
+    pos = np.array([m * N + b for b in range(B)], np.int64)
+    pos[2], pos[4] = 77, m * 1000 + 3
+    rng = np.random.default_rng(9)
+    sel = np.full((B, k), -1, np.int32)
+    for b in range(B):
+        nt = int(O.n_visible(pos[b], m, N))
+        pick = np.sort(rng.permutation(nt)[:k])
+        sel[b, : len(pick)] = pick
+    tau = 1.0 / math.sqrt(D)
+    sd, pd, skd = Hx.to_dev(sel), Hx.to_dev(pos), Hx.to_dev(sink)
+    flag = lib.BATCH_INVARIANT
+    # a workspace is given, so without the flag these few-query calls would
+    # split their lists, by counts that follow B
+    ws = torch.empty(max(lib.attn_workspace(1, 1, H, D, N + W), lib.attn_workspace(B, 1, H, D, N + W), 16),
+                     dtype=torch.uint8, device=Hx.dev())
+    out = torch.empty(qd.shape, dtype=torch.bfloat16, device=Hx.dev())
+    lib.sparse_attn_decode(qd, cst, N, sd, k, rst, pd, W, skd, tau, out, flags=flag, ws=ws)
+    outh = torch.empty((B, 1, H, D), dtype=torch.bfloat16, device=Hx.dev())
+    lib.hca_attn(qd[:, None], cst, m, N, pd[:, None], rst, W, skd, tau, outh, flags=lib.WIN_RING | flag, ws=ws)
+    for b in range(B):
+        one = torch.empty_like(out[b:b + 1])
+        lib.sparse_attn_decode(qd[b:b + 1], _seq_store(cst, b), N, sd[b:b + 1], k, _seq_store(rst, b), pd[b:b + 1],
+                               W, skd, tau, one, flags=flag, ws=ws)
+        oneh = torch.empty_like(outh[b:b + 1])
+        lib.hca_attn(qd[b:b + 1, None], _seq_store(cst, b), m, N, pd[b:b + 1, None], _seq_store(rst, b), W, skd,
+                     tau, oneh, flags=lib.WIN_RING | flag, ws=ws)
+        _sync()
+        assert torch.equal(one, out[b:b + 1]), f"CSA decode of sequence {b} depends on the batch"
+        assert torch.equal(oneh, outh[b:b + 1]), f"HCA decode of sequence {b} depends on the batch"
+    got, goth = out.float().cpu().numpy(), outh.float().cpu().numpy()[:, 0]
+    for b in (0, 2, 4):
+        want, _ = O.csa_decode(qv[b], cdeq[b], sel[b], rdeq[b], int(pos[b]), W, sink.astype(np.float64), tau)
+        Hx.check_attn(got[b], want)
+        want, _ = O.hca_decode(qv[b], cdeq[b], m, N, rdeq[b], int(pos[b]), W, sink.astype(np.float64), tau)
+        Hx.check_attn(goth[b], want)
+
+
 def test_decode_step_graph_replays_match_eager(lib):
     """A decode step (indexer top-k over a long list, sparse attention with
     split merge, HCA attention over a ring window) captured in one HIP graph:
