@@ -512,8 +512,9 @@ def test_batch_invariant_decode_is_independent_of_the_batch(lib):
 
 
 def test_decode_step_graph_replays_match_eager(lib):
-    """A decode step (indexer top-k over a long list, sparse attention with
-    split merge, HCA attention over a ring window) captured in one HIP graph:
+    """A decode step (cache maintenance of a new token, indexer top-k over a
+    long list, sparse attention with split merge, HCA attention over a ring
+    window) captured in one HIP graph:
     every replay, with other work and synchronisations between replays,
     equals the eager step bit for bit (the kernels are deterministic and the
     library neither allocates, synchronises nor clears memory inside a call)."""
@@ -532,15 +533,27 @@ def test_decode_step_graph_replays_match_eager(lib):
     aws = torch.empty(max(lib.attn_workspace(B, 1, H, D, k + W), 16), dtype=torch.uint8, device=dev)
     hws = torch.empty(max(lib.attn_workspace(B, 1, H, D, Nh + W), 16), dtype=torch.uint8, device=dev)
     tau = 1.0 / math.sqrt(D)
+    # cache maintenance of a new token: three of the four positions close a block
+    tok = Hx.bf16_dev(synth.tensor(0, "kv", (B, D), rmsnorm=True, layer=9))
+    tail = Hx.bf16_dev(synth.tensor(0, "kv", (B, m, D), rmsnorm=True, layer=10))
+    gate = Hx.to_dev(synth.tensor(0, "gate", (D,), std=0.02).astype(np.float32))
+    bias = Hx.to_dev(synth.tensor(0, "bias", (m,), std=0.02).astype(np.float32))
+    app = lib.alloc_store(B, 4, D, "fp8", R, device=dev)
+    app_win = lib.alloc_store(B, W, D, "fp8", R, device=dev)
+    app_pos = Hx.to_dev(np.array([3, 7, 11, 2], np.int64))
 
     def step():
+        lib.decode_append(tok, app_pos, tail, m, gate, bias, app, app_win, W)
         lib.indexer_topk(qst, wt, kst, N, pos, B, 1, H_I, m, k, sel, iws)
         lib.sparse_attn_decode(qd, cst, N, sel, k, rst, pos, W, sinkt, tau, out, ws=aws)
         lib.hca_attn(qd[:, None], cst, 128, Nh, pos[:, None], rst, W, sinkt, tau, out_h, flags=lib.WIN_RING, ws=hws)
 
+    app.rows.fill_(0)
+    app.scales.fill_(0)
+    app_win.rows.fill_(0)
     step()
     _sync()
-    ref = (sel.clone(), out.clone(), out_h.clone())
+    ref = (sel.clone(), out.clone(), out_h.clone(), app.rows.clone(), app.scales.clone(), app_win.rows.clone())
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -554,10 +567,16 @@ def test_decode_step_graph_replays_match_eager(lib):
         sel.fill_(-9)
         out.zero_()
         out_h.zero_()
+        app.rows.fill_(0)
+        app.scales.fill_(0)
+        app_win.rows.fill_(0)
         _sync()
         g.replay()
         _sync()
         assert torch.equal(sel, ref[0]) and torch.equal(out, ref[1]) and torch.equal(out_h, ref[2]), f"replay {r}"
+        assert torch.equal(app.rows, ref[3]) and torch.equal(app.scales, ref[4]), f"replay {r}: appended entries"
+        assert torch.equal(app_win.rows, ref[5]), f"replay {r}: window rows"
+    assert bool(ref[3][0, 0].any()) and not bool(ref[3][3].any())   # p = 3 closed block 0; p = 2 closed none
 
 
 def test_partial_then_swa_merge_equals_fused(lib):
