@@ -199,43 +199,45 @@ __global__ __launch_bounds__(kAttnThreads) void attn_valu_kernel(AttnArgs a) {
   if (a.lse && p == 0) a.lse[bq * a.H + h] = lse;
 }
 
-// Fixed-order merge of split partials, with the sink.  One workgroup per
-// (query, head): the split weights e^{m_s - M} / Z are formed once, then each
-// thread combines four dims at a time.
+// Fixed-order merge of split partials, with the sink.  One wavefront per
+// (query, head): lane s holds split s's (m_s, l_s), so the maximum and the
+// denominator are wavefront reductions (fixed butterfly order), and each
+// lane combines its dims over the splits in split order.  For D = 512 and at
+// most kMergeRegs splits (the decode shapes) every partial row this lane
+// needs is loaded at the start, in flight together with the statistics.
 constexpr int kMaxSplit = 64;
+constexpr int kMergeRegs = 8;
 
 __global__ __launch_bounds__(64) void attn_split_merge_kernel(AttnArgs a) {
-  __shared__ float s_wt[kMaxSplit];
-  __shared__ float s_lse;
   const int64_t bq = blockIdx.x;
   const int h = blockIdx.y;
   const int D = a.D;
-  const float* wo = a.ws + (bq * a.H + h) * a.nsplit * (int64_t)D;
-  const float* wml = a.ws + (int64_t)a.B * a.Tq * a.H * a.nsplit * D + (bq * a.H + h) * a.nsplit * 2;
-  if (threadIdx.x == 0) {
-    const float sig = (a.partial || !a.sink) ? -INFINITY : a.sink[h];
-    float M = sig;
-    for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, wml[2 * s]);
-    float Z = 0.0f;
-    if (M > -INFINITY) {
-      Z = sig > -INFINITY ? expf(sig - M) : 0.0f;
-      for (int s = 0; s < a.nsplit; ++s)
-        if (wml[2 * s] > -INFINITY) Z += wml[2 * s + 1] * expf(wml[2 * s] - M);
-    }
-    for (int s = 0; s < a.nsplit; ++s)
-      s_wt[s] = (M > -INFINITY && wml[2 * s] > -INFINITY) ? expf(wml[2 * s] - M) / Z : 0.0f;
-    s_lse = M > -INFINITY ? M + logf(Z) : -INFINITY;
+  const int lane = threadIdx.x;
+  const int ns = a.nsplit;
+  const float* wo = a.ws + (bq * a.H + h) * ns * (int64_t)D;
+  const float* wml = a.ws + (int64_t)a.B * a.Tq * a.H * ns * D + (bq * a.H + h) * ns * 2;
+  const bool regs = D == 8 * kWave && ns <= kMergeRegs;          // uniform
+  float4 v[kMergeRegs][2];
+  if (regs) {
+#pragma unroll
+    for (int s = 0; s < kMergeRegs; ++s)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)   // unused splits re-read split 0 (ignored): every load goes out
+        v[s][c] = *(const float4*)(wo + (int64_t)(s < ns ? s : 0) * D + 4 * lane + 4 * kWave * c);
   }
-  __syncthreads();
+  const float m_s = lane < ns ? wml[2 * lane] : -INFINITY;
+  const float l_s = lane < ns ? wml[2 * lane + 1] : 0.0f;
+  const float sig = (a.partial || !a.sink) ? -INFINITY : a.sink[h];
+  const float M = fmaxf(wave_max(m_s), sig);
+  float Z = 0.0f, w_s = 0.0f;
+  if (M > -INFINITY) {                                            // uniform
+    const float e_s = m_s > -INFINITY ? expf(m_s - M) : 0.0f;
+    Z = wave_sum(l_s * e_s) + (sig > -INFINITY ? expf(sig - M) : 0.0f);
+    w_s = e_s / Z;
+  }
+  const float lse = M > -INFINITY ? M + logf(Z) : -INFINITY;
   const int64_t qoff = (bq * a.H + h) * (int64_t)D;
-  for (int d = 4 * threadIdx.x; d < D; d += 4 * blockDim.x) {
-    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-    for (int s = 0; s < a.nsplit; ++s) {
-      const float w = s_wt[s];
-      const float4 v = *(const float4*)(wo + (int64_t)s * D + d);
-      acc.x = fmaf(v.x, w, acc.x); acc.y = fmaf(v.y, w, acc.y);
-      acc.z = fmaf(v.z, w, acc.z); acc.w = fmaf(v.w, w, acc.w);
-    }
+  auto store4 = [&](int d, const float4& acc) {
     if (a.out_f32) {
       *(float4*)((float*)a.out + qoff + d) = acc;
     } else {
@@ -244,8 +246,34 @@ __global__ __launch_bounds__(64) void attn_split_merge_kernel(AttnArgs a) {
       w.y = f32_to_bf16(acc.z) | (f32_to_bf16(acc.w) << 16);
       *(uint2*)((uint16_t*)a.out + qoff + d) = w;
     }
+  };
+  if (regs) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+      for (int s = 0; s < kMergeRegs; ++s) {
+        const float w = __shfl(w_s, s);
+        if (s < ns) {                                             // uniform; no early exit, so v stays in registers
+          acc.x = fmaf(v[s][c].x, w, acc.x); acc.y = fmaf(v[s][c].y, w, acc.y);
+          acc.z = fmaf(v[s][c].z, w, acc.z); acc.w = fmaf(v[s][c].w, w, acc.w);
+        }
+      }
+      store4(4 * lane + 4 * kWave * c, acc);
+    }
+  } else {
+    for (int d = 4 * lane; d < D; d += 4 * kWave) {
+      float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      for (int s = 0; s < ns; ++s) {
+        const float w = __shfl(w_s, s);
+        const float4 x = *(const float4*)(wo + (int64_t)s * D + d);
+        acc.x = fmaf(x.x, w, acc.x); acc.y = fmaf(x.y, w, acc.y);
+        acc.z = fmaf(x.z, w, acc.z); acc.w = fmaf(x.w, w, acc.w);
+      }
+      store4(d, acc);
+    }
   }
-  if (a.lse && threadIdx.x == 0) a.lse[bq * a.H + h] = s_lse;
+  if (a.lse && lane == 0) a.lse[bq * a.H + h] = lse;
 }
 
 // ------------------------------------------------------------ host side
