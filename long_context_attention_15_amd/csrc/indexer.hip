@@ -1442,20 +1442,23 @@ __global__ __launch_bounds__(kIdxThreads) void idx_long_final_kernel(IdxArgs a) 
   __shared__ uint32_t s_pre[kIdxThreads + 1];
   const int tid = threadIdx.x;
   const int64_t bq = blockIdx.x;
+  uint8_t* wq = a.ws + bq * a.per_query;
+  const uint32_t* counts = (const uint32_t*)(wq + a.off_counts);
+  const uint2* region = (const uint2*)(wq + a.off_region);
+  // the count load goes out together with the position load (the counts are
+  // workspace memory, readable whatever nt turns out to be)
+  const uint32_t cnt_ld = tid < a.nseg ? counts[tid] : 0u;
   const int64_t nt = idx_visible(a, bq);
   int32_t* out = a.sel + bq * a.k;
   if (nt <= a.k) {
     for (int i = tid; i < a.k; i += kIdxThreads) out[i] = i < nt ? i : -1;
     return;
   }
-  uint8_t* wq = a.ws + bq * a.per_query;
-  const uint32_t* counts = (const uint32_t*)(wq + a.off_counts);
-  const uint2* region = (const uint2*)(wq + a.off_region);
   // segment offsets in the concatenated candidate list (nseg <= kIdxThreads;
   // s_pre[s] for every s <= kIdxThreads, so that segment s holds s_pre[s+1]
   // - s_pre[s] candidates)
   const int lane = tid % kWave, wave = tid / kWave;
-  const uint32_t cnt_mine = tid < a.nseg ? counts[tid] : 0u;
+  const uint32_t cnt_mine = cnt_ld;
   const uint32_t incl = wave_scan<0>(cnt_mine);
   if (lane == kWave - 1) sh.wtot[0][wave] = incl;
   __syncthreads();
