@@ -325,6 +325,52 @@ def test_indexer_long_list_exact_ties(lib, N, k):
             assert np.array_equal(sel[b, i], want), f"sequence {b} query {i}"
 
 
+def test_indexer_long_lists_many_rounds_of_workgroups(lib):
+    """The one-pass long-list path with 255 queries of 8 chunks each (2040
+    workgroups, several rounds of the resident slots): the chunks of a query
+    wait for one another, which must neither stall nor lose candidates when
+    most of the grid is not resident.  Keys are random FP8 codes made on the
+    device; three queries are checked against the oracle, every query's
+    selection for validity (ascending, distinct, visible)."""
+    import torch
+    from oracle import codec
+    B, N, H_I, d_I, m, k = 255, 60000, 8, 64, 4, 512
+    gen = torch.Generator(device=Hx.dev())
+    gen.manual_seed(17)
+
+    def codes(shape):
+        c = torch.randint(0, 256, shape, generator=gen, device=Hx.dev(), dtype=torch.int32)
+        c = torch.where((c & 0x7F) == 0x7F, c - 1, c)          # no NaN codes
+        return c.to(torch.uint8)
+
+    krows = codes((B, N, d_I))
+    qrows = codes((B, H_I, d_I))
+    ksc = torch.full((B, N), 2.0 ** -4, dtype=torch.float32, device=Hx.dev())
+    qsc = torch.full((B, H_I), 2.0 ** -3, dtype=torch.float32, device=Hx.dev())
+    w = (torch.randn((B, 1, H_I), generator=gen, device=Hx.dev()) * 0.5).contiguous()
+    kst = lib.Store(krows, ksc, N, d_I, 0, lib.FP8_E4M3)
+    qst = lib.Store(qrows, qsc, H_I, d_I, 0, lib.FP8_E4M3)
+    pos = np.array([m * N - 1 - 7 * (b % 5) for b in range(B)], np.int64)
+    sel = torch.full((B, 1, k), -7, dtype=torch.int32, device=Hx.dev())
+    ws = torch.empty(max(lib.indexer_topk_workspace(B, 1, N, k), 16), dtype=torch.uint8, device=Hx.dev())
+    lib.indexer_topk(qst, w, kst, N, Hx.to_dev(pos), B, 1, H_I, m, k, sel, ws)
+    _sync()
+    got = sel[:, 0].cpu().numpy()
+    for b in range(B):
+        nt = int(O.n_visible(int(pos[b]), m, N))
+        row = got[b]
+        assert np.all(row[:k] >= 0) and np.all(row < nt) and np.all(np.diff(row) > 0), f"query {b}"
+    flips = 0
+    for b in (0, 128, 254):
+        nt = int(O.n_visible(int(pos[b]), m, N))
+        kv = codec.e4m3_decode(krows[b, :nt].cpu().numpy()) * 2.0 ** -4
+        qv = codec.e4m3_decode(qrows[b].cpu().numpy()) * 2.0 ** -3
+        wv = w[b, 0].cpu().numpy().astype(np.float64)
+        s_ = O.indexer_scores(qv, wv, kv)
+        flips += Hx.check_topk(got[b], s_, k, Hx.score_error_bound(qv, wv, kv))
+    assert flips <= 2
+
+
 def test_indexer_no_visible_entries_and_k_above_count(lib):
     B, T, N, H_I, d_I, m, k = 1, 40, 10, 2, 64, 4, 16
     kst, kdeq, qst, qdeq, w = _indexer_inputs(B, T, N, H_I, d_I, "fp8", seed_shift=2)
