@@ -1,11 +1,14 @@
-// Block compression + quantisation (csa_compress_kv).
+// Block compression + quantisation (csa_compress_kv, csa_decode_append).
 //
 // One wavefront per output entry.  Lane l owns VPL contiguous dims
 // [l*VPL, l*VPL + VPL), so a row of 512 bf16 is one 16-byte load per lane.
 // Pass 1 computes the m logits <x_i, gate> + bias_i (wave reductions), the
 // softmax weights are formed in LDS, pass 2 accumulates sum_i alpha_i x_i in
 // fixed order (the rows of pass 1 are still in L2), then the row is quantised
-// and written.  HBM traffic: the tokens once plus the stored rows.
+// and written; both passes load the block's rows kRowBatch at a time.  HBM
+// traffic: the tokens once plus the stored rows.  The same entry code
+// (compress_entry, store_entry) serves decode-time appends, so their bytes
+// equal prefill's; m = 1 takes the packed quantiser quant_rows_kernel.
 #include "common.h"
 #include "launch.h"
 
