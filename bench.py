@@ -246,6 +246,24 @@ class Decode1M:
                                                              flags=c.WIN_RING, ws=self.aws)))
         return o
 
+    def unfused_window_ops(self):
+        """The step's CSA attention as the pages' two-part form: attention over
+        the selected entries only (CSA_ATTN_PARTIAL: float32 partial + LSE),
+        then swa_merge adds the window and the sink (the step fuses both)."""
+        import torch
+        c = self.csa
+        if not hasattr(self, "part_o"):
+            self.part_o = torch.empty(self.q.shape, dtype=torch.float32, device="cuda")
+            self.part_lse = torch.empty(self.q.shape[:2], dtype=torch.float32, device="cuda")
+            self.out_m = torch.empty_like(self.q)
+        return [
+            ("csa_sparse_attn_decode(partial)", lambda: c.sparse_attn_decode(
+                self.q, self.ckv, self.N, self.sel, self.k, self.ring, self.pos, self.W, self.sink, self.tau,
+                self.part_o, lse=self.part_lse, flags=c.ATTN_PARTIAL, ws=self.aws)),
+            ("swa_merge", lambda: c.swa_merge(self.q[:, None], self.ring, self.pos[:, None], self.W, c.WIN_RING,
+                                              self.part_o, self.part_lse, self.sink, self.tau, self.out_m[:, None])),
+        ]
+
     def invariant_ops(self):
         """The step's attention with CSA_BATCH_INVARIANT (no split lists)."""
         c = self.csa
@@ -498,6 +516,9 @@ def main():
             _, per_close = time_ops(d.append_ops(d.pos_close_m, d.pos_close_mh), args.decode_steps, 2, flush=d.flush)
             dec[name]["append_us"] = {n: v * 1e3 for n, v in per_app.items()}
             dec[name]["append_block_close_us"] = {n: v * 1e3 for n, v in per_close.items()}
+            # row a7 on its own: partial attention + swa_merge (window and sink)
+            _, per_sw = time_ops(d.unfused_window_ops(), args.decode_steps, 2, flush=d.flush)
+            dec[name]["unfused_window_us"] = {n: v * 1e3 for n, v in per_sw.items()}
             # the attention with batch-invariant results (no split lists)
             _, per_inv = time_ops(d.invariant_ops(), args.decode_steps, 2, flush=d.flush)
             dec[name]["batch_invariant_attn_us"] = {n: v * 1e3 for n, v in per_inv.items()}

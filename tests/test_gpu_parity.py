@@ -488,6 +488,38 @@ def test_csa_decode_parity(lib):
         Hx.check_attn(got[b], want)
 
 
+def test_decode_partial_then_ring_swa_merge_equals_fused(lib):
+    """The two-part form of a decode step (attention over the selected entries
+    only, then swa_merge over the ring window with the sink) agrees with the
+    fused decode and with the oracle."""
+    import torch
+    B, H, D, R, N, k, W, m = 3, 128, 512, 64, 4000, 1024, 128, 4
+    qd, qv, cst, cdeq, rst, rdeq, sink = _decode_setup(B, H, D, R, N, W, 5)
+    pos = np.array([m * N + 1, m * N - 9, 70], np.int64)
+    rng = np.random.default_rng(8)
+    sel = np.full((B, k), -1, np.int32)
+    for b in range(B):
+        nt = int(O.n_visible(pos[b], m, N))
+        pick = np.sort(rng.permutation(nt)[:k])
+        sel[b, : len(pick)] = pick
+    ws = torch.empty(max(lib.attn_workspace(B, 1, H, D, k + W), 16), dtype=torch.uint8, device=Hx.dev())
+    tau = 1.0 / math.sqrt(D)
+    sd, pd, skd = Hx.to_dev(sel), Hx.to_dev(pos), Hx.to_dev(sink)
+    fused = torch.empty(qd.shape, dtype=torch.bfloat16, device=Hx.dev())
+    lib.sparse_attn_decode(qd, cst, N, sd, k, rst, pd, W, skd, tau, fused, ws=ws)
+    part = torch.empty(qd.shape, dtype=torch.float32, device=Hx.dev())
+    plse = torch.empty((B, H), dtype=torch.float32, device=Hx.dev())
+    lib.sparse_attn_decode(qd, cst, N, sd, k, rst, pd, W, skd, tau, part, lse=plse, flags=lib.ATTN_PARTIAL, ws=ws)
+    out = torch.empty((B, 1, H, D), dtype=torch.bfloat16, device=Hx.dev())
+    lib.swa_merge(qd[:, None], rst, pd[:, None], W, lib.WIN_RING, part, plse, skd, tau, out)
+    _sync()
+    got, ref = out[:, 0].float().cpu().numpy(), fused.float().cpu().numpy()
+    Hx.check_attn(got, ref)
+    for b in range(B):
+        want, _ = O.csa_decode(qv[b], cdeq[b], sel[b], rdeq[b], int(pos[b]), W, sink.astype(np.float64), tau)
+        Hx.check_attn(got[b], want)
+
+
 def test_hca_decode_parity(lib):
     import torch
     B, H, D, R, N, W, m = 3, 128, 512, 64, 300, 128, 128
