@@ -436,3 +436,86 @@ def test_decode_append_equals_prefill_compression_and_keeps_the_last_window():
     # m' = 128 blocks: none closes before position 127; the window is the last W of the steps
     e2, w2 = O.decode_append(x, g, b, 128, W, 0, T)
     assert e2 == {} and sorted(w2.values()) == list(range(T - W, T))
+
+
+# ------------------------------------------------------------ MXFP4 pins
+def _mx_golden():
+    return json.load(open(os.path.join(GOLDEN, "mxfp4_blocks.json")))
+
+
+def test_mxfp4_decode_hand_worked_blocks():
+    """OCP MX v1.0 decode of hand-worked blocks: an E8M0 byte e is exactly
+    2^(e-127) and each element is its E2M1 table value times that scale
+    (a bias of 128 or a wrong table entry fails here)."""
+    for blk in _mx_golden()["decode_blocks"]:
+        codes = np.array(blk["codes"], dtype=np.uint8)[None, :]
+        got = codec.mxfp4_decode(codes, np.array([[blk["e8m0"]]], dtype=np.uint8))[0]
+        if "values" in blk:
+            want = np.array(blk["values"], dtype=np.float64)
+        else:
+            want = np.array([math.ldexp(v, blk["values_exp2"]) for v in blk["values_mant"]])
+        assert np.array_equal(got, want), blk["note"]
+        assert np.array_equal(np.signbit(got), np.signbit(want)), blk["note"]
+
+
+def test_mxfp4_row_packing_puts_element_2i_in_the_low_nibble():
+    """The stored MXFP4 row layout: byte i holds element 2i in its low nibble
+    and element 2i+1 in its high nibble; one E8M0 byte per 32 elements (a
+    nibble swap or a per-block scale mix-up fails here)."""
+    row = _mx_golden()["packed_row"]
+    v = np.array(row["values"], dtype=np.float64)[None, :]
+    packed, e8 = O.pack_rows(v, "mxfp4")
+    assert packed.tolist() == [row["bytes"]]
+    assert e8.tolist() == [row["e8m0"]]
+    back = O.unpack_rows(np.array([row["bytes"]], np.uint8), np.array([row["e8m0"]], np.uint8), "mxfp4", 64)
+    assert np.array_equal(back, v)
+
+
+def test_mxfp4_round_trip_is_the_nearest_scaled_e2m1_value():
+    """decode(encode(x)) is, element by element, the nearest value of
+    {+-2^E v : v an E2M1 magnitude} with E the block's shared exponent found
+    by brute force (largest E with 2^(E+2) <= amax), ties to the even code,
+    saturating at 6 * 2^E."""
+    rng = np.random.default_rng(61)
+    x = (rng.normal(0, 1, (24, 64)) * rng.lognormal(0, 2, (24, 1))).astype(np.float32).astype(np.float64)
+    x[3, :32] = 0.0                                   # an all-zero block
+    x[5, 7] = -0.0
+    codes, e8 = codec.mxfp4_encode(x)
+    got = codec.mxfp4_decode(codes, e8)
+    mags = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    for r in range(x.shape[0]):
+        for blk in range(2):
+            seg = x[r, 32 * blk: 32 * blk + 32]
+            amax = float(np.max(np.abs(seg)))
+            if amax == 0.0:
+                E = -127
+            else:
+                E = -300
+                while 2.0 ** (E + 1 + 2) <= amax:
+                    E += 1
+            for i in range(32):
+                a = abs(seg[i]) / 2.0 ** E
+                best = min(range(8), key=lambda c: (abs(mags[c] - a), c & 1))
+                want = math.copysign(mags[best] * 2.0 ** E, seg[i])
+                assert got[r, 32 * blk + i] == want, (r, blk, i)
+
+
+def test_kv_cache_is_about_two_percent_of_a_bf16_gqa8_cache():
+    """kenelite analysis section 8: at long context the KV cache is about 2 % of
+    a BF16 GQA-8, head-dim-128 cache.  Per token and per layer pair (CSA and
+    HCA alternate: llm-tech overview) this layout stores a CSA entry (576-byte
+    row + 4-byte scale) and an indexer key (64 FP8 + 4-byte scale) every m = 4
+    tokens and an HCA entry every m' = 128 tokens; the sliding windows are a
+    fixed 128 rows per layer and vanish per token at 1M."""
+    g = json.load(open(os.path.join(GOLDEN, "page_constants.json")))
+    assert g["csa_hca_alternate"]["value"] is True
+    base = g["kv_cache_vs_bf16_gqa8_hd128"]["baseline"]
+    bf16_per_layer = 2 * base["kv_heads"] * base["head_dim"] * base["bytes_per_value"]    # K and V
+    m, mh = g["csa_block_m"]["value"], g["hca_block_m_prime"]["value"]
+    entry = O.row_bytes("fp8", 512, 64) + 4
+    key = O.row_bytes("fp8", 64, 0) + 4
+    T, W = 1 << 20, g["sliding_window"]["value"]
+    csa = (T // m) * (entry + key) + W * entry
+    hca = (T // mh) * entry + W * entry
+    ratio = (csa + hca) / (2 * T * bf16_per_layer)
+    assert abs(ratio - g["kv_cache_vs_bf16_gqa8_hd128"]["value_approx"]) < 0.005, ratio
