@@ -26,6 +26,8 @@
  *     writes nothing; a failed launch returns CSA_EHIP.  csa_last_error()
  *     gives a message for the last failure on the calling thread.
  *   - Results are deterministic: fixed reduction orders, no float atomics.
+ *   - Query, output and partial-result arrays of the attention entry points
+ *     (q, out, part_out) must be 16-byte aligned; lse arrays 4-byte aligned.
  *   - Positions: a prefill query row t has position t.  A query at position
  *     t sees compressed entry j iff (j+1)*m - 1 <= t, i.e. the first
  *     n_t = min(n_entries, floor((t+1)/m)) entries, and the window positions
@@ -93,6 +95,14 @@ typedef struct {
                                only, whatever else is in the batch (the
                                default splits few-query calls to fill the
                                chip, and the split count follows B)          */
+
+/* diagnostic event counters (csa_diag_counters) */
+#define CSA_DIAG_INDEXER_GIVEUPS 0      /* one-pass long-list indexer workgroups that
+                                           stopped waiting for their query's other
+                                           chunks and kept every key as a candidate   */
+#define CSA_DIAG_INDEXER_WIDE_SELECT 1  /* final selections over more candidates than
+                                           fit in LDS (heavy ties, or the above)      */
+#define CSA_DIAG_COUNT 4
 
 const char* csa_version(void);
 const char* csa_status_string(int status);
@@ -239,6 +249,24 @@ csa_status swa_merge(const void* q, int q_fmt, int B, int Tq, int H, csa_store w
                      const int64_t* q_pos, int W, int flags, const float* part_out,
                      const float* part_lse, const float* sink, float sm_scale, void* out,
                      hipStream_t stream);
+
+/*
+ * csa_diag_counters -- diagnostics for tests and benchmarks.
+ * Copies min(n, CSA_DIAG_COUNT) event counters of the current device into
+ * the HOST array out (uint64) and, if reset != 0, clears them.  Synchronises
+ * the device first (not for use inside stream capture).  The counted events
+ * leave results exact; they only cost time.
+ *
+ * Environment switches, read at each call of the entry points:
+ *   CSA_INDEXER_SPIN_LIMIT=n  (0 <= n <= 65536) the number of polls a
+ *       one-pass long-list indexer workgroup spends waiting for its query's
+ *       other chunks before it stops waiting (default 65536); 0 makes every
+ *       workgroup stop at once.  For tests of that path.
+ *   CSA_DEBUG_SYNC=1  every entry point synchronises its stream after
+ *       enqueueing and reports an asynchronous kernel failure as CSA_EHIP
+ *       (not for use inside stream capture).
+ */
+csa_status csa_diag_counters(uint64_t* out, int n, int reset);
 
 #ifdef __cplusplus
 }

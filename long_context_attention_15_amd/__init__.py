@@ -53,6 +53,7 @@ _SIGS = {
                                 _SZ, _P], _I),
     "hca_attn": ([_P, _I, _I, _I, _I, _CStore, _I, _I64, _P, _CStore, _I, _P, _F, _P, _P, _I, _P, _SZ, _P], _I),
     "swa_merge": ([_P, _I, _I, _I, _I, _CStore, _P, _I, _I, _P, _P, _P, _F, _P, _P], _I),
+    "csa_diag_counters": ([_P, _I, _I], _I),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -145,6 +146,16 @@ def alloc_store(B: int, cap: int, dim: int, fmt, rope: int = 0, device="cuda") -
     else:
         scales = None
     return Store(rows, scales, cap, dim, rope, fmt)
+
+
+DIAG_INDEXER_GIVEUPS, DIAG_INDEXER_WIDE_SELECT, DIAG_COUNT = 0, 1, 4
+
+
+def diag_counters(reset: bool = False):
+    """csa_diag_counters: the device's diagnostic event counters (synchronises the device)."""
+    buf = (ctypes.c_uint64 * DIAG_COUNT)()
+    _check(load().csa_diag_counters(ctypes.cast(buf, ctypes.c_void_p), DIAG_COUNT, int(reset)), "csa_diag_counters")
+    return [int(v) for v in buf]
 
 
 # ------------------------------------------------------------- entry points

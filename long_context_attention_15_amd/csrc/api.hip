@@ -3,6 +3,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 #include "common.h"
@@ -23,6 +24,19 @@ csa_status fail(csa_status st, const char* fmt, ...) {
 csa_status hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return CSA_OK;
   return fail(CSA_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// CSA_DEBUG_SYNC=1: synchronise the stream after a launch and report any
+// asynchronous failure of the enqueued kernels.
+csa_status launched(hipError_t e, hipStream_t stream, const char* what) {
+  if (e != hipSuccess) return hip_status(e, what);
+  const char* dbg = getenv("CSA_DEBUG_SYNC");
+  if (dbg && dbg[0] == '1') {
+    e = hipStreamSynchronize(stream);
+    if (e == hipSuccess) e = hipGetLastError();
+    if (e != hipSuccess) return fail(CSA_EHIP, "%s (CSA_DEBUG_SYNC): %s", what, hipGetErrorString(e));
+  }
+  return CSA_OK;
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -71,7 +85,8 @@ csa_status check_q(const void* q, int q_fmt, int H, int dim, const void* out) {
   if (!q) return fail(CSA_EINVAL, "q is NULL");
   if (!out) return fail(CSA_EINVAL, "out is NULL");
   if (q_fmt != CSA_F32 && q_fmt != CSA_BF16) return fail(CSA_EUNSUPPORTED, "q_fmt must be CSA_F32 or CSA_BF16");
-  if (!aligned(q, 4) || !aligned(out, 4)) return fail(CSA_EINVAL, "q and out must be 4-byte aligned");
+  // the MFMA kernel moves q and out rows with 16-byte accesses
+  if (!aligned(q, 16) || !aligned(out, 16)) return fail(CSA_EINVAL, "q and out must be 16-byte aligned");
   if (H < 1) return fail(CSA_EINVAL, "H < 1");
   if (!csa::attn_supported(H, dim)) return fail(CSA_EUNSUPPORTED, "H = %d with dim = %d is not supported", H, dim);
   return CSA_OK;
@@ -116,8 +131,8 @@ csa_status csa_compress_kv(const void* tok, int tok_fmt, int B, int64_t T, int64
     return fail(CSA_EUNSUPPORTED, "rope_dim must be a multiple of dim / 64");
   if (out.fmt == CSA_MXFP4 && out.dim > 64) return fail(CSA_EUNSUPPORTED, "MXFP4 output needs dim <= 64");
   if (out_row0 < 0 || out_row0 + T / m > out.cap) return fail(CSA_EINVAL, "out_row0 + floor(T/m) > out.cap");
-  return hip_status(csa::launch_compress(tok, tok_fmt, B, T, tok_bstride, m, gate, bias, out, out_row0, stream),
-                    "csa_compress_kv launch");
+  return launched(csa::launch_compress(tok, tok_fmt, B, T, tok_bstride, m, gate, bias, out, out_row0, stream), stream,
+                  "csa_compress_kv launch");
 }
 
 csa_status csa_decode_append(const void* tok, int tok_fmt, int B, const int64_t* pos, void* tail, int tail_rows,
@@ -142,8 +157,8 @@ csa_status csa_decode_append(const void* tok, int tok_fmt, int B, const int64_t*
     if (win.fmt == CSA_FP8_E4M3 && win.rope_dim % vpl != 0)
       return fail(CSA_EUNSUPPORTED, "win.rope_dim must be a multiple of dim / 64");
   }
-  return hip_status(csa::launch_decode_append(tok, tok_fmt, B, pos, tail, tail_rows, m, gate, bias, out, win, W, stream),
-                    "csa_decode_append launch");
+  return launched(csa::launch_decode_append(tok, tok_fmt, B, pos, tail, tail_rows, m, gate, bias, out, win, W, stream),
+                  stream, "csa_decode_append launch");
 }
 
 size_t csa_indexer_topk_workspace(int B, int Tq, int64_t n_entries, int k) {
@@ -174,9 +189,9 @@ csa_status csa_indexer_topk(csa_store q_idx, const float* head_w, csa_store keys
   if (plan.ws > 0 && (!ws || ws_bytes < plan.ws))
     return fail(CSA_EWORKSPACE, "workspace of %zu bytes needed, %zu given", plan.ws, ws ? ws_bytes : (size_t)0);
   if (plan.ws > 0 && !aligned(ws, 16)) return fail(CSA_EINVAL, "ws must be 16-byte aligned");
-  return hip_status(csa::launch_indexer(q_idx, head_w, keys, n_entries, q_pos, B, Tq, H_I, m, k, sel, ws, plan,
-                                        stream),
-                    "csa_indexer_topk launch");
+  return launched(csa::launch_indexer(q_idx, head_w, keys, n_entries, q_pos, B, Tq, H_I, m, k, sel, ws, plan,
+                                      stream),
+                  stream, "csa_indexer_topk launch");
 }
 
 size_t csa_attn_workspace(int B, int Tq, int H, int dim, int64_t max_list) {
@@ -200,7 +215,7 @@ static csa_status run_attn(csa::AttnCall& c, int flags, hipStream_t stream, cons
     return fail(CSA_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, c.ws_bytes);
   if (need > 0 && c.ws && !aligned(c.ws, 16)) return fail(CSA_EINVAL, "ws must be 16-byte aligned");
   c.allow_split = need > 0 && c.ws != nullptr && !(flags & CSA_BATCH_INVARIANT);
-  return hip_status(csa::launch_attn(c, stream), what);
+  return launched(csa::launch_attn(c, stream), stream, what);
 }
 
 static csa::AttnCall base_call(const void* q, int q_fmt, int B, int Tq, int H, int D, float sm_scale,
@@ -287,6 +302,7 @@ csa_status swa_merge(const void* q, int q_fmt, int B, int Tq, int H, csa_store w
   if (win.fmt == CSA_MXFP4) return fail(CSA_EUNSUPPORTED, "window rows must be F32 or FP8");
   CSA_TRY(check_q(q, q_fmt, H, win.dim, out));
   if (!part_out || !part_lse) return fail(CSA_EINVAL, "part_out and part_lse must be non-NULL");
+  if (!aligned(part_out, 16) || !aligned(part_lse, 4)) return fail(CSA_EINVAL, "part_out must be 16-byte aligned");
   const bool ring = (flags & CSA_WIN_RING) != 0;
   if (ring && !q_pos) return fail(CSA_EINVAL, "CSA_WIN_RING needs q_pos");
   if (W > 0 && ring && win.cap < W) return fail(CSA_EINVAL, "win.cap < W");
@@ -295,6 +311,12 @@ csa_status swa_merge(const void* q, int q_fmt, int B, int Tq, int H, csa_store w
   c.mode = csa::kModeNone; c.win = win; c.W = W; c.ring = ring; c.q_pos = q_pos;
   c.prior_o = part_out; c.prior_lse = part_lse;
   return run_attn(c, flags, stream, "swa_merge launch");
+}
+
+csa_status csa_diag_counters(uint64_t* out, int n, int reset) {
+  g_err[0] = 0;
+  if (!out || n < 0) return fail(CSA_EINVAL, "out is NULL or n < 0");
+  return hip_status(csa::diag_counters(out, n, reset != 0), "csa_diag_counters");
 }
 
 }  // extern "C"

@@ -602,11 +602,13 @@ __global__ __launch_bounds__(kMThreads, 1) void attn_mfma_kernel(MfmaArgs a) {
   }
 }
 
-// The MFMA kernel masks empty slots through a -1e30 logit, which needs a
-// positive softmax scale; other scales take the general kernel.
+// The MFMA kernel masks empty slots through a -1e30 logit: the scaled logit
+// of an empty slot (about -1e30 tau log2 e in base 2) must lie far below
+// anything exp2 can resolve, so the kernel takes scales above 1e4 / (1e30
+// log2 e) only; other scales (tiny, zero or negative) take the general kernel.
 bool attn_mfma_eligible(int q_fmt, int H, int D, const csa_store& kv, bool has_prior, float tau) {
-  return !has_prior && tau > 0.0f && q_fmt == CSA_BF16 && D == kMD && H % 64 == 0 && kv.fmt == CSA_FP8_E4M3 &&
-         kv.row_bytes == kRawRow;
+  return !has_prior && tau * kLog2e * 1.0e30f >= 1.0e4f && q_fmt == CSA_BF16 && D == kMD && H % 64 == 0 &&
+         kv.fmt == CSA_FP8_E4M3 && kv.row_bytes == kRawRow;
 }
 
 hipError_t launch_attn_mfma(const AttnCall& c, int nsplit, int split_len, hipStream_t st) {

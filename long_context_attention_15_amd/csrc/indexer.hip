@@ -8,6 +8,8 @@
 // each chunk emits its local top-k as candidates and a merge kernel selects
 // the final top-k from the candidates (the candidate list is in ascending
 // index order, so position order is index order for the tie rule).
+#include <cstdlib>
+
 #include "common.h"
 #include "launch.h"
 
@@ -232,7 +234,14 @@ struct IdxArgs {
   uint8_t* ws;
   size_t per_query, off_scores, off_uni, off_region, off_counts, off_skey, off_sidx, off_ctr;
   int lm, nseg, rstride;   // rstride: entries between consecutive candidate regions
+  int spin_max;            // one-pass long lists: polls before a workgroup stops waiting
 };
+
+// Diagnostic event counters of this device (read and cleared by
+// csa_diag_counters): one-pass indexer workgroups that stopped waiting for
+// their query's other chunks, and final selections that took the
+// many-candidate path.  One atomic add per event; events are rare.
+__device__ unsigned long long g_diag[CSA_DIAG_COUNT];
 
 // visible entries of query bq
 __device__ __forceinline__ int64_t idx_visible(const IdxArgs& a, int64_t bq) {
@@ -1304,7 +1313,7 @@ __global__ __launch_bounds__(kIdxThreads) void idx_long_compact_kernel(IdxArgs a
 // workgroup that gives up takes T = 0 (all its keys become candidates),
 // which keeps the selection exact, only slower.  kLFusedMaxChunks <= 2 x 64
 // (one polling wavefront, two slots per lane).
-constexpr int kLSpinMax = 1 << 16;   // polls of the arrival counter (tens of milliseconds)
+constexpr int kLSpinMax = 1 << 16;   // default polls of the chunk slots (tens of milliseconds)
 constexpr int kLParts = kIdxThreads / kLSets;   // threads per strided set in the set maxima
 static_assert(kLParts * kLSets == kIdxThreads && kLSets == 2 * kWave, "set maxima layout");
 
@@ -1388,7 +1397,7 @@ __global__ __launch_bounds__(kIdxThreads) void idx_long_fused_kernel(IdxArgs a) 
     const int nact = (int)((nt + a.chunk - 1) / a.chunk);
     uint32_t t = 0u;
     bool all = false;
-    for (int it = 0; !all && it < kLSpinMax; ++it) {
+    for (int it = 0; !all && it < a.spin_max; ++it) {
       const uint64_t s0 = lane < nact ? __hip_atomic_load(slots + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                                       : ((uint64_t)1 << 32) | 0xffffffffu;
       const uint64_t s1 = lane + kWave < nact
@@ -1402,7 +1411,10 @@ __global__ __launch_bounds__(kIdxThreads) void idx_long_fused_kernel(IdxArgs a) 
         __builtin_amdgcn_s_sleep(16);
       }
     }
-    if (lane == 0) s_T = all ? t : 0u;
+    if (lane == 0) {
+      s_T = all ? t : 0u;
+      if (!all) atomicAdd(&g_diag[CSA_DIAG_INDEXER_GIVEUPS], 1ull);
+    }
   }
   __syncthreads();
   const uint32_t T = use_t ? s_T : 0u;
@@ -1490,7 +1502,8 @@ __global__ __launch_bounds__(kIdxThreads) void idx_long_final_kernel(IdxArgs a) 
     emit_selected(s_cand, ncand, thr, need_eq, sh, [&](int pos, int rank) { out[rank] = s_cidx[pos]; });
     return;
   }
-  // many candidates (heavy ties): concatenated in the workspace
+  // many candidates (heavy ties, or chunks that stopped waiting): concatenated in the workspace
+  if (tid == 0) atomicAdd(&g_diag[CSA_DIAG_INDEXER_WIDE_SELECT], 1ull);
   uint32_t* skey = (uint32_t*)(wq + a.off_skey);
   int32_t* sidx = (int32_t*)(wq + a.off_sidx);
   for (int sg = 0; sg < a.nseg; ++sg) {
@@ -1508,6 +1521,32 @@ __global__ __launch_bounds__(kIdxThreads) void idx_long_final_kernel(IdxArgs a) 
 }
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Wait budget of the one-pass long-list indexer: kLSpinMax polls, or the
+// value of CSA_INDEXER_SPIN_LIMIT (>= 0) for tests of the path a workgroup
+// takes when it stops waiting (0: every workgroup takes it at once).
+static int indexer_spin_limit() {
+  const char* e = getenv("CSA_INDEXER_SPIN_LIMIT");
+  if (!e || !*e) return kLSpinMax;
+  char* end = nullptr;
+  const long v = strtol(e, &end, 10);
+  return (end && *end == 0 && v >= 0 && v <= kLSpinMax) ? (int)v : kLSpinMax;
+}
+
+hipError_t diag_counters(uint64_t* out, int n, bool reset) {
+  unsigned long long h[CSA_DIAG_COUNT];
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return e;
+  e = hipMemcpyFromSymbol(h, HIP_SYMBOL(g_diag), sizeof(h), 0, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return e;
+  for (int i = 0; i < n && i < CSA_DIAG_COUNT; ++i) out[i] = h[i];
+  if (reset) {
+    unsigned long long z[CSA_DIAG_COUNT] = {};
+    e = hipMemcpyToSymbol(HIP_SYMBOL(g_diag), z, sizeof(z), 0, hipMemcpyHostToDevice);
+    if (e == hipSuccess) e = hipDeviceSynchronize();
+  }
+  return e;
+}
 
 IdxPlan indexer_plan(int B, int Tq, int64_t n_entries, int k) {
   IdxPlan p{};
@@ -1611,6 +1650,7 @@ hipError_t launch_indexer(const csa_store& qidx, const float* head_w, const csa_
   a.off_region = plan.off_region; a.off_counts = plan.off_counts; a.off_skey = plan.off_skey;
   a.off_sidx = plan.off_sidx; a.off_ctr = plan.off_ctr; a.lm = plan.lm; a.nseg = plan.nseg;
   a.rstride = plan.rstride;
+  a.spin_max = indexer_spin_limit();
   a.sel = sel;
   const size_t half = plan.ws / 2;
   a.ws_key = (uint32_t*)ws;

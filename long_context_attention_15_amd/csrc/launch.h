@@ -33,6 +33,8 @@ IdxPlan indexer_plan(int B, int Tq, int64_t n_entries, int k);
 // Many queries over FP8 keys of 64 dims: the single-pass streaming top-k,
 // which needs no workspace.
 bool indexer_stream_ok(const csa_store& keys, int H_I, int B, int Tq, int64_t n_entries, int k);
+// Diagnostic counters of the current device (synchronises it).
+hipError_t diag_counters(uint64_t* out, int n, bool reset);
 hipError_t launch_indexer(const csa_store& qidx, const float* head_w, const csa_store& keys,
                           int64_t n_entries, const int64_t* q_pos, int B, int Tq, int H_I, int m,
                           int k, int32_t* sel, void* ws, const IdxPlan& plan, hipStream_t st);

@@ -39,6 +39,10 @@ def test_library_exports_every_declared_symbol(lib):
     assert set(_declared_functions()) == set(csa.EXPORTS)
 
 
+def test_diag_counters_reject_a_null_array(lib):
+    assert lib.csa_diag_counters(None, 2, 0) == 1
+
+
 def test_version_and_status_strings(lib):
     assert "gfx950" in csa.version()
     assert lib.csa_status_string(0).decode() == "CSA_OK"
@@ -131,6 +135,12 @@ def test_attention_rejects_bad_arguments(lib):
     assert pre(n=101) == 1
     assert pre(flags=csa.WIN_RING) == 1
     assert pre(flags=8) == 1
+    # q and out move in 16-byte pieces: a bf16 view offset by 2 or 4 elements is rejected
+    assert pre(q=P + 4) == 1 and "16-byte" in lib.csa_last_error().decode()
+    assert pre(q=P + 8) == 1
+    assert lib.csa_sparse_attn_prefill(P, csa.BF16, 1, 256, 64, kv, 100, P, 64, win, 128, 0, 0.04, P + 4, 0, 0,
+                                       None) == 1
+    assert lib.swa_merge(P, csa.BF16, 1, 8, 64, win, 0, 128, 0, P + 8, P, 0, 0.04, P, None) == 1
     # decode: workspace required for few queries
     ring = _store(P, 128, 512, 64, csa.FP8_E4M3, P)
     st = lib.csa_sparse_attn_decode(P, csa.BF16, 4, 128, kv, 100, P, 64, ring, P, 128, 0, 0.04, P, 0, 0, P, 16,

@@ -433,12 +433,13 @@ def test_hca_prefill_parity(lib, H, D, R, T, m, W):
         assert np.all(got[: m - 1] == 0)                # no entries, no window, no sink
 
 
-@pytest.mark.parametrize("tau_mult", [60.0, 0.0, -1.0])
+@pytest.mark.parametrize("tau_mult", [60.0, 0.0, -1.0, 1e-29 * math.sqrt(512)])
 def test_csa_prefill_extreme_and_nonpositive_scales(lib, tau_mult):
     """A large softmax scale puts later logits far above the first tile's
     maximum, which the MFMA kernel meets with its exact-maximum recompute; a
-    zero or negative scale takes the general kernel (the MFMA kernel masks
-    empty slots through a -1e30 logit).  Both must still match the oracle."""
+    zero, negative or tiny positive scale (1e-29, at which a -1e30 logit would
+    no longer vanish under exp2) takes the general kernel (the MFMA kernel
+    masks empty slots through a -1e30 logit).  All must match the oracle."""
     import torch
     H, D, R, T, m, k, W = 64, 512, 64, 400, 4, 64, 128
     N = T // m
