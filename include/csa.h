@@ -224,6 +224,25 @@ csa_status csa_sparse_attn_decode(const void* q, int q_fmt, int B, int H, csa_st
                                   hipStream_t stream);
 
 /*
+ * csa_sparse_attn_decode_noalloc -- csa_sparse_attn_decode for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same operation, arguments
+ * and results as csa_sparse_attn_decode, but the split partials go to a
+ * scratch array the library holds in each device's memory (48 MiB per
+ * device, held until the process ends) instead of a caller workspace.  The
+ * call allocates nothing.  Sizes whose split partials need more than 48 MiB
+ * (csa_attn_workspace(B, 1, H, dim, k + W) > 48 MiB) return CSA_EINVAL.
+ * Every call on a device shares that device's scratch: calls that overlap in
+ * time on one device (other streams, other threads) race and must not be
+ * issued; calls on one stream are ordered and safe.  The scratch keeps the
+ * last call's partials; nothing in it needs to start at zero.
+ */
+csa_status csa_sparse_attn_decode_noalloc(const void* q, int q_fmt, int B, int H, csa_store ckv,
+                                          int64_t n_entries, const int32_t* sel, int k, csa_store ring,
+                                          const int64_t* pos, int W, const float* sink, float sm_scale,
+                                          void* out, float* lse, int flags, hipStream_t stream);
+
+/*
  * hca_attn -- HCA dense attention (kenelite analysis section 6; model-card
  * notes: heavier compression with dense attention) over every visible entry
  * j < n_t = min(n_entries, floor((t+1)/m_prime)) plus the window and sink.

@@ -54,6 +54,8 @@ _SIGS = {
     "hca_attn": ([_P, _I, _I, _I, _I, _CStore, _I, _I64, _P, _CStore, _I, _P, _F, _P, _P, _I, _P, _SZ, _P], _I),
     "swa_merge": ([_P, _I, _I, _I, _I, _CStore, _P, _I, _I, _P, _P, _P, _F, _P, _P], _I),
     "csa_diag_counters": ([_P, _I, _I], _I),
+    "csa_sparse_attn_decode_noalloc": ([_P, _I, _I, _I, _CStore, _I64, _P, _I, _CStore, _P, _I, _P, _F, _P, _P, _I,
+                                        _P], _I),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -213,6 +215,15 @@ def sparse_attn_decode(q, ckv: Store, n_entries: int, sel, k: int, ring: Store, 
     _check(load().csa_sparse_attn_decode(_ptr(q), _fmt_of(q), B, H, ckv.c(), n_entries, _ptr(sel), k, ring.c(),
                                          _ptr(pos), W, _ptr(sink), sm_scale, _ptr(out), _ptr(lse), flags, _ptr(ws),
                                          wsb, _stream(stream)), "csa_sparse_attn_decode")
+
+
+def sparse_attn_decode_noalloc(q, ckv: Store, n_entries: int, sel, k: int, ring: Store, pos, W: int, sink,
+                               sm_scale: float, out, lse=None, flags: int = 0, stream=None):
+    """csa_sparse_attn_decode_noalloc: as sparse_attn_decode, split partials in the library's device scratch."""
+    B, H, D = q.shape
+    _check(load().csa_sparse_attn_decode_noalloc(_ptr(q), _fmt_of(q), B, H, ckv.c(), n_entries, _ptr(sel), k,
+                                                 ring.c(), _ptr(pos), W, _ptr(sink), sm_scale, _ptr(out), _ptr(lse),
+                                                 flags, _stream(stream)), "csa_sparse_attn_decode_noalloc")
 
 
 def hca_attn(q, hkv: Store, m_prime: int, n_entries: int, q_pos, win: Store, W: int, sink, sm_scale: float,

@@ -5,6 +5,8 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <atomic>
+#include <mutex>
 
 #include "common.h"
 #include "launch.h"
@@ -93,6 +95,37 @@ csa_status check_q(const void* q, int q_fmt, int H, int dim, const void* out) {
 }
 
 #define CSA_TRY(x) do { csa_status _s = (x); if (_s != CSA_OK) return _s; } while (0)
+
+// Scratch of the allocation-free decode entry point: split partials of the
+// decode attention (float32 o, m, l per head and split).  Each device holds
+// its own copy for the life of the process.  In host code `scratch` names a
+// host-side stand-in, never the device memory: the device address comes from
+// hipGetSymbolAddress, once per device, and only that address is used.
+constexpr size_t kScratchBytes = (size_t)48 << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+csa_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(CSA_EUNSUPPORTED, "device %d beyond the scratch table", dev);
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !p) return hip_status(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return CSA_OK;
+}
 
 }  // namespace
 
@@ -266,6 +299,23 @@ csa_status csa_sparse_attn_decode(const void* q, int q_fmt, int B, int H, csa_st
   c.ckv = ckv; c.n_entries = n_entries; c.mode = csa::kModeSel; c.sel = sel; c.k = k; c.m = 1;
   c.win = ring; c.W = W; c.ring = 1; c.q_pos = pos; c.ws = ws; c.ws_bytes = ws_bytes;
   return run_attn(c, flags | 0, stream, "csa_sparse_attn_decode launch");
+}
+
+csa_status csa_sparse_attn_decode_noalloc(const void* q, int q_fmt, int B, int H, csa_store ckv, int64_t n_entries,
+                                          const int32_t* sel, int k, csa_store ring, const int64_t* pos, int W,
+                                          const float* sink, float sm_scale, void* out, float* lse, int flags,
+                                          hipStream_t stream) {
+  g_err[0] = 0;
+  if (B < 0 || H < 1 || k < 1) return fail(CSA_EINVAL, "B >= 0, H >= 1 and k >= 1 needed");
+  const int64_t max_list = (int64_t)k + ((flags & CSA_ATTN_PARTIAL) ? 0 : (W > 0 ? W : 0));
+  const size_t need = csa::attn_workspace(B, 1, H, ckv.dim, max_list);
+  if (need > kScratchBytes)
+    return fail(CSA_EINVAL, "these sizes need %zu bytes of scratch, more than the %zu bytes of the no-allocation path",
+                need, kScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) CSA_TRY(scratch_of_current_device(&ws));
+  return csa_sparse_attn_decode(q, q_fmt, B, H, ckv, n_entries, sel, k, ring, pos, W, sink, sm_scale, out, lse, flags,
+                                ws, need > 0 ? kScratchBytes : 0, stream);
 }
 
 csa_status hca_attn(const void* q, int q_fmt, int B, int Tq, int H, csa_store hkv, int m_prime,

@@ -39,6 +39,17 @@ def test_library_exports_every_declared_symbol(lib):
     assert set(_declared_functions()) == set(csa.EXPORTS)
 
 
+def test_noalloc_decode_rejects_sizes_beyond_its_scratch(lib):
+    """73 sequences of 224 heads split their lists into 64 MiB of partials,
+    more than the 48 MiB scratch of the allocation-free entry point."""
+    kv = _store(P, 100, 512, 64, csa.FP8_E4M3, P)
+    ring = _store(P, 128, 512, 64, csa.FP8_E4M3, P)
+    assert lib.csa_attn_workspace(73, 1, 224, 512, 1024 + 128) > 48 << 20
+    st = lib.csa_sparse_attn_decode_noalloc(P, csa.BF16, 73, 224, kv, 100, P, 1024, ring, P, 128, 0, 0.04, P, 0, 0,
+                                            None)
+    assert st == 1 and "scratch" in lib.csa_last_error().decode()
+
+
 def test_diag_counters_reject_a_null_array(lib):
     assert lib.csa_diag_counters(None, 2, 0) == 1
 
