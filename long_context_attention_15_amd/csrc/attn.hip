@@ -357,7 +357,7 @@ hipError_t launch_attn(const AttnCall& c, hipStream_t st) {
   a.ws = (float*)c.ws;
   if ((int64_t)c.B * c.Tq == 0) return hipSuccess;
   if (mfma) {
-    hipError_t e = launch_attn_mfma(c, a.nsplit, a.split_len, st);
+    hipError_t e = launch_attn_m32(c, a.nsplit, a.split_len, st);
     if (e != hipSuccess || a.nsplit == 1) return e;
     hipLaunchKernelGGL(attn_split_merge_kernel, dim3((unsigned)((int64_t)c.B * c.Tq), c.H), dim3(64), 0, st, a);
     return hipGetLastError();

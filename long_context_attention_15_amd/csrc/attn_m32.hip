@@ -1,0 +1,504 @@
+// Gathered-entry attention on bf16 MFMA (gfx950), 32 heads per wavefront:
+// head dim 512 stored as FP8 bulk (448 dims, one power-of-two scale per row)
+// + BF16 RoPE dims (64), bf16 queries.
+//
+// Work item: one query row, 64 heads, one split of its entry list (the
+// window rows, then the top-k / visible compressed entries).  Two
+// wavefronts; wavefront w owns heads [32 w, 32 w + 32) over all 512 dims, so
+// every product runs on v_mfma_f32_32x32x16_bf16 with the 32 heads as the N
+// side: each operand read from LDS feeds twice the flops of a 16-head
+// layout.  Two workgroups share a CU (LDS 77 KiB each, one wavefront per
+// SIMD), so one workgroup's barriers and epilogue overlap the other's
+// products.  Per tile of 32 entries:
+//   * the raw 576-byte rows go HBM -> LDS by LDS DMA three tiles ahead, unit
+//     major: 16-byte unit u of row r at position 32 u + (r ^ 4 (u & 1)) of
+//     the tile, so a wave-wide load covers units 2 j, 2 j + 1 of all 32 rows
+//     (a lane always loads from the same row) and every 16-lane group of the
+//     reads below, and both halves of each 32-lane pass of the transposing
+//     reads, fall on distinct banks;
+//   * S^T = K Q^T (32 entries x 32 heads, K = 16 dims per step): each lane
+//     reads 16 FP8 bytes of its entry row (two K-steps) and converts them
+//     with the row scale to BF16 exactly (power-of-two scales); RoPE dims
+//     are read as BF16;
+//   * softmax in base 2 against a per-head reference fixed at the first
+//     filled tile (a head is one lane column of the accumulators, split over
+//     lanes l and l + 32);
+//   * O^T += V^T P^T (32 dims x 32 heads, K = 16 entries per step): V^T comes
+//     from 8-bit transposing LDS reads of the FP8 codes, converted unscaled,
+//     with the row scale folded into P; RoPE dims from 16-bit transposing
+//     reads.  P stays in registers: its K order is the order in which the
+//     S^T accumulators hold a lane's entries.
+// K = V = the stored entry (shared KV).
+#include "common.h"
+#include "launch.h"
+
+namespace csa {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef int v2i32 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) v2i32 lds_v2i32;
+
+constexpr int kD = 512;                    // head dim
+constexpr int kT = 32;                     // entries per tile
+constexpr int kThreads = 128;              // two wavefronts
+constexpr int kRow = 576;                  // 448 FP8 + 64 BF16
+constexpr int kUnits = kRow / 16;          // 16-byte units per row
+constexpr int kTileBytes = kT * kRow;      // 18432 = 18 wave-wide 1 KiB loads
+constexpr int kLoadsW = kTileBytes / 1024 / 2;   // 9 loads per wavefront per tile
+constexpr int kStages = 4;                 // raw tile buffers
+constexpr int kLead = 3;                   // DMA distance in tiles
+constexpr int kSlots = 8;                  // slot tables (two build batches)
+constexpr int kBatch = 4;                  // tiles per table build (2 per wavefront)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kEmpty = -1.0e30f;         // logit of an empty slot
+
+struct Args {
+  const uint16_t* q; int B, Tq, H;
+  Store ckv; int64_t n_entries; int mode; const int32_t* sel; int k; int m;
+  Store win; int W; int ring; const int64_t* q_pos;
+  const float* sink; float tau;
+  void* out; int out_f32; float* lse; int partial;
+  int nsplit; int split_len; float* ws;
+};
+
+// Zero row that empty slots gather from (device globals start zeroed).
+__device__ __attribute__((aligned(16))) uint8_t zero_row[1024];
+
+// byte offset in a raw tile of 16-byte unit u of row r
+__device__ __forceinline__ int unit_off(int r, int u) { return 16 * (kT * u + (r ^ (4 * (u & 1)))); }
+// entry behind K index 8 h + e of PV step c: the order in which lane
+// (head, h) holds its S^T accumulator rows 8 c .. 8 c + 7
+__device__ __forceinline__ int pv_entry(int c, int h, int e) { return 16 * c + 8 * (e >> 2) + 4 * h + (e & 3); }
+
+__device__ __forceinline__ int64_t visible(int64_t t, int m, int64_t n) {
+  int64_t v = t < 0 ? 0 : (t + 1) / m;
+  return v < n ? v : n;
+}
+
+// 8 FP8 codes -> 8 BF16 values times s (exact for a power-of-two s).
+__device__ __forceinline__ u32x4 cvt8(u32x2 w, float s) {
+  u32x4 r;
+  r.x = __builtin_bit_cast(unsigned int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, s, false));
+  r.y = __builtin_bit_cast(unsigned int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, s, true));
+  r.z = __builtin_bit_cast(unsigned int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, s, false));
+  r.w = __builtin_bit_cast(unsigned int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, s, true));
+  return r;
+}
+
+#define M32_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+
+// 16-byte LDS DMA (lane l's bytes land at dst + 16 l) and 4-byte LDS DMA
+// (lane l's word at dst + 4 l), as inline asm with no register result:
+// completion is tracked by explicit vmcnt waits.
+__device__ __forceinline__ void dma16(const void* src, void* dst) {
+  const unsigned lds = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)dst);
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* src, void* dst) {
+  const unsigned lds = __builtin_amdgcn_readfirstlane((unsigned)(uintptr_t)dst);
+  asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+}
+
+__device__ __forceinline__ float swap32_max(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+__device__ __forceinline__ float swap32_sum(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
+__global__ __launch_bounds__(kThreads, 1) void attn_m32_kernel(Args a) {
+  __shared__ __attribute__((aligned(16))) uint8_t Raw[kStages][kTileBytes];
+  __shared__ const uint8_t* Tptr[kSlots][kT];                     // row address (zero row if empty)
+  __shared__ __attribute__((aligned(16))) float Tscl[kSlots][kT];  // row scale (0 if empty)
+  __shared__ __attribute__((aligned(16))) float Tbias[kSlots][kT]; // 0 filled, kEmpty empty
+  __shared__ __attribute__((aligned(16))) int32_t Tsel[kSlots][kT];
+  __shared__ int s_over;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int hcol = lane & 31, hh = lane >> 5;        // head column, lane half
+  const int64_t bq = xcd_remap(blockIdx.x, gridDim.x);   // query row (b * Tq + q)
+  const int b = (int)(bq / a.Tq);
+  const int h = blockIdx.y * 64 + wave * 32 + hcol;           // this lane's head
+  const int64_t t = a.q_pos ? a.q_pos[bq] : (int64_t)(bq % a.Tq);
+  const int64_t Lc = a.mode == kModeSel ? a.k : (a.mode == kModeRange ? visible(t, a.m, a.n_entries) : 0);
+  const int64_t L = Lc + a.W;
+  const int64_t i0 = (int64_t)blockIdx.z * a.split_len;
+  const int64_t i1 = a.nsplit == 1 ? L : (i0 + a.split_len < L ? i0 + a.split_len : L);
+  const int ntiles = i1 > i0 ? (int)((i1 - i0 + kT - 1) / kT) : 0;
+
+  // ---- slot tables.  Lane tl of a building wavefront owns slot i0 + 32
+  // tile + tl of the entry list (lanes 32-63 the next tile): the W window
+  // rows first, then the Lc compressed entries.  Row address and bias are
+  // stored now; the row scale and the sel entries arrive by LDS DMA, so no
+  // load result is carried in registers across tiles.  Slot arithmetic is
+  // 32-bit (lists stay far below 2^31 entries).
+  const int i0i = (int)i0, i1i = (int)i1;
+  const int win_p0 = (int)(t - a.W + 1);
+  const bool sel_mode = a.mode == kModeSel;
+  const int n_ent = (int)a.n_entries, win_cap = (int)a.win.cap;
+  const uint8_t* const ckv_base = a.ckv.rows + (size_t)b * a.ckv.cap * a.ckv.row_bytes;
+  const float* const ckv_sc = (const float*)a.ckv.scales + (size_t)b * a.ckv.cap;
+  const uint8_t* const win_base = a.win.rows + (size_t)b * a.win.cap * a.win.row_bytes;
+  const float* const win_sc = (const float*)a.win.scales + (size_t)b * a.win.cap;
+  const int32_t* const sel_row = sel_mode ? a.sel + bq * a.k : nullptr;
+  auto table2 = [&](int tile, int jsel) {          // tiles `tile`, tile + 1 (tile even)
+    const int ts = tile & (kSlots - 1);
+    const int slot = i0i + tile * kT + lane;
+    int p = win_p0 + slot;
+    const bool p_ok = p >= 0 && (a.ring || p < win_cap);
+    if (a.ring) p = p >= 0 ? p % a.W : 0;
+    const bool in_list = slot < i1i, is_c = slot >= a.W;
+    const int j = sel_mode ? jsel : slot - a.W;
+    const bool ok = in_list && (is_c ? (unsigned)j < (unsigned)n_ent : p_ok);
+    const int idx = is_c ? j : p;
+    const uint8_t* ptr = (is_c ? ckv_base : win_base) + (size_t)idx * kRow;
+    const float* sp = (is_c ? ckv_sc : win_sc) + idx;
+    (&Tptr[0][0])[ts * kT + lane] = ok ? ptr : zero_row;
+    (&Tbias[0][0])[ts * kT + lane] = ok ? 0.0f : kEmpty;
+    dma4(ok ? (const void*)sp : (const void*)zero_row, &Tscl[ts][0]);
+  };
+  auto sel_dma2 = [&](int tile) {                  // sel entries of tiles `tile`, tile + 1
+    const int slot = i0i + tile * kT + lane;
+    dma4(sel_mode && slot >= a.W && slot < i1i ? (const void*)(sel_row + (slot - a.W)) : (const void*)zero_row,
+         &Tsel[tile & (kSlots - 1)][0]);
+  };
+  // Row DMA of `tile` into Raw[tile % kStages]: wave-wide load j = wave +
+  // 2 jj fills positions 64 j .. 64 j + 63, i.e. units 2 j + hh of row
+  // hcol ^ (4 hh) for lane (hh, hcol): a lane reads one row of the tile.
+  const int dma_row = hcol ^ (4 * hh);
+  auto dma_src = [&](int tile) { return Tptr[tile & (kSlots - 1)][dma_row] + 16 * hh; };
+  auto dma_rows = [&](const uint8_t* src, int tile, int jj) {
+    const int j = wave + 2 * jj;
+    dma16(src + 32 * j, Raw[tile % kStages] + 1024 * j);
+  };
+
+  const float sig2 = (a.nsplit > 1 || a.partial || !a.sink) ? -INFINITY : a.sink[h] * kLog2e;
+
+  // ---- Q^T operands.  K-step pair s < 14 (FP8 dims 32 s .. 32 s + 31): step
+  // 2 s + i, K index 8 hh + e <-> dim 32 s + 16 hh + 8 i + e; RoPE step j < 4:
+  // K index 8 hh + e <-> dim 448 + 16 j + 8 hh + e.
+  bf16x8 qf[32];
+  {
+    const uint16_t* qp = a.q + (bq * a.H + h) * (int64_t)kD;
+#pragma unroll
+    for (int s = 0; s < 14; ++s)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        qf[2 * s + i] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qp + 32 * s + 16 * hh + 8 * i));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) qf[28 + j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qp + 448 + 16 * j + 8 * hh));
+  }
+  // LDS byte offsets of this lane's reads within a raw tile.
+  // K (S^T A operand): entry ke = hcol, FP8 pair s at unit 2 s + hh, RoPE
+  // step j at unit 28 + 2 j + hh: unit_off(ke, 2 s + hh) = k_off + 1024 s.
+  const int ke = hcol;
+  const int k_off = unit_off(ke, hh);
+  // V^T FP8 (8-bit transposing reads): 16-lane group g = lane >> 4 covers
+  // dims 16 (g & 1) .. +16 of a 32-dim block (unit 2 db + (g & 1)), entries
+  // of half hh = g >> 1; source lane i16 reads 8 bytes of row
+  // pv_entry(c, hh, i16 >> 1), half i16 & 1: v_fp8[c] + 1024 db.
+  const int g = lane >> 4, i16 = lane & 15;
+  int v_fp8[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) v_fp8[c] = unit_off(pv_entry(c, hh, i16 >> 1), g & 1) + 8 * (i16 & 1);
+  // V^T RoPE (16-bit transposing reads): row pv_entry(c, hh, 4 rd + (i16 >> 2)),
+  // bf16 dims 448 + 32 bb + 16 (g & 1) + 4 (i16 & 3) .. +4, i.e. unit
+  // 28 + 4 bb + 2 (g & 1) + (i16 & 3) / 2, half i16 & 1: v_rope[c][rd] + 2048 bb.
+  int v_rope[2][2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c)
+#pragma unroll
+    for (int rd = 0; rd < 2; ++rd)
+      v_rope[c][rd] = unit_off(pv_entry(c, hh, 4 * rd + (i16 >> 2)), 28 + 2 * (g & 1) + ((i16 & 3) >> 1)) +
+                      8 * (i16 & 1);
+
+  f32x16 acc[16];
+#pragma unroll
+  for (int db = 0; db < 16; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
+  const float sc2 = a.tau * kLog2e;
+  // Softmax reference per head (log2 units): fixed at the first tile with a
+  // filled slot; probabilities relative to it stay below 2^kMaxLift, else
+  // the query is recomputed once with the exact maximum (tracked as xmax).
+  constexpr float kMaxLift = 64.0f;
+  float mref = 0.0f, xmax = -INFINITY, lrun = 0.0f;
+  bool mset = false;
+  if (tid == 0) s_over = 0;
+
+  // One pass over the entry list: prologue and tile loop.  It runs a second
+  // time only when some logit exceeded the reference by 2^kMaxLift (written
+  // out twice rather than as a loop, so that nothing of the prologue is
+  // kept live across the tile loop for the next round).
+  auto pass = [&]() {
+    // ---- prologue: sel entries of tiles 0 .. 7, tables of tiles 0 .. 3,
+    // rows of tiles 0 .. kLead-1.  With the window first in the list, the
+    // first tiles' tables need no sel entry when the split starts the list
+    // and the window covers them (or there are no sel entries): their row
+    // loads go out without waiting for the sel loads.
+    const bool early = !sel_mode || (i0i == 0 && a.W >= kBatch * kT);
+    sel_dma2(2 * wave);
+    sel_dma2(kBatch + 2 * wave);
+    if (!early) {
+      M32_WAIT_VMCNT(0);
+      asm volatile("" ::: "memory");
+    }
+    table2(2 * wave, (&Tsel[0][0])[2 * wave * kT + lane]);
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+    for (int pt = 0; pt < kLead; ++pt) {
+      const uint8_t* src = dma_src(pt);
+#pragma unroll
+      for (int jj = 0; jj < kLoadsW; ++jj) dma_rows(src, pt, jj);
+    }
+    M32_WAIT_VMCNT((kLead - 1) * kLoadsW);      // tile 0 in (loads complete in order)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+    for (int it = 0; it < ntiles; ++it) {
+      const uint8_t* raw = Raw[it % kStages];
+      const int ts = it & (kSlots - 1);
+      const uint8_t* dsrc = dma_src(it + kLead);
+      if ((it & (kBatch - 1)) == 0) {
+        // tables of tiles it+4 .. it+7 (sel entries landed at least one
+        // iteration ago) and sel entries of tiles it+8 .. it+11
+        const int tb = it + kBatch + 2 * wave;
+        table2(tb, (&Tsel[0][0])[(tb & (kSlots - 1)) * kT + lane]);
+        sel_dma2(it + 2 * kBatch + 2 * wave);
+      }
+
+      // ---- S^T = K Q^T in one accumulator chain that starts at the slot
+      // bias, so empty slots drop out of the softmax by themselves.
+      f32x16 sa;
+      bool filled = false;                       // some slot of the tile holds an entry
+      {
+        const float* tbs = Tbias[ts];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 bv = *(const float4*)(tbs + 8 * q4 + 4 * hh);
+          sa[4 * q4 + 0] = bv.x; sa[4 * q4 + 1] = bv.y; sa[4 * q4 + 2] = bv.z; sa[4 * q4 + 3] = bv.w;
+          filled = filled || bv.x == 0.0f || bv.y == 0.0f || bv.z == 0.0f || bv.w == 0.0f;
+        }
+      }
+      const bool tile_filled = __ballot(filled) != 0ull;
+      const float ksc = Tscl[ts][ke];
+      constexpr int kSD = 2;                     // K read distance (pairs)
+      u32x4 kr[18];
+#pragma unroll
+      for (int s = 0; s < kSD; ++s) kr[s] = *(const u32x4*)(raw + k_off + 1024 * s);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int s = 0; s < 18; ++s) {
+        // reads 0..13: FP8 pairs; 14..17: RoPE steps
+        if (s + kSD < 18) {
+          const int sn = s + kSD;
+          kr[sn] = *(const u32x4*)(raw + k_off + 1024 * sn);   // FP8 pair sn, or RoPE step sn - 14
+        }
+        if (s < 14) {
+          const u32x4 k0 = cvt8(u32x2{kr[s].x, kr[s].y}, ksc);
+          const u32x4 k1 = cvt8(u32x2{kr[s].z, kr[s].w}, ksc);
+          sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, k0), qf[2 * s], sa, 0, 0, 0);
+          sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, k1), qf[2 * s + 1], sa, 0, 0, 0);
+        } else {
+          sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr[s]), qf[28 + s - 14], sa, 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+
+      // ---- V^T reads of the first dim blocks go out before the softmax
+      constexpr int kVD = 4;
+      v2i32 vf[2][14];
+#pragma unroll
+      for (int db = 0; db < kVD; ++db)
+        vf[0][db] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32*)(raw + v_fp8[0] + 1024 * db));
+      __builtin_amdgcn_sched_barrier(0);
+
+      // ---- softmax: lane holds entries 8 (r >> 2) + 4 hh + (r & 3) of head h
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] = sa[r];
+      {
+        if (!mset && tile_filled) {
+          // first tile with a filled slot (slots are shared by all heads, so
+          // this is wave-uniform): the head's maximum over the tile
+          float mt = -INFINITY;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mt = fmaxf(mt, x[r] * sc2);
+          mref = swap32_max(mt);
+          mset = true;
+        }
+      }
+      float p[16];
+      float psum = 0.0f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float y = fmaf(x[r], sc2, -mref);
+        xmax = fmaxf(xmax, y);
+        p[r] = __builtin_amdgcn_exp2f(y);
+        psum += p[r];
+      }
+      lrun += psum;
+      // P^T operands of PV step c: unscaled (RoPE dims) and times the row
+      // scale of each entry (FP8 dims, whose codes convert unscaled)
+      bf16x8 pr[2], ps[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const float4 s0 = *(const float4*)(Tscl[ts] + 16 * c + 4 * hh);
+        const float4 s1 = *(const float4*)(Tscl[ts] + 16 * c + 8 + 4 * hh);
+        const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pr[c][e] = (__bf16)p[8 * c + e];
+          ps[c][e] = (__bf16)(p[8 * c + e] * sv[e]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+
+      // ---- O^T += V^T P^T: step c over entries, 14 FP8 dim blocks + 2 RoPE
+      // blocks; rows of tile it + kLead go out between the products (their
+      // table was written at least one iteration ago, their buffer was
+      // freed by the barrier that ended iteration it - 1)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+#pragma unroll
+        for (int db = 0; db < 14; ++db) {
+          const int n = db + kVD;
+          if (n < 14) vf[c][n] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32*)(raw + v_fp8[c] + 1024 * n));
+          else if (c == 0) vf[1][n - 14] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32*)(raw + v_fp8[1] + 1024 * (n - 14)));
+          const u32x4 v = cvt8(u32x2{(unsigned)vf[c][db].x, (unsigned)vf[c][db].y}, 1.0f);
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v), ps[c], acc[db], 0, 0, 0);
+          const int di = 14 * c + db;            // 28 slots, 9 loads: every third
+          if (di % 3 == 1 && di / 3 < kLoadsW) dma_rows(dsrc, it + kLead, di / 3);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int bb = 0; bb < 2; ++bb) {
+          const u32x2 r0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(raw + v_rope[c][0] + 2048 * bb)));
+          const u32x2 r1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(raw + v_rope[c][1] + 2048 * bb)));
+          const u32x4 v = u32x4{r0.x, r0.y, r1.x, r1.y};
+          acc[14 + bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v), pr[c], acc[14 + bb], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // rows of tile it+1 are in before the barrier: loads complete in
+      // order, and after them every wave issued the loads of tiles it+2 and
+      // it+3 (and the table loads, which only make the wait stricter)
+      M32_WAIT_VMCNT(2 * kLoadsW);
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    }
+    // every LDS DMA of this pass has landed before anything reuses LDS
+    M32_WAIT_VMCNT(0);
+    xmax = swap32_max(xmax);
+    lrun = swap32_sum(lrun);
+  };
+  pass();
+  if (__ballot(mset && xmax > kMaxLift) != 0ull && lane == 0) s_over = 1;
+  __syncthreads();
+  if (s_over) {                                  // uniform: recompute with the exact maximum
+#pragma unroll
+    for (int db = 0; db < 16; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
+    lrun = 0.0f;
+    if (mset) mref += xmax;
+    xmax = -INFINITY;
+    pass();
+  }
+  __syncthreads();
+  const float mrun = mset ? mref : -INFINITY;
+
+  // ---- epilogue: lane holds O^T dims 32 db + 8 q + 4 hh + (0..3) of head h
+  // (acc[db][4 q + 0..3]).  Rows go out through LDS so that each store
+  // instruction writes one contiguous piece of a head row.
+  const bool split = a.nsplit > 1;
+  float scale = 1.0f, lse = -INFINITY;
+  if (!split) {
+    const float M = fmaxf(mrun, sig2);
+    scale = 0.0f;
+    if (M > -INFINITY) {
+      const float fm = mrun > -INFINITY ? exp2f(mrun - M) : 0.0f;
+      const float Z = lrun * fm + (sig2 > -INFINITY ? exp2f(sig2 - M) : 0.0f);
+      scale = fm / Z;
+      lse = (M + log2f(Z)) * kLn2;
+    }
+  }
+  const bool f32 = split || a.out_f32;
+  constexpr int kStageRow = 1024 + 16;
+  uint8_t* const stg = &Raw[0][0] + wave * 32 * kStageRow;
+  const int64_t hrow0 = bq * a.H + blockIdx.y * 64 + wave * 32;   // this wave's first head row
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    if (half == 1 && !f32) break;                // uniform
+    if (f32) {
+      // dims 256 half .. +256: blocks 8 half .. 8 half + 7
+#pragma unroll
+      for (int k8 = 0; k8 < 8; ++k8) {
+        const int db = 8 * half + k8;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          float4 v;
+          v.x = acc[db][4 * q4 + 0] * scale; v.y = acc[db][4 * q4 + 1] * scale;
+          v.z = acc[db][4 * q4 + 2] * scale; v.w = acc[db][4 * q4 + 3] * scale;
+          *(float4*)(stg + hcol * kStageRow + 4 * (32 * k8 + 8 * q4 + 4 * hh)) = v;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int db = 0; db < 16; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          u32x2 w;
+          w.x = f32_to_bf16(acc[db][4 * q4 + 0] * scale) | (f32_to_bf16(acc[db][4 * q4 + 1] * scale) << 16);
+          w.y = f32_to_bf16(acc[db][4 * q4 + 2] * scale) | (f32_to_bf16(acc[db][4 * q4 + 3] * scale) << 16);
+          *(u32x2*)(stg + hcol * kStageRow + 2 * (32 * db + 8 * q4 + 4 * hh)) = w;
+        }
+    }
+    // (each wave writes and reads only its own rows: its LDS accesses stay in order)
+#pragma unroll 4
+    for (int r = 0; r < 32; ++r) {
+      const u32x4 v = *(const u32x4*)(stg + r * kStageRow + 16 * lane);
+      const int64_t hr = hrow0 + r;
+      uint8_t* dst = split ? (uint8_t*)(a.ws + (hr * a.nsplit + blockIdx.z) * (int64_t)kD)
+                           : (f32 ? (uint8_t*)((float*)a.out + hr * kD) : (uint8_t*)((uint16_t*)a.out + hr * kD));
+      *(u32x4*)(dst + 1024 * half + 16 * lane) = v;
+    }
+  }
+  if (split) {
+    if (hh == 0) {
+      float* wml = a.ws + (int64_t)a.B * a.Tq * a.H * a.nsplit * kD + ((bq * a.H + h) * a.nsplit + blockIdx.z) * 2;
+      wml[0] = mrun > -INFINITY ? mrun * kLn2 : -INFINITY;
+      wml[1] = lrun;
+    }
+  } else if (a.lse && hh == 0) {
+    a.lse[bq * a.H + h] = lse;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_m32(const AttnCall& c, int nsplit, int split_len, hipStream_t st) {
+  if (c.n_entries + c.W + kT > INT32_MAX || c.ckv.cap > INT32_MAX || c.win.cap > INT32_MAX) return hipErrorInvalidValue;
+  Args a;
+  a.q = (const uint16_t*)c.q; a.B = c.B; a.Tq = c.Tq; a.H = c.H;
+  a.ckv = c.ckv.rows ? view(c.ckv) : view(c.win);
+  a.n_entries = c.n_entries; a.mode = c.mode; a.sel = c.sel; a.k = c.k; a.m = c.m;
+  a.win = c.win.rows ? view(c.win) : a.ckv;
+  a.W = c.W; a.ring = c.ring; a.q_pos = c.q_pos;
+  a.sink = c.sink; a.tau = c.tau;
+  a.out = c.out; a.out_f32 = c.partial; a.lse = c.lse; a.partial = c.partial;
+  a.nsplit = nsplit; a.split_len = split_len; a.ws = (float*)c.ws;
+  const dim3 grid((unsigned)((int64_t)c.B * c.Tq), c.H / 64, nsplit);
+  hipLaunchKernelGGL(attn_m32_kernel, grid, dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace csa

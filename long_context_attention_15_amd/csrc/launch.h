@@ -58,5 +58,6 @@ bool attn_supported(int H, int D);
 hipError_t launch_attn(const AttnCall& c, hipStream_t st);
 bool attn_mfma_eligible(int q_fmt, int H, int D, const csa_store& kv, bool has_prior, float tau);
 hipError_t launch_attn_mfma(const AttnCall& c, int nsplit, int split_len, hipStream_t st);
+hipError_t launch_attn_m32(const AttnCall& c, int nsplit, int split_len, hipStream_t st);
 
 }  // namespace csa
