@@ -37,6 +37,7 @@ namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -72,10 +73,10 @@ struct Args {
 __device__ __attribute__((aligned(16))) uint8_t zero_row[1024];
 
 // byte offset in a raw tile of 16-byte unit u of row r
-__device__ __forceinline__ int unit_off(int r, int u) { return 16 * (kT * u + (r ^ (4 * (u & 1)))); }
+__device__ __forceinline__ int unit_off(int r, int u) { return 16 * (kT * u + (r ^ (8 * (u & 1)))); }
 // entry behind K index 8 h + e of PV step c: the order in which lane
 // (head, h) holds its S^T accumulator rows 8 c .. 8 c + 7
-__device__ __forceinline__ int pv_entry(int c, int h, int e) { return 16 * c + 8 * (e >> 2) + 4 * h + (e & 3); }
+__device__ __forceinline__ int pv_entry(int c, int h, int e) { return 16 * c + 8 * h + e; }
 
 __device__ __forceinline__ int64_t visible(int64_t t, int m, int64_t n) {
   int64_t v = t < 0 ? 0 : (t + 1) / m;
@@ -175,7 +176,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_m32_kernel(Args a) {
   // Row DMA of `tile` into Raw[tile % kStages]: wave-wide load j = wave +
   // 2 jj fills positions 64 j .. 64 j + 63, i.e. units 2 j + hh of row
   // hcol ^ (4 hh) for lane (hh, hcol): a lane reads one row of the tile.
-  const int dma_row = hcol ^ (4 * hh);
+  const int dma_row = hcol ^ (8 * hh);
   auto dma_src = [&](int tile) { return Tptr[tile & (kSlots - 1)][dma_row] + 16 * hh; };
   auto dma_rows = [&](const uint8_t* src, int tile, int jj) {
     const int j = wave + 2 * jj;
@@ -187,27 +188,34 @@ __global__ __launch_bounds__(kThreads, 1) void attn_m32_kernel(Args a) {
   // ---- Q^T operands.  K-step pair s < 14 (FP8 dims 32 s .. 32 s + 31): step
   // 2 s + i, K index 8 hh + e <-> dim 32 s + 16 hh + 8 i + e; RoPE step j < 4:
   // K index 8 hh + e <-> dim 448 + 16 j + 8 hh + e.
-  bf16x8 qf[32];
+  // (S^T runs on 16x16x32 products: head half hq = heads 16 hq .. +16 of the
+  // wave, K-step ks = dims 32 ks .. +32; lane l holds head 16 hq + l % 16,
+  // dims 32 ks + 8 (l / 16) .. +8.)
+  const int g = lane >> 4, i16 = lane & 15;
+  bf16x8 qf[16][2];
   {
-    const uint16_t* qp = a.q + (bq * a.H + h) * (int64_t)kD;
 #pragma unroll
-    for (int s = 0; s < 14; ++s)
+    for (int hq = 0; hq < 2; ++hq) {
+      const uint16_t* qp = a.q + (bq * a.H + blockIdx.y * 64 + wave * 32 + 16 * hq + i16) * (int64_t)kD + 8 * g;
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        qf[2 * s + i] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qp + 32 * s + 16 * hh + 8 * i));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) qf[28 + j] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qp + 448 + 16 * j + 8 * hh));
+      for (int ks = 0; ks < 16; ++ks) qf[ks][hq] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qp + 32 * ks));
+    }
   }
   // LDS byte offsets of this lane's reads within a raw tile.
-  // K (S^T A operand): entry ke = hcol, FP8 pair s at unit 2 s + hh, RoPE
-  // step j at unit 28 + 2 j + hh: unit_off(ke, 2 s + hh) = k_off + 1024 s.
-  const int ke = hcol;
-  const int k_off = unit_off(ke, hh);
+  // K (S^T A operand of entry half eh, K-step ks): row 16 eh + i16, FP8
+  // bytes 32 ks + 8 g .. +8 (unit 2 ks + g / 2, half g & 1): k_fp8[eh] + 1024
+  // ks; RoPE step ks = 14 + j: BF16 dims 448 + 32 j + 8 g (unit 28 + 4 j + g).
+  int k_fp8[2], k_rope[2][2];
+#pragma unroll
+  for (int eh = 0; eh < 2; ++eh) {
+    k_fp8[eh] = unit_off(16 * eh + i16, g >> 1) + 8 * (g & 1);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) k_rope[eh][j] = unit_off(16 * eh + i16, 28 + 4 * j + g);
+  }
   // V^T FP8 (8-bit transposing reads): 16-lane group g = lane >> 4 covers
   // dims 16 (g & 1) .. +16 of a 32-dim block (unit 2 db + (g & 1)), entries
   // of half hh = g >> 1; source lane i16 reads 8 bytes of row
   // pv_entry(c, hh, i16 >> 1), half i16 & 1: v_fp8[c] + 1024 db.
-  const int g = lane >> 4, i16 = lane & 15;
   int v_fp8[2];
 #pragma unroll
   for (int c = 0; c < 2; ++c) v_fp8[c] = unit_off(pv_entry(c, hh, i16 >> 1), g & 1) + 8 * (i16 & 1);
@@ -276,41 +284,51 @@ __global__ __launch_bounds__(kThreads, 1) void attn_m32_kernel(Args a) {
         sel_dma2(it + 2 * kBatch + 2 * wave);
       }
 
-      // ---- S^T = K Q^T in one accumulator chain that starts at the slot
-      // bias, so empty slots drop out of the softmax by themselves.
-      f32x16 sa;
+      // ---- S^T = K Q^T as four 16 x 16 blocks (entry half eh x head half
+      // hq), four independent accumulator chains; each starts at the slot
+      // bias, so empty slots drop out of the softmax.
+      f32x4 sblk[2][2];
       bool filled = false;                       // some slot of the tile holds an entry
-      {
-        const float* tbs = Tbias[ts];
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const float4 bv = *(const float4*)(tbs + 8 * q4 + 4 * hh);
-          sa[4 * q4 + 0] = bv.x; sa[4 * q4 + 1] = bv.y; sa[4 * q4 + 2] = bv.z; sa[4 * q4 + 3] = bv.w;
-          filled = filled || bv.x == 0.0f || bv.y == 0.0f || bv.z == 0.0f || bv.w == 0.0f;
-        }
+      for (int eh = 0; eh < 2; ++eh) {
+        const float4 bv = *(const float4*)(Tbias[ts] + 16 * eh + 4 * g);
+        sblk[eh][0] = f32x4{bv.x, bv.y, bv.z, bv.w};
+        sblk[eh][1] = sblk[eh][0];
+        filled = filled || bv.x == 0.0f || bv.y == 0.0f || bv.z == 0.0f || bv.w == 0.0f;
       }
       const bool tile_filled = __ballot(filled) != 0ull;
-      const float ksc = Tscl[ts][ke];
-      constexpr int kSD = 2;                     // K read distance (pairs)
-      u32x4 kr[18];
+      const float ksc[2] = {Tscl[ts][i16], Tscl[ts][16 + i16]};
+      // K operand reads in order r = 2 ks + eh: FP8 (8 bytes) for ks < 14,
+      // BF16 (16 bytes) for the RoPE steps
+      constexpr int kSD = 3;                     // K read distance (reads)
+      u32x2 kf[28];
+      u32x4 kb[4];
+      auto kread = [&](int r) {
+        const int ks = r >> 1, eh = r & 1;
+        if (ks < 14) kf[r] = *(const u32x2*)(raw + k_fp8[eh] + 1024 * ks);
+        else kb[r - 28] = *(const u32x4*)(raw + k_rope[eh][ks - 14]);
+      };
+      // The operand of read r is converted during step r - 1, into the
+      // other of two register sets, so that a conversion never writes the
+      // registers a product in flight is still reading.
+      u32x4 kop[2];
+      auto kconv = [&](int r) {
+        const int ks = r >> 1, eh = r & 1;
+        kop[r & 1] = ks < 14 ? cvt8(kf[r], ksc[eh]) : kb[r - 28];
+      };
 #pragma unroll
-      for (int s = 0; s < kSD; ++s) kr[s] = *(const u32x4*)(raw + k_off + 1024 * s);
+      for (int r = 0; r < kSD; ++r) kread(r);
+      kconv(0);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int s = 0; s < 18; ++s) {
-        // reads 0..13: FP8 pairs; 14..17: RoPE steps
-        if (s + kSD < 18) {
-          const int sn = s + kSD;
-          kr[sn] = *(const u32x4*)(raw + k_off + 1024 * sn);   // FP8 pair sn, or RoPE step sn - 14
-        }
-        if (s < 14) {
-          const u32x4 k0 = cvt8(u32x2{kr[s].x, kr[s].y}, ksc);
-          const u32x4 k1 = cvt8(u32x2{kr[s].z, kr[s].w}, ksc);
-          sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, k0), qf[2 * s], sa, 0, 0, 0);
-          sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, k1), qf[2 * s + 1], sa, 0, 0, 0);
-        } else {
-          sa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kr[s]), qf[28 + s - 14], sa, 0, 0, 0);
-        }
+      for (int r = 0; r < 32; ++r) {
+        if (r + kSD < 32) kread(r + kSD);
+        if (r + 1 < 32) kconv(r + 1);
+        const int ks = r >> 1, eh = r & 1;
+#pragma unroll
+        for (int hq = 0; hq < 2; ++hq)
+          sblk[eh][hq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kop[r & 1]), qf[ks][hq],
+                                                               sblk[eh][hq], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
 
@@ -323,9 +341,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_m32_kernel(Args a) {
       __builtin_amdgcn_sched_barrier(0);
 
       // ---- softmax: lane holds entries 8 (r >> 2) + 4 hh + (r & 3) of head h
+      // Lane 16 g + c holds, in block (eh, hq), entries 16 eh + 4 g + i of
+      // head 16 hq + c.  One 16-lane row swap per value gives lane 32 h' + hc
+      // the 16 entries 16 eh + 8 h' + e (e < 8) of head hc: x[8 eh + e].
       float x[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) x[r] = sa[r];
+      for (int eh = 0; eh < 2; ++eh)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(sblk[eh][0][i]),
+                                                           __float_as_uint(sblk[eh][1][i]), false, false);
+          x[8 * eh + i] = __uint_as_float(sw[0]);
+          x[8 * eh + 4 + i] = __uint_as_float(sw[1]);
+        }
       {
         if (!mset && tile_filled) {
           // first tile with a filled slot (slots are shared by all heads, so
@@ -352,8 +380,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_m32_kernel(Args a) {
       bf16x8 pr[2], ps[2];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const float4 s0 = *(const float4*)(Tscl[ts] + 16 * c + 4 * hh);
-        const float4 s1 = *(const float4*)(Tscl[ts] + 16 * c + 8 + 4 * hh);
+        const float4 s0 = *(const float4*)(Tscl[ts] + pv_entry(c, hh, 0));
+        const float4 s1 = *(const float4*)(Tscl[ts] + pv_entry(c, hh, 4));
         const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -367,26 +395,35 @@ __global__ __launch_bounds__(kThreads, 1) void attn_m32_kernel(Args a) {
       // blocks; rows of tile it + kLead go out between the products (their
       // table was written at least one iteration ago, their buffer was
       // freed by the barrier that ended iteration it - 1)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-#pragma unroll
-        for (int db = 0; db < 14; ++db) {
-          const int n = db + kVD;
-          if (n < 14) vf[c][n] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32*)(raw + v_fp8[c] + 1024 * n));
-          else if (c == 0) vf[1][n - 14] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32*)(raw + v_fp8[1] + 1024 * (n - 14)));
-          const u32x4 v = cvt8(u32x2{(unsigned)vf[c][db].x, (unsigned)vf[c][db].y}, 1.0f);
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v), ps[c], acc[db], 0, 0, 0);
-          const int di = 14 * c + db;            // 28 slots, 9 loads: every third
-          if (di % 3 == 1 && di / 3 < kLoadsW) dma_rows(dsrc, it + kLead, di / 3);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int bb = 0; bb < 2; ++bb) {
+      // Product f = 16 c + db (PV step c, dim block db: 14 FP8 blocks, then
+      // 2 RoPE blocks); its operand is read kVD FP8 blocks ahead and
+      // converted during product f - 1 into the other of two register sets.
+      u32x4 vop[2];
+      auto vread = [&](int n) {                  // FP8 block n of the 28 (step n / 14, block n % 14)
+        vf[n / 14][n % 14] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32*)(raw + v_fp8[n / 14] + 1024 * (n % 14)));
+      };
+      auto vconv = [&](int f) {
+        const int c = f >> 4, db = f & 15;
+        if (db < 14) {
+          vop[f & 1] = cvt8(u32x2{(unsigned)vf[c][db].x, (unsigned)vf[c][db].y}, 1.0f);
+        } else {
+          const int bb = db - 14;
           const u32x2 r0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(raw + v_rope[c][0] + 2048 * bb)));
           const u32x2 r1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(raw + v_rope[c][1] + 2048 * bb)));
-          const u32x4 v = u32x4{r0.x, r0.y, r1.x, r1.y};
-          acc[14 + bb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, v), pr[c], acc[14 + bb], 0, 0, 0);
+          vop[f & 1] = u32x4{r0.x, r0.y, r1.x, r1.y};
         }
+      };
+      vconv(0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int f = 0; f < 32; ++f) {
+        const int c = f >> 4, db = f & 15;
+        const int nf = 14 * c + (db < 14 ? db : 13) + kVD;      // FP8 read kVD blocks ahead
+        if (db < 14 && nf < 28) vread(nf);
+        if (f + 1 < 32) vconv(f + 1);
+        acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vop[f & 1]), db < 14 ? ps[c] : pr[c],
+                                                          acc[db], 0, 0, 0);
+        if (f % 3 == 1 && f / 3 < kLoadsW) dma_rows(dsrc, it + kLead, f / 3);   // 9 row loads, every third product
         __builtin_amdgcn_sched_barrier(0);
       }
       // rows of tile it+1 are in before the barrier: loads complete in
