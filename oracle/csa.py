@@ -95,6 +95,64 @@ def decode_append(x: np.ndarray, gate: np.ndarray, bias: np.ndarray, m: int, W: 
     return entries, window
 
 
+# ---------------------------------------------- RMSNorm and partial RoPE
+def rms_norm(x: np.ndarray, gain, eps: float) -> np.ndarray:
+    """RMSNorm of every last-axis row (10100 analysis, section 3 item 1,
+    auxiliary optimisations: queries and KV entries are RMS-normalised, which
+    keeps the logits from blowing up): x / sqrt(mean(x^2) + eps) * gain."""
+    x = np.asarray(x, np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * np.asarray(gain, np.float64)
+
+
+def rope_angles(positions, theta) -> np.ndarray:
+    """Rotation angle of pair i at a position: the binary32 product of the
+    position (as binary32) and theta_i (binary32), the precision in which the
+    kernels form it; [n, R/2] float64."""
+    pos32 = np.asarray(positions, np.float64).astype(np.float32)
+    th32 = np.asarray(theta, np.float32)
+    return (pos32[:, None] * th32[None, :]).astype(np.float64)
+
+
+def rope(x: np.ndarray, positions, theta, rope_dims: int) -> np.ndarray:
+    """Partial rotary position embedding (10100 analysis, section 3 item 1:
+    partial RoPE keeps relative position information; llm-tech overview:
+    the RoPE dims are the ones kept in BF16): the last rope_dims dims of each
+    row, taken as consecutive pairs (x_a, x_b), are rotated by the row's
+    angle for that pair: (x_a cos - x_b sin, x_a sin + x_b cos).  Rows
+    [n, D], positions [n], theta [rope_dims / 2]."""
+    x = np.array(x, np.float64, copy=True)
+    if rope_dims == 0:
+        return x
+    D = x.shape[-1]
+    ang = rope_angles(positions, theta)
+    c, s = np.cos(ang), np.sin(ang)
+    a = x[:, D - rope_dims::2].copy()
+    b = x[:, D - rope_dims + 1::2].copy()
+    x[:, D - rope_dims::2] = a * c - b * s
+    x[:, D - rope_dims + 1::2] = a * s + b * c
+    return x
+
+
+def entry_positions(n: int, m: int, pos0: int = 0) -> np.ndarray:
+    """Position given to compressed entry j when it is rotated: the position
+    of the last token of its block, pos0 + (j + 1) m - 1 (a block's entry
+    becomes visible at that position, so a query there and the entry get
+    the same angle; m = 1 gives each token its own position)."""
+    return pos0 + (np.arange(n, dtype=np.int64) + 1) * m - 1
+
+
+def post_rows(rows: np.ndarray, positions, gain=None, eps: float = 1e-6, theta=None, rope_dims: int = 0):
+    """RMSNorm (when gain is given), then partial RoPE (when theta is given)
+    of stored rows or queries at their positions."""
+    y = np.asarray(rows, np.float64)
+    if gain is not None:
+        y = rms_norm(y, gain, eps)
+    if theta is not None and rope_dims:
+        y = rope(y, positions, theta, rope_dims)
+    return y
+
+
 # ------------------------------------------------------------- storage rows
 def row_bytes(fmt: str, D: int, R: int = 0) -> int:
     if fmt == "f32":

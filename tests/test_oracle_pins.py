@@ -519,3 +519,95 @@ def test_kv_cache_is_about_two_percent_of_a_bf16_gqa8_cache():
     hca = (T // mh) * entry + W * entry
     ratio = (csa + hca) / (2 * T * bf16_per_layer)
     assert abs(ratio - g["kv_cache_vs_bf16_gqa8_hd128"]["value_approx"]) < 0.005, ratio
+
+
+# ------------------------------------------- RMSNorm and partial RoPE pins
+def test_rms_norm_matches_torch_and_gives_unit_rms():
+    """10100 analysis, section 3 item 1: RMSNorm of query / KV entries.
+    Against torch's own rms_norm (float64) and the closed forms: with unit
+    gain and eps = 0 every row has mean square 1; a constant row becomes
+    sign * gain."""
+    rng = np.random.default_rng(71)
+    x = rng.normal(0, 3, (40, 64))
+    gain = rng.normal(1, 0.1, 64)
+    got = O.rms_norm(x, gain, 1e-6)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (64,), weight=torch.from_numpy(gain), eps=1e-6).numpy()
+    np.testing.assert_allclose(got, ref, rtol=1e-13, atol=1e-14)
+    unit = O.rms_norm(x, np.ones(64), 0.0)
+    np.testing.assert_allclose(np.mean(unit * unit, axis=1), 1.0, rtol=1e-14)
+    const = O.rms_norm(np.full((2, 64), -2.5), gain, 0.0)
+    np.testing.assert_allclose(const, np.tile(-gain, (2, 1)), rtol=1e-14)
+
+
+def _exact_theta(R):
+    """Frequencies that are powers of two, so that every position * theta
+    below is exact in binary32 and the angle algebra holds exactly."""
+    return 2.0 ** -np.arange(R // 2, dtype=np.float64)
+
+
+def test_rope_rotates_consecutive_pairs_of_the_trailing_dims_only():
+    """Partial RoPE touches only the last R dims, pair by pair: a basis
+    vector in the bulk is unchanged; one at dim D - R + 2i moves only within
+    (D - R + 2i, D - R + 2i + 1), by the pair's angle; position 0 is the
+    identity."""
+    D, R = 16, 8
+    theta = _exact_theta(R)
+    for d in range(D):
+        e = np.zeros((1, D)); e[0, d] = 1.0
+        y = O.rope(e, [3], theta, R)[0]
+        if d < D - R:
+            assert np.array_equal(y, e[0])
+            continue
+        i = (d - (D - R)) // 2
+        a = 3 * theta[i]
+        pair = [D - R + 2 * i, D - R + 2 * i + 1]
+        assert np.all(y[[k for k in range(D) if k not in pair]] == 0.0)
+        if (d - (D - R)) % 2 == 0:
+            np.testing.assert_allclose(y[pair], [math.cos(a), math.sin(a)], rtol=1e-15, atol=1e-16)
+        else:
+            np.testing.assert_allclose(y[pair], [-math.sin(a), math.cos(a)], rtol=1e-15, atol=1e-16)
+    x = synth.normal(0, 72, (5, D))
+    assert np.array_equal(O.rope(x, np.zeros(5), theta, R), x)
+
+
+def test_rope_preserves_norms_and_scores_depend_on_relative_position_only():
+    """Rotations preserve each pair's length, and the RoPE part of a score
+    <R_p q, R_s k> equals <q, R_(s-p) k>: it depends on s - p only (exact
+    here: the angles are exact binary32 products)."""
+    D, R = 64, 16
+    theta = _exact_theta(R)
+    q = synth.normal(0, 73, (6, D))
+    k = synth.normal(0, 74, (6, D))
+    ps = np.array([0, 5, 17, 33, 100, 7])
+    ss = np.array([3, 5, 40, 2, 100, 70])
+    rq = O.rope(q, ps, theta, R)
+    rk = O.rope(k, ss, theta, R)
+    np.testing.assert_allclose(np.linalg.norm(rq[:, D - R:].reshape(6, -1, 2), axis=2),
+                               np.linalg.norm(q[:, D - R:].reshape(6, -1, 2), axis=2), rtol=1e-14)
+    lhs = np.sum(rq[:, D - R:] * rk[:, D - R:], axis=1)
+    rel = O.rope(k, ss - ps, theta, R)
+    rhs = np.sum(q[:, D - R:] * rel[:, D - R:], axis=1)
+    np.testing.assert_allclose(lhs, rhs, rtol=1e-12, atol=1e-12)
+    # composition: rotating by p then by s is rotating by p + s
+    np.testing.assert_allclose(O.rope(O.rope(q, ps, theta, R), ss, theta, R), O.rope(q, ps + ss, theta, R),
+                               rtol=1e-12, atol=1e-13)
+
+
+def test_compressed_entry_takes_the_position_of_its_block_end():
+    """A block of m equal tokens compresses to that token (softmax weights sum
+    to 1), so after the post-processing its entry must equal the token
+    post-processed at the block's last position (m-1, 2m-1, ...), the
+    position at which the entry becomes visible to queries."""
+    D, R, m = 32, 8, 4
+    theta = _exact_theta(R)
+    tok = synth.normal(0, 75, (5, 1, D))
+    x = np.repeat(tok, m, axis=1).reshape(5 * m, D)
+    gain = synth.normal(0, 76, (D,)) * 0.1 + 1.0
+    c = O.compress(x, synth.normal(0, 77, (D,)), synth.normal(0, 78, (m,)), m)
+    pos = O.entry_positions(5, m, pos0=8)
+    assert list(pos) == [11, 15, 19, 23, 27]
+    got = O.post_rows(c, pos, gain, 1e-6, theta, R)
+    want = O.post_rows(tok[:, 0], pos, gain, 1e-6, theta, R)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+    # m = 1 gives every token its own position
+    assert list(O.entry_positions(4, 1, pos0=3)) == [3, 4, 5, 6]
