@@ -54,6 +54,15 @@ class Gen:
         return x if dtype is None else x.to(dtype)
 
 
+def norm_rope(csa, gen, D, R, base=10000.0):
+    """RMSNorm (gain 1 + N(0, 0.1^2), eps 1e-6) and RoPE of the R trailing
+    dims (theta_i = base^(-2i/R)) as the library's post-processing block."""
+    import torch
+    theta = torch.pow(torch.tensor(base, dtype=torch.float64),
+                      -2.0 * torch.arange(R // 2, dtype=torch.float64) / R).float().cuda()
+    return csa.NormRope(gain=1.0 + gen.normal((D,), std=0.1), eps=1e-6, rope_dims=R, theta=theta)
+
+
 def quantised_rows(csa, gen, B, n, D, fmt, R, chunk_rows=1 << 18, cap=None):
     """A store of n RMS-normalised N(0,1) rows per batch element (cap >= n
     rows allocated), quantised by the library's own m = 1 compressor (as a
@@ -111,23 +120,30 @@ class Prefill128K:
         nws = csa.indexer_topk_workspace(1, T, self.N, k)
         self.ws = torch.empty(max(nws, 16), dtype=torch.uint8, device="cuda")
         self.tau = 1.0 / math.sqrt(D)
+        self.post = norm_rope(csa, g, D, R)
 
-    def ops(self):
+    def ops(self, post=None):
+        """The step; with `post`, RMSNorm + partial RoPE fused into the
+        compressors (stored entries and window rows) and the attention
+        kernels (queries)."""
         c = self.csa
         return [
-            ("csa_compress_kv(m=4)", lambda: c.compress_kv(self.kv, self.m, self.gate, self.bias, self.ckv)),
-            ("csa_compress_kv(window)", lambda: c.compress_kv(self.kv, 1, self.gate, self.one, self.win)),
+            ("csa_compress_kv(m=4)", lambda: c.compress_kv(self.kv, self.m, self.gate, self.bias, self.ckv,
+                                                           post=post)),
+            ("csa_compress_kv(window)", lambda: c.compress_kv(self.kv, 1, self.gate, self.one, self.win, post=post)),
             ("csa_compress_kv(idx keys)", lambda: c.compress_kv(self.xi, self.m, self.gate_i, self.bias_i, self.keys)),
             ("csa_compress_kv(idx q)", lambda: c.compress_kv(self.qi, 1, self.zero_i, self.one, self.qst)),
             ("csa_indexer_topk", lambda: c.indexer_topk(self.qst, self.w, self.keys, self.N, None, 1, self.T,
                                                         self.HI, self.m, self.k, self.sel, self.ws)),
             ("csa_sparse_attn_prefill", lambda: c.sparse_attn_prefill(self.q, self.ckv, self.N, self.sel, self.k,
                                                                       self.win, self.W, self.sink, self.tau,
-                                                                      self.out)),
-            ("hca_compress_kv(m=128)", lambda: c.compress_kv(self.kv_h, self.mh, self.gate_h, self.bias_h, self.hkv)),
-            ("hca_compress_kv(window)", lambda: c.compress_kv(self.kv_h, 1, self.gate_h, self.one, self.win_h)),
+                                                                      self.out, q_post=post)),
+            ("hca_compress_kv(m=128)", lambda: c.compress_kv(self.kv_h, self.mh, self.gate_h, self.bias_h, self.hkv,
+                                                             post=post)),
+            ("hca_compress_kv(window)", lambda: c.compress_kv(self.kv_h, 1, self.gate_h, self.one, self.win_h,
+                                                              post=post)),
             ("hca_attn", lambda: c.hca_attn(self.q_h, self.hkv, self.mh, self.Nh, None, self.win_h, self.W,
-                                            self.sink_h, self.tau, self.out_h)),
+                                            self.sink_h, self.tau, self.out_h, q_post=post)),
         ]
 
     # algorithmic work per launch
@@ -210,27 +226,31 @@ class Decode1M:
             self.hkv_tok = g.normal((B, D), rms=True, dtype=bf)
             self.h_tail = g.normal((B, mh, D), rms=True, dtype=bf)
             self.g_h, self.b_h = g.normal((D,), std=0.02), g.normal((mh,), std=0.02)
+        self.post = norm_rope(csa, g, D, R)
         # positions at which the step closes a block (CSA every m tokens, HCA every m')
         self.pos_close_m = torch.full((B,), ctx + m - 1, dtype=torch.int64, device="cuda")
         self.pos_close_mh = torch.full((B,), ctx + mh - 1, dtype=torch.int64, device="cuda")
 
-    def append_ops(self, pos, pos_h):
+    def append_ops(self, pos, pos_h, post=None):
         """Cache maintenance of the step's new token (window slot, tails, and
-        the compressed entry when a block closes at that position)."""
+        the compressed entry when a block closes at that position); `post`
+        adds RMSNorm + partial RoPE to the KV rows written."""
         c = self.csa
         o = [
             ("csa_decode_append(kv)", lambda: c.decode_append(self.kv_tok, pos, self.kv_tail, self.m, self.g_kv,
-                                                              self.b_kv, self.ckv, self.ring, self.W)),
+                                                              self.b_kv, self.ckv, self.ring, self.W, post=post)),
             ("csa_decode_append(idx keys)", lambda: c.decode_append(self.ik_tok, pos, self.ik_tail, self.m,
                                                                     self.g_ik, self.b_ik, self.keys)),
         ]
         if self.hybrid:
             o.append(("hca_decode_append(kv)", lambda: c.decode_append(self.hkv_tok, pos_h, self.h_tail, self.mh,
                                                                        self.g_h, self.b_h, self.hkv, self.ring_h,
-                                                                       self.W)))
+                                                                       self.W, post=post)))
         return o
 
-    def ops(self):
+    def ops(self, post=None):
+        """The decode step; `post` adds RMSNorm + partial RoPE of the queries
+        to the attention kernels."""
         c = self.csa
         o = [
             ("csa_compress_kv(idx q)", lambda: c.compress_kv(self.qi, 1, self.zero_i, self.one, self.qst)),
@@ -238,12 +258,12 @@ class Decode1M:
                                                         self.HI, self.m, self.k, self.sel, self.iws)),
             ("csa_sparse_attn_decode", lambda: c.sparse_attn_decode(self.q, self.ckv, self.N, self.sel, self.k,
                                                                     self.ring, self.pos, self.W, self.sink,
-                                                                    self.tau, self.out, ws=self.aws)),
+                                                                    self.tau, self.out, ws=self.aws, q_post=post)),
         ]
         if self.hybrid:
             o.append(("hca_attn(decode)", lambda: c.hca_attn(self.q_h, self.hkv, self.mh, self.Nh, self.pos[:, None],
                                                              self.ring_h, self.W, self.sink_h, self.tau, self.out_h,
-                                                             flags=c.WIN_RING, ws=self.aws)))
+                                                             flags=c.WIN_RING, ws=self.aws, q_post=post)))
         return o
 
     def unfused_window_ops(self):
@@ -416,7 +436,7 @@ def cpu_baseline(T=131072, n_sample=512, budget_s=15.0):
 
 # ------------------------------------------------------------- HBM traffic
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "csa_hca_prefill_128k_hbm_traffic.md")
-KERNEL_SOURCE = os.path.join(ROOT, "long_context_attention_15_amd", "csrc", "attn_mfma.hip")
+KERNEL_SOURCE = os.path.join(ROOT, "long_context_attention_15_amd", "csrc", "attn_m32.hip")
 
 
 def recorded_traffic(op):
@@ -489,6 +509,11 @@ def main():
         result["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": MFMA_BF16_TFLOPS,
                               "unit": "TFLOP/s", "frac": ach / MFMA_BF16_TFLOPS, "traffic": recorded_traffic(dom)}
         result["prefill_ops_tflops"] = {n: alg[n]["flops"] / (per[n] * 1e-3) / 1e12 for n in alg}
+        # RMSNorm + partial RoPE fused into the step (stored rows and queries)
+        ms_p, per_p = time_ops(pf.ops(pf.post), args.steps, args.warmup)
+        result["norm_rope_prefill"] = {"ms_per_step": ms_p, "added_ms": ms_p - ms,
+                                       "added_ms_per_op": {n: per_p[n] - per[n] for n in per
+                                                           if "idx" not in n and "indexer" not in n}}
         del pf
         torch.cuda.empty_cache()
     if args.only in ("all", "decode"):
@@ -516,6 +541,13 @@ def main():
             _, per_close = time_ops(d.append_ops(d.pos_close_m, d.pos_close_mh), args.decode_steps, 2, flush=d.flush)
             dec[name]["append_us"] = {n: v * 1e3 for n, v in per_app.items()}
             dec[name]["append_block_close_us"] = {n: v * 1e3 for n, v in per_close.items()}
+            # RMSNorm + partial RoPE: queries in the step, KV rows in the appends
+            ms_gp = time_graph(d.ops(d.post), args.decode_steps, flush=d.flush)
+            _, per_appp = time_ops(d.append_ops(d.pos_close_m, d.pos_close_mh, d.post), args.decode_steps, 2,
+                                   flush=d.flush)
+            dec[name]["norm_rope"] = {"us_per_step": ms_gp * 1e3, "added_us": (ms_gp - ms_g) * 1e3,
+                                      "append_block_close_added_us": {n: (per_appp[n] - per_close[n]) * 1e3
+                                                                      for n in per_close}}
             # row a7 on its own: partial attention + swa_merge (window and sink)
             _, per_sw = time_ops(d.unfused_window_ops(), args.decode_steps, 2, flush=d.flush)
             dec[name]["unfused_window_us"] = {n: v * 1e3 for n, v in per_sw.items()}

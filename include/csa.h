@@ -83,6 +83,38 @@ typedef struct {
   int32_t row_bytes;
 } csa_store;
 
+/*
+ * Optional post-processing of stored KV rows (csa_compress_kv,
+ * csa_decode_append) and of queries (attention entry points): RMSNorm, then
+ * partial RoPE (10100 analysis, section 3 item 1, auxiliary optimisations:
+ * RMSNorm on query / KV entries against logit blow-up, partial rotary
+ * embedding for relative position; llm-tech overview, other architecture
+ * details: the RoPE dims are the BF16 ones).  A NULL pointer to this struct
+ * means none of it.
+ *   norm_gain  DEVICE float [dim], 16-byte aligned, or NULL for no RMSNorm:
+ *              y = x / sqrt(mean(x^2) + norm_eps) * norm_gain over the row
+ *              (a query row is one head's dim values);
+ *   rope_dims  trailing dims rotated: even, 0 <= rope_dims <= dim (0: none);
+ *   rope_theta DEVICE float [rope_dims / 2]: pair i = dims (dim - rope_dims
+ *              + 2 i, dim - rope_dims + 2 i + 1) of a row at position p turns
+ *              by a = fl32(fl32(p) * rope_theta[i]):
+ *              (x, y) -> (x cos a - y sin a, x sin a + y cos a);
+ *   pos0       csa_compress_kv only: position of token row 0.  Compressed
+ *              entry j is at pos0 + (j + 1) m - 1, the last token of its
+ *              block (where it becomes visible); m = 1 rows at pos0 + j.
+ * Decode appends use the new token's position for its window row and for
+ * the entry it closes; queries use their own positions (row t, or q_pos).
+ * The processed query is rounded to the query format before it is used
+ * (BF16 queries stay BF16).
+ */
+typedef struct {
+  const float* norm_gain;
+  float norm_eps;
+  int32_t rope_dims;
+  const float* rope_theta;
+  int64_t pos0;
+} csa_norm_rope;
+
 /* flags of the attention entry points */
 #define CSA_ATTN_PARTIAL 1  /* attend to the compressed entries only: no window,
                                no sink; `out` is float32, normalised over those
@@ -125,10 +157,13 @@ const char* csa_last_error(void);   /* host string, per calling thread */
  * gate: [dim] float32; bias: [m] float32.  1 <= m <= 1024; dim in
  * {32, 64, 128, 256, 512}; MXFP4 output needs dim in {32, 64}.
  * Writes floor(T/m) rows per batch element; out_row0 + floor(T/m) <= out.cap.
+ * post (nullable): RMSNorm and partial RoPE of each entry before it is
+ * quantised (see csa_norm_rope).
  */
 csa_status csa_compress_kv(const void* tok, int tok_fmt, int B, int64_t T, int64_t tok_bstride,
                            int m, const float* gate, const float* bias,
-                           csa_store out, int64_t out_row0, hipStream_t stream);
+                           csa_store out, int64_t out_row0, const csa_norm_rope* post,
+                           hipStream_t stream);
 
 /*
  * csa_decode_append -- cache maintenance for one decoded token per sequence
@@ -153,11 +188,12 @@ csa_status csa_compress_kv(const void* tok, int tok_fmt, int B, int64_t T, int64
  * tokens of its current block (from prefill, or earlier calls).
  * tok: [B][dim] (CSA_F32 or CSA_BF16), 16-byte aligned, as is tail.
  * dim, formats and rope_dim as for csa_compress_kv; win.dim == out.dim,
- * 1 <= W <= win.cap.
+ * 1 <= W <= win.cap.  post (nullable) as for csa_compress_kv, at position p
+ * for both the window row and the entry (pos0 is not used).
  */
 csa_status csa_decode_append(const void* tok, int tok_fmt, int B, const int64_t* pos, void* tail, int tail_rows,
                              int m, const float* gate, const float* bias, csa_store out, csa_store win, int W,
-                             hipStream_t stream);
+                             const csa_norm_rope* post, hipStream_t stream);
 
 /*
  * csa_indexer_topk -- Lightning Indexer scores and top-k selection
@@ -199,11 +235,14 @@ csa_status csa_indexer_topk(csa_store q_idx, const float* head_w, csa_store keys
  * sink: float32 [H] or NULL (= -inf).  out: [B][T][H][dim] in q_fmt (float32
  * with CSA_ATTN_PARTIAL).  lse: float32 [B][T][H] or NULL.
  * Indices outside [0, n_entries) in sel are skipped.
+ * q_post (nullable): RMSNorm and partial RoPE of each query head row at its
+ * position before it is used (see csa_norm_rope; pos0 is not used).
  */
 csa_status csa_sparse_attn_prefill(const void* q, int q_fmt, int B, int T, int H,
                                    csa_store ckv, int64_t n_entries, const int32_t* sel, int k,
                                    csa_store win, int W, const float* sink, float sm_scale,
-                                   void* out, float* lse, int flags, hipStream_t stream);
+                                   void* out, float* lse, int flags, const csa_norm_rope* q_post,
+                                   hipStream_t stream);
 
 /* Workspace bytes of csa_sparse_attn_decode / hca_attn for these sizes. */
 size_t csa_attn_workspace(int B, int Tq, int H, int dim, int64_t max_list);
@@ -215,13 +254,13 @@ size_t csa_attn_workspace(int B, int Tq, int H, int dim, int64_t max_list);
  * Same arithmetic as the prefill.  ws: optional; NULL runs each sequence in
  * one workgroup per head group, otherwise >= csa_attn_workspace(B, 1, H,
  * dim, k + W) bytes (CSA_EWORKSPACE if smaller) lets long lists be split
- * across workgroups and merged in a fixed order.
+ * across workgroups and merged in a fixed order.  q_post as for the prefill.
  */
 csa_status csa_sparse_attn_decode(const void* q, int q_fmt, int B, int H, csa_store ckv,
                                   int64_t n_entries, const int32_t* sel, int k, csa_store ring,
                                   const int64_t* pos, int W, const float* sink, float sm_scale,
                                   void* out, float* lse, int flags, void* ws, size_t ws_bytes,
-                                  hipStream_t stream);
+                                  const csa_norm_rope* q_post, hipStream_t stream);
 
 /*
  * csa_sparse_attn_decode_noalloc -- csa_sparse_attn_decode for callers that
@@ -240,7 +279,8 @@ csa_status csa_sparse_attn_decode(const void* q, int q_fmt, int B, int H, csa_st
 csa_status csa_sparse_attn_decode_noalloc(const void* q, int q_fmt, int B, int H, csa_store ckv,
                                           int64_t n_entries, const int32_t* sel, int k, csa_store ring,
                                           const int64_t* pos, int W, const float* sink, float sm_scale,
-                                          void* out, float* lse, int flags, hipStream_t stream);
+                                          void* out, float* lse, int flags, const csa_norm_rope* q_post,
+                                          hipStream_t stream);
 
 /*
  * hca_attn -- HCA dense attention (kenelite analysis section 6; model-card
@@ -250,12 +290,12 @@ csa_status csa_sparse_attn_decode_noalloc(const void* q, int q_fmt, int B, int H
  * win: position-indexed raw rows, or a ring with CSA_WIN_RING.
  * ws: optional, as for csa_sparse_attn_decode, sized by
  * csa_attn_workspace(B, Tq, H, dim, n_entries + W) (0 for calls with enough
- * queries to fill the GPU).
+ * queries to fill the GPU).  q_post as for csa_sparse_attn_prefill.
  */
 csa_status hca_attn(const void* q, int q_fmt, int B, int Tq, int H, csa_store hkv, int m_prime,
                     int64_t n_entries, const int64_t* q_pos, csa_store win, int W,
                     const float* sink, float sm_scale, void* out, float* lse, int flags,
-                    void* ws, size_t ws_bytes, hipStream_t stream);
+                    void* ws, size_t ws_bytes, const csa_norm_rope* q_post, hipStream_t stream);
 
 /*
  * swa_merge -- sliding-window attention merged with a partial result
@@ -263,11 +303,13 @@ csa_status hca_attn(const void* q, int q_fmt, int B, int Tq, int H, csa_store hk
  *   o = (e^{lse_p} o_p + sum_w e^{l_w} v_w) / (e^{lse_p} + sum_w e^{l_w} + e^{sink}).
  * part_out: float32 [B][Tq][H][dim]; part_lse: float32 [B][Tq][H].
  * q_pos / win / flags as in hca_attn (CSA_WIN_RING only).  out: q_fmt.
+ * q_post as for csa_sparse_attn_prefill (the partial must come from the
+ * same processed queries).
  */
 csa_status swa_merge(const void* q, int q_fmt, int B, int Tq, int H, csa_store win,
                      const int64_t* q_pos, int W, int flags, const float* part_out,
                      const float* part_lse, const float* sink, float sm_scale, void* out,
-                     hipStream_t stream);
+                     const csa_norm_rope* q_post, hipStream_t stream);
 
 /*
  * csa_diag_counters -- diagnostics for tests and benchmarks.

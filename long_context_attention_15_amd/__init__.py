@@ -35,6 +35,31 @@ class _CStore(ctypes.Structure):
                 ("row_bytes", ctypes.c_int32)]
 
 
+class _CNormRope(ctypes.Structure):
+    _fields_ = [("norm_gain", ctypes.c_void_p), ("norm_eps", ctypes.c_float), ("rope_dims", ctypes.c_int32),
+                ("rope_theta", ctypes.c_void_p), ("pos0", ctypes.c_int64)]
+
+
+@dataclass
+class NormRope:
+    """csa_norm_rope: RMSNorm (gain: float32 [dim] device tensor, or None) then
+    partial RoPE of the last rope_dims dims (theta: float32 [rope_dims/2]
+    device tensor) of stored rows or queries; pos0 = position of token row 0
+    for csa_compress_kv."""
+    gain: object = None
+    eps: float = 1e-6
+    rope_dims: int = 0
+    theta: object = None
+    pos0: int = 0
+
+    def c(self) -> "_CNormRope":
+        return _CNormRope(_ptr(self.gain), self.eps, self.rope_dims, _ptr(self.theta), self.pos0)
+
+
+def _post(p):
+    return None if p is None else ctypes.byref(p.c())
+
+
 _lib: Optional[ctypes.CDLL] = None
 
 _P, _I, _I64, _F, _SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
@@ -42,20 +67,20 @@ _SIGS = {
     "csa_version": ([], ctypes.c_char_p),
     "csa_status_string": ([_I], ctypes.c_char_p),
     "csa_last_error": ([], ctypes.c_char_p),
-    "csa_compress_kv": ([_P, _I, _I, _I64, _I64, _I, _P, _P, _CStore, _I64, _P], _I),
-    "csa_decode_append": ([_P, _I, _I, _P, _P, _I, _I, _P, _P, _CStore, _CStore, _I, _P], _I),
+    "csa_compress_kv": ([_P, _I, _I, _I64, _I64, _I, _P, _P, _CStore, _I64, _P, _P], _I),
+    "csa_decode_append": ([_P, _I, _I, _P, _P, _I, _I, _P, _P, _CStore, _CStore, _I, _P, _P], _I),
     "csa_indexer_topk_workspace": ([_I, _I, _I64, _I], _SZ),
     "csa_indexer_topk": ([_CStore, _P, _CStore, _I64, _P, _I, _I, _I, _I, _I, _P, _P, _SZ, _P], _I),
     "csa_attn_workspace": ([_I, _I, _I, _I, _I64], _SZ),
     "csa_sparse_attn_prefill": ([_P, _I, _I, _I, _I, _CStore, _I64, _P, _I, _CStore, _I, _P, _F, _P, _P, _I,
-                                 _P], _I),
+                                 _P, _P], _I),
     "csa_sparse_attn_decode": ([_P, _I, _I, _I, _CStore, _I64, _P, _I, _CStore, _P, _I, _P, _F, _P, _P, _I, _P,
-                                _SZ, _P], _I),
-    "hca_attn": ([_P, _I, _I, _I, _I, _CStore, _I, _I64, _P, _CStore, _I, _P, _F, _P, _P, _I, _P, _SZ, _P], _I),
-    "swa_merge": ([_P, _I, _I, _I, _I, _CStore, _P, _I, _I, _P, _P, _P, _F, _P, _P], _I),
+                                _SZ, _P, _P], _I),
+    "hca_attn": ([_P, _I, _I, _I, _I, _CStore, _I, _I64, _P, _CStore, _I, _P, _F, _P, _P, _I, _P, _SZ, _P, _P], _I),
+    "swa_merge": ([_P, _I, _I, _I, _I, _CStore, _P, _I, _I, _P, _P, _P, _F, _P, _P, _P], _I),
     "csa_diag_counters": ([_P, _I, _I], _I),
     "csa_sparse_attn_decode_noalloc": ([_P, _I, _I, _I, _CStore, _I64, _P, _I, _CStore, _P, _I, _P, _F, _P, _P, _I,
-                                        _P], _I),
+                                        _P, _P], _I),
 }
 EXPORTS = tuple(_SIGS)
 
@@ -161,16 +186,17 @@ def diag_counters(reset: bool = False):
 
 
 # ------------------------------------------------------------- entry points
-def compress_kv(tok, m: int, gate, bias, out: Store, out_row0: int = 0, stream=None):
+def compress_kv(tok, m: int, gate, bias, out: Store, out_row0: int = 0, post: Optional[NormRope] = None,
+                stream=None):
     """csa_compress_kv: tok [B][T][dim] float32 or bfloat16 (rows contiguous)."""
     B, T, D = tok.shape
     assert tok.stride(2) == 1 and tok.stride(1) == D, "token rows must be contiguous"
     _check(load().csa_compress_kv(_ptr(tok), _fmt_of(tok), B, T, tok.stride(0), m, _ptr(gate), _ptr(bias),
-                                  out.c(), out_row0, _stream(stream)), "csa_compress_kv")
+                                  out.c(), out_row0, _post(post), _stream(stream)), "csa_compress_kv")
 
 
 def decode_append(tok, pos, tail, m: int, gate, bias, out: Store, win: Optional[Store] = None, W: int = 0,
-                  stream=None):
+                  post: Optional[NormRope] = None, stream=None):
     """csa_decode_append: tok [B][dim] float32 or bfloat16, pos [B] int64, tail [B][R][dim] (tok's dtype,
     R a multiple of m); window row pos mod W of `win` when given, entry (pos+1)/m - 1 of `out` when a
     block closes."""
@@ -179,7 +205,8 @@ def decode_append(tok, pos, tail, m: int, gate, bias, out: Store, win: Optional[
     assert tail.shape[2] == D and pos.dtype.itemsize == 8 and pos.numel() == B
     wc = win.c() if win is not None else _CStore(None, None, 0, 0, 0, 0, 0)
     _check(load().csa_decode_append(_ptr(tok), _fmt_of(tok), B, _ptr(pos), _ptr(tail), int(tail.shape[1]), m,
-                                    _ptr(gate), _ptr(bias), out.c(), wc, W, _stream(stream)), "csa_decode_append")
+                                    _ptr(gate), _ptr(bias), out.c(), wc, W, _post(post), _stream(stream)),
+           "csa_decode_append")
 
 
 def indexer_topk_workspace(B: int, Tq: int, n_entries: int, k: int) -> int:
@@ -199,46 +226,52 @@ def attn_workspace(B: int, Tq: int, H: int, dim: int, max_list: int) -> int:
 
 
 def sparse_attn_prefill(q, ckv: Store, n_entries: int, sel, k: int, win: Store, W: int, sink, sm_scale: float,
-                        out, lse=None, flags: int = 0, stream=None):
+                        out, lse=None, flags: int = 0, q_post: Optional[NormRope] = None, stream=None):
     """csa_sparse_attn_prefill: q [B][T][H][dim]."""
     B, T, H, D = q.shape
     _check(load().csa_sparse_attn_prefill(_ptr(q), _fmt_of(q), B, T, H, ckv.c(), n_entries, _ptr(sel), k, win.c(),
-                                          W, _ptr(sink), sm_scale, _ptr(out), _ptr(lse), flags, _stream(stream)),
+                                          W, _ptr(sink), sm_scale, _ptr(out), _ptr(lse), flags, _post(q_post),
+                                          _stream(stream)),
            "csa_sparse_attn_prefill")
 
 
 def sparse_attn_decode(q, ckv: Store, n_entries: int, sel, k: int, ring: Store, pos, W: int, sink,
-                       sm_scale: float, out, lse=None, flags: int = 0, ws=None, stream=None):
+                       sm_scale: float, out, lse=None, flags: int = 0, ws=None, q_post: Optional[NormRope] = None,
+                       stream=None):
     """csa_sparse_attn_decode: q [B][H][dim], pos int64 [B]."""
     B, H, D = q.shape
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
     _check(load().csa_sparse_attn_decode(_ptr(q), _fmt_of(q), B, H, ckv.c(), n_entries, _ptr(sel), k, ring.c(),
                                          _ptr(pos), W, _ptr(sink), sm_scale, _ptr(out), _ptr(lse), flags, _ptr(ws),
-                                         wsb, _stream(stream)), "csa_sparse_attn_decode")
+                                         wsb, _post(q_post), _stream(stream)), "csa_sparse_attn_decode")
 
 
 def sparse_attn_decode_noalloc(q, ckv: Store, n_entries: int, sel, k: int, ring: Store, pos, W: int, sink,
-                               sm_scale: float, out, lse=None, flags: int = 0, stream=None):
+                               sm_scale: float, out, lse=None, flags: int = 0, q_post: Optional[NormRope] = None,
+                               stream=None):
     """csa_sparse_attn_decode_noalloc: as sparse_attn_decode, split partials in the library's device scratch."""
     B, H, D = q.shape
     _check(load().csa_sparse_attn_decode_noalloc(_ptr(q), _fmt_of(q), B, H, ckv.c(), n_entries, _ptr(sel), k,
                                                  ring.c(), _ptr(pos), W, _ptr(sink), sm_scale, _ptr(out), _ptr(lse),
-                                                 flags, _stream(stream)), "csa_sparse_attn_decode_noalloc")
+                                                 flags, _post(q_post), _stream(stream)),
+           "csa_sparse_attn_decode_noalloc")
 
 
 def hca_attn(q, hkv: Store, m_prime: int, n_entries: int, q_pos, win: Store, W: int, sink, sm_scale: float,
-             out, lse=None, flags: int = 0, ws=None, stream=None):
+             out, lse=None, flags: int = 0, ws=None, q_post: Optional[NormRope] = None, stream=None):
     """hca_attn: q [B][Tq][H][dim]; q_pos int64 [B][Tq] or None (prefill)."""
     B, Tq, H, D = q.shape
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
     _check(load().hca_attn(_ptr(q), _fmt_of(q), B, Tq, H, hkv.c(), m_prime, n_entries, _ptr(q_pos), win.c(), W,
-                           _ptr(sink), sm_scale, _ptr(out), _ptr(lse), flags, _ptr(ws), wsb, _stream(stream)),
+                           _ptr(sink), sm_scale, _ptr(out), _ptr(lse), flags, _ptr(ws), wsb, _post(q_post),
+                           _stream(stream)),
            "hca_attn")
 
 
 def swa_merge(q, win: Store, q_pos, W: int, flags: int, part_out, part_lse, sink, sm_scale: float, out,
-              stream=None):
+              q_post: Optional[NormRope] = None, stream=None):
     """swa_merge: q [B][Tq][H][dim]; part_out float32 like q; part_lse [B][Tq][H]."""
     B, Tq, H, D = q.shape
     _check(load().swa_merge(_ptr(q), _fmt_of(q), B, Tq, H, win.c(), _ptr(q_pos), W, flags, _ptr(part_out),
-                            _ptr(part_lse), _ptr(sink), sm_scale, _ptr(out), _stream(stream)), "swa_merge")
+                            _ptr(part_lse), _ptr(sink), sm_scale, _ptr(out), _post(q_post), _stream(stream)),
+           "swa_merge")

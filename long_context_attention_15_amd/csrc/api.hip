@@ -96,6 +96,19 @@ csa_status check_q(const void* q, int q_fmt, int H, int dim, const void* out) {
 
 #define CSA_TRY(x) do { csa_status _s = (x); if (_s != CSA_OK) return _s; } while (0)
 
+// The optional RMSNorm / partial RoPE of rows of `dim` values.
+csa_status check_post(const csa_norm_rope* p, int dim, const char* name) {
+  if (!p) return CSA_OK;
+  if (p->norm_gain && !aligned(p->norm_gain, 16)) return fail(CSA_EINVAL, "%s.norm_gain must be 16-byte aligned", name);
+  if (p->norm_gain && (!std::isfinite(p->norm_eps) || p->norm_eps < 0.0f))
+    return fail(CSA_EINVAL, "%s.norm_eps must be finite and >= 0", name);
+  if (p->rope_dims < 0 || p->rope_dims > dim || p->rope_dims % 2 != 0)
+    return fail(CSA_EINVAL, "%s.rope_dims = %d must be even and within [0, %d]", name, p->rope_dims, dim);
+  if (p->rope_dims > 0 && (!p->rope_theta || !aligned(p->rope_theta, 4)))
+    return fail(CSA_EINVAL, "%s.rope_theta must be a 4-byte aligned array when rope_dims > 0", name);
+  return CSA_OK;
+}
+
 // Scratch of the allocation-free decode entry point: split partials of the
 // decode attention (float32 o, m, l per head and split).  Each device holds
 // its own copy for the life of the process.  In host code `scratch` names a
@@ -148,7 +161,7 @@ const char* csa_last_error(void) { return g_err; }
 
 csa_status csa_compress_kv(const void* tok, int tok_fmt, int B, int64_t T, int64_t tok_bstride, int m,
                            const float* gate, const float* bias, csa_store out, int64_t out_row0,
-                           hipStream_t stream) {
+                           const csa_norm_rope* post, hipStream_t stream) {
   g_err[0] = 0;
   if (B < 0 || T < 0) return fail(CSA_EINVAL, "B and T must be >= 0");
   if (m < 1 || m > csa::compress_max_m()) return fail(CSA_EINVAL, "m = %d outside [1, %d]", m, csa::compress_max_m());
@@ -164,13 +177,15 @@ csa_status csa_compress_kv(const void* tok, int tok_fmt, int B, int64_t T, int64
     return fail(CSA_EUNSUPPORTED, "rope_dim must be a multiple of dim / 64");
   if (out.fmt == CSA_MXFP4 && out.dim > 64) return fail(CSA_EUNSUPPORTED, "MXFP4 output needs dim <= 64");
   if (out_row0 < 0 || out_row0 + T / m > out.cap) return fail(CSA_EINVAL, "out_row0 + floor(T/m) > out.cap");
-  return launched(csa::launch_compress(tok, tok_fmt, B, T, tok_bstride, m, gate, bias, out, out_row0, stream), stream,
-                  "csa_compress_kv launch");
+  CSA_TRY(check_post(post, out.dim, "post"));
+  return launched(csa::launch_compress(tok, tok_fmt, B, T, tok_bstride, m, gate, bias, out, out_row0,
+                                       csa::norm_rope_of(post), stream),
+                  stream, "csa_compress_kv launch");
 }
 
 csa_status csa_decode_append(const void* tok, int tok_fmt, int B, const int64_t* pos, void* tail, int tail_rows,
                              int m, const float* gate, const float* bias, csa_store out, csa_store win, int W,
-                             hipStream_t stream) {
+                             const csa_norm_rope* post, hipStream_t stream) {
   g_err[0] = 0;
   if (B < 0) return fail(CSA_EINVAL, "B must be >= 0");
   if (m < 1 || m > csa::compress_max_m()) return fail(CSA_EINVAL, "m = %d outside [1, %d]", m, csa::compress_max_m());
@@ -190,7 +205,9 @@ csa_status csa_decode_append(const void* tok, int tok_fmt, int B, const int64_t*
     if (win.fmt == CSA_FP8_E4M3 && win.rope_dim % vpl != 0)
       return fail(CSA_EUNSUPPORTED, "win.rope_dim must be a multiple of dim / 64");
   }
-  return launched(csa::launch_decode_append(tok, tok_fmt, B, pos, tail, tail_rows, m, gate, bias, out, win, W, stream),
+  CSA_TRY(check_post(post, out.dim, "post"));
+  return launched(csa::launch_decode_append(tok, tok_fmt, B, pos, tail, tail_rows, m, gate, bias, out, win, W,
+                                            csa::norm_rope_of(post), stream),
                   stream, "csa_decode_append launch");
 }
 
@@ -232,7 +249,10 @@ size_t csa_attn_workspace(int B, int Tq, int H, int dim, int64_t max_list) {
   return csa::attn_workspace(B, Tq, H, dim, max_list);
 }
 
-static csa_status run_attn(csa::AttnCall& c, int flags, hipStream_t stream, const char* what) {
+static csa_status run_attn(csa::AttnCall& c, int flags, const csa_norm_rope* q_post, hipStream_t stream,
+                           const char* what) {
+  CSA_TRY(check_post(q_post, c.D, "q_post"));
+  c.qn = csa::norm_rope_of(q_post);
   if (flags & ~(CSA_ATTN_PARTIAL | CSA_WIN_RING | CSA_BATCH_INVARIANT))
     return fail(CSA_EINVAL, "unknown flags 0x%x", flags);
   if (!std::isfinite(c.tau)) return fail(CSA_EINVAL, "sm_scale must be finite");
@@ -263,7 +283,7 @@ static csa::AttnCall base_call(const void* q, int q_fmt, int B, int Tq, int H, i
 csa_status csa_sparse_attn_prefill(const void* q, int q_fmt, int B, int T, int H, csa_store ckv,
                                    int64_t n_entries, const int32_t* sel, int k, csa_store win, int W,
                                    const float* sink, float sm_scale, void* out, float* lse, int flags,
-                                   hipStream_t stream) {
+                                   const csa_norm_rope* q_post, hipStream_t stream) {
   g_err[0] = 0;
   if (B < 0 || T < 0) return fail(CSA_EINVAL, "B and T must be >= 0");
   CSA_TRY(check_store(ckv, "ckv"));
@@ -278,13 +298,13 @@ csa_status csa_sparse_attn_prefill(const void* q, int q_fmt, int B, int T, int H
   csa::AttnCall c = base_call(q, q_fmt, B, T, H, ckv.dim, sm_scale, sink, out, lse);
   c.ckv = ckv; c.n_entries = n_entries; c.mode = csa::kModeSel; c.sel = sel; c.k = k; c.m = 1;
   c.win = win; c.W = W; c.ring = 0;
-  return run_attn(c, flags, stream, "csa_sparse_attn_prefill launch");
+  return run_attn(c, flags, q_post, stream, "csa_sparse_attn_prefill launch");
 }
 
 csa_status csa_sparse_attn_decode(const void* q, int q_fmt, int B, int H, csa_store ckv, int64_t n_entries,
                                   const int32_t* sel, int k, csa_store ring, const int64_t* pos, int W,
                                   const float* sink, float sm_scale, void* out, float* lse, int flags,
-                                  void* ws, size_t ws_bytes, hipStream_t stream) {
+                                  void* ws, size_t ws_bytes, const csa_norm_rope* q_post, hipStream_t stream) {
   g_err[0] = 0;
   if (B < 0) return fail(CSA_EINVAL, "B must be >= 0");
   CSA_TRY(check_store(ckv, "ckv"));
@@ -298,13 +318,13 @@ csa_status csa_sparse_attn_decode(const void* q, int q_fmt, int B, int H, csa_st
   csa::AttnCall c = base_call(q, q_fmt, B, 1, H, ckv.dim, sm_scale, sink, out, lse);
   c.ckv = ckv; c.n_entries = n_entries; c.mode = csa::kModeSel; c.sel = sel; c.k = k; c.m = 1;
   c.win = ring; c.W = W; c.ring = 1; c.q_pos = pos; c.ws = ws; c.ws_bytes = ws_bytes;
-  return run_attn(c, flags | 0, stream, "csa_sparse_attn_decode launch");
+  return run_attn(c, flags, q_post, stream, "csa_sparse_attn_decode launch");
 }
 
 csa_status csa_sparse_attn_decode_noalloc(const void* q, int q_fmt, int B, int H, csa_store ckv, int64_t n_entries,
                                           const int32_t* sel, int k, csa_store ring, const int64_t* pos, int W,
                                           const float* sink, float sm_scale, void* out, float* lse, int flags,
-                                          hipStream_t stream) {
+                                          const csa_norm_rope* q_post, hipStream_t stream) {
   g_err[0] = 0;
   if (B < 0 || H < 1 || k < 1) return fail(CSA_EINVAL, "B >= 0, H >= 1 and k >= 1 needed");
   const int64_t max_list = (int64_t)k + ((flags & CSA_ATTN_PARTIAL) ? 0 : (W > 0 ? W : 0));
@@ -315,13 +335,13 @@ csa_status csa_sparse_attn_decode_noalloc(const void* q, int q_fmt, int B, int H
   void* ws = nullptr;
   if (need > 0) CSA_TRY(scratch_of_current_device(&ws));
   return csa_sparse_attn_decode(q, q_fmt, B, H, ckv, n_entries, sel, k, ring, pos, W, sink, sm_scale, out, lse, flags,
-                                ws, need > 0 ? kScratchBytes : 0, stream);
+                                ws, need > 0 ? kScratchBytes : 0, q_post, stream);
 }
 
 csa_status hca_attn(const void* q, int q_fmt, int B, int Tq, int H, csa_store hkv, int m_prime,
                     int64_t n_entries, const int64_t* q_pos, csa_store win, int W, const float* sink,
                     float sm_scale, void* out, float* lse, int flags, void* ws, size_t ws_bytes,
-                    hipStream_t stream) {
+                    const csa_norm_rope* q_post, hipStream_t stream) {
   g_err[0] = 0;
   if (B < 0 || Tq < 0) return fail(CSA_EINVAL, "B and Tq must be >= 0");
   if (m_prime < 1) return fail(CSA_EINVAL, "m_prime < 1");
@@ -339,12 +359,12 @@ csa_status hca_attn(const void* q, int q_fmt, int B, int Tq, int H, csa_store hk
   csa::AttnCall c = base_call(q, q_fmt, B, Tq, H, hkv.dim, sm_scale, sink, out, lse);
   c.ckv = hkv; c.n_entries = n_entries; c.mode = csa::kModeRange; c.m = m_prime;
   c.win = win; c.W = W; c.ring = ring; c.q_pos = q_pos; c.ws = ws; c.ws_bytes = ws_bytes;
-  return run_attn(c, flags, stream, "hca_attn launch");
+  return run_attn(c, flags, q_post, stream, "hca_attn launch");
 }
 
 csa_status swa_merge(const void* q, int q_fmt, int B, int Tq, int H, csa_store win, const int64_t* q_pos, int W,
                      int flags, const float* part_out, const float* part_lse, const float* sink, float sm_scale,
-                     void* out, hipStream_t stream) {
+                     void* out, const csa_norm_rope* q_post, hipStream_t stream) {
   g_err[0] = 0;
   if (B < 0 || Tq < 0) return fail(CSA_EINVAL, "B and Tq must be >= 0");
   if (flags & CSA_ATTN_PARTIAL) return fail(CSA_EINVAL, "swa_merge takes no CSA_ATTN_PARTIAL flag");
@@ -360,7 +380,7 @@ csa_status swa_merge(const void* q, int q_fmt, int B, int Tq, int H, csa_store w
   csa::AttnCall c = base_call(q, q_fmt, B, Tq, H, win.dim, sm_scale, sink, out, nullptr);
   c.mode = csa::kModeNone; c.win = win; c.W = W; c.ring = ring; c.q_pos = q_pos;
   c.prior_o = part_out; c.prior_lse = part_lse;
-  return run_attn(c, flags, stream, "swa_merge launch");
+  return run_attn(c, flags, q_post, stream, "swa_merge launch");
 }
 
 csa_status csa_diag_counters(uint64_t* out, int n, int reset) {

@@ -25,6 +25,7 @@ struct AttnArgs {
   const float* prior_o; const float* prior_lse;
   void* out; int out_f32; float* lse; int partial;
   int nsplit; int split_len; float* ws;
+  NormRope qn;
 };
 
 __device__ __forceinline__ int64_t query_pos(const AttnArgs& a, int64_t bq) {
@@ -111,6 +112,36 @@ __global__ __launch_bounds__(kAttnThreads) void attn_valu_kernel(AttnArgs a) {
     const int d = p + TPH * r;
     qv[r] = a.q_f32 ? ((const float*)a.q)[qoff + d] : bf16_to_f32(((const uint16_t*)a.q)[qoff + d]);
     o[r] = 0.0f;
+  }
+  if (a.qn.gain || a.qn.rope_dims > 0) {         // uniform: RMSNorm / partial RoPE of the query row
+    if (a.qn.gain) {
+      float ss = 0.0f;
+#pragma unroll
+      for (int r = 0; r < DPT; ++r) ss = fmaf(qv[r], qv[r], ss);
+#pragma unroll
+      for (int off = TPH / 2; off > 0; off >>= 1) ss += __shfl_xor(ss, off, TPH);
+      const float rr = 1.0f / sqrtf(ss / (float)D + a.qn.eps);
+#pragma unroll
+      for (int r = 0; r < DPT; ++r) qv[r] = qv[r] * rr * a.qn.gain[p + TPH * r];
+    }
+    if (a.qn.rope_dims > 0) {                     // the pair partner of dim d is dim d ^ 1, in thread p ^ 1
+      const int d0 = D - a.qn.rope_dims;
+      const float pf = (float)t;
+#pragma unroll
+      for (int r = 0; r < DPT; ++r) {
+        const int d = p + TPH * r;
+        const float other = __shfl_xor(qv[r], 1, TPH);
+        if (d >= d0) {
+          float x = (d & 1) ? other : qv[r], y = (d & 1) ? qv[r] : other;
+          rope_pair(x, y, pf, a.qn.theta[(d - d0) >> 1]);
+          qv[r] = (d & 1) ? y : x;
+        }
+      }
+    }
+    if (!a.q_f32) {                               // BF16 queries stay BF16
+#pragma unroll
+      for (int r = 0; r < DPT; ++r) qv[r] = bf16_to_f32(f32_to_bf16(qv[r]));
+    }
   }
   float mrun = -INFINITY, lrun = 0.0f;
   if (a.prior_o) {
@@ -349,6 +380,7 @@ hipError_t launch_attn(const AttnCall& c, hipStream_t st) {
   a.W = c.W; a.ring = c.ring; a.q_pos = c.q_pos;
   a.sink = c.sink; a.tau = c.tau; a.prior_o = c.prior_o; a.prior_lse = c.prior_lse;
   a.out = c.out; a.out_f32 = c.partial || c.q_fmt == CSA_F32; a.lse = c.lse; a.partial = c.partial;
+  a.qn = c.qn;
   const int64_t max_list = (c.mode == kModeSel ? c.k : (c.mode == kModeRange ? c.n_entries : 0)) + c.W;
   int len = 0;
   const bool mfma = attn_mfma_eligible(c.q_fmt, c.H, c.D, c.ckv.rows ? c.ckv : c.win, c.prior_o != nullptr, c.tau);

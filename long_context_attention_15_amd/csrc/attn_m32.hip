@@ -67,6 +67,7 @@ struct Args {
   const float* sink; float tau;
   void* out; int out_f32; float* lse; int partial;
   int nsplit; int split_len; float* ws;
+  NormRope qn;
 };
 
 // Zero row that empty slots gather from (device globals start zeroed).
@@ -199,6 +200,44 @@ __global__ __launch_bounds__(kThreads, 1) void attn_m32_kernel(Args a) {
       const uint16_t* qp = a.q + (bq * a.H + blockIdx.y * 64 + wave * 32 + 16 * hq + i16) * (int64_t)kD + 8 * g;
 #pragma unroll
       for (int ks = 0; ks < 16; ++ks) qf[ks][hq] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qp + 32 * ks));
+    }
+  }
+  if (a.qn.gain || a.qn.rope_dims > 0) {          // uniform: RMSNorm / partial RoPE of the query rows
+    const float pf = (float)t;
+    const int d0 = kD - a.qn.rope_dims;
+#pragma unroll
+    for (int hq = 0; hq < 2; ++hq) {
+      float rr = 1.0f;
+      if (a.qn.gain) {                            // a head's 512 dims: 4 lanes (i16 + 16 g) x 128
+        float ss = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ss = fmaf((float)qf[ks][hq][e], (float)qf[ks][hq][e], ss);
+        ss += __shfl_xor(ss, 16);
+        ss += __shfl_xor(ss, 32);
+        rr = 1.0f / sqrtf(ss / (float)kD + a.qn.eps);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks) {
+        const int dd = 32 * ks + 8 * g;           // this lane's 8 dims of K-step ks
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (float)qf[ks][hq][e];
+        if (a.qn.gain) {
+          const float4 g0 = *(const float4*)(a.qn.gain + dd), g1 = *(const float4*)(a.qn.gain + dd + 4);
+          const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = v[e] * rr * gv[e];
+        }
+        if (a.qn.rope_dims > 0) {
+#pragma unroll
+          for (int e = 0; e < 8; e += 2)
+            if (dd + e >= d0) rope_pair(v[e], v[e + 1], pf, a.qn.theta[(dd + e - d0) >> 1]);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[ks][hq][e] = (__bf16)v[e];   // BF16 queries stay BF16
+      }
     }
   }
   // LDS byte offsets of this lane's reads within a raw tile.
@@ -522,6 +561,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_m32_kernel(Args a) {
 
 }  // namespace
 
+// The kernel masks empty slots through a -1e30 logit: the scaled logit of an
+// empty slot (about -1e30 tau log2 e in base 2) must lie far below anything
+// exp2 can resolve, so it takes scales above 1e4 / (1e30 log2 e) only; other
+// scales (tiny, zero or negative) take the general kernel.
+bool attn_mfma_eligible(int q_fmt, int H, int D, const csa_store& kv, bool has_prior, float tau) {
+  return !has_prior && tau * kLog2e * 1.0e30f >= 1.0e4f && q_fmt == CSA_BF16 && D == kD && H % 64 == 0 &&
+         kv.fmt == CSA_FP8_E4M3 && kv.row_bytes == kRow;
+}
+
 hipError_t launch_attn_m32(const AttnCall& c, int nsplit, int split_len, hipStream_t st) {
   if (c.n_entries + c.W + kT > INT32_MAX || c.ckv.cap > INT32_MAX || c.win.cap > INT32_MAX) return hipErrorInvalidValue;
   Args a;
@@ -533,6 +581,7 @@ hipError_t launch_attn_m32(const AttnCall& c, int nsplit, int split_len, hipStre
   a.sink = c.sink; a.tau = c.tau;
   a.out = c.out; a.out_f32 = c.partial; a.lse = c.lse; a.partial = c.partial;
   a.nsplit = nsplit; a.split_len = split_len; a.ws = (float*)c.ws;
+  a.qn = c.qn;
   const dim3 grid((unsigned)((int64_t)c.B * c.Tq), c.H / 64, nsplit);
   hipLaunchKernelGGL(attn_m32_kernel, grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();

@@ -34,6 +34,30 @@ inline StoreW wview(const csa_store& s) {
   return StoreW{(uint8_t*)s.rows, s.scales, s.cap, s.dim, s.rope_dim, s.fmt, s.row_bytes};
 }
 
+// ------------------------------------------------- RMSNorm / partial RoPE
+// Post-processing of stored rows and queries (csa_norm_rope): gain == NULL
+// means no RMSNorm, rope_dims == 0 no rotation.
+struct NormRope {
+  const float* gain;
+  float eps;
+  int rope_dims;
+  const float* theta;
+  int64_t pos0;
+};
+inline NormRope norm_rope_of(const csa_norm_rope* p) {
+  return p ? NormRope{p->norm_gain, p->norm_eps, p->rope_dims, p->rope_theta, p->pos0}
+           : NormRope{nullptr, 0.0f, 0, nullptr, 0};
+}
+
+// Turn the pair (x, y) by the binary32 angle fl32(pos * theta).
+__device__ __forceinline__ void rope_pair(float& x, float& y, float pos, float theta) {
+  float sn, cs;
+  sincosf(__fmul_rn(pos, theta), &sn, &cs);
+  const float nx = x * cs - y * sn, ny = x * sn + y * cs;
+  x = nx;
+  y = ny;
+}
+
 // ------------------------------------------------------------------ BF16
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 

@@ -106,6 +106,50 @@ __device__ __forceinline__ void store_entry(const float (&acc)[VPL], bool active
   }
 }
 
+// RMSNorm and partial RoPE of one row held VPL dims per lane (lane l: dims
+// [l*VPL, l*VPL + VPL); lanes with active == false hold none) at `position`.
+// Called by the whole wavefront (the sum of squares is a wavefront
+// reduction; with one dim per lane a pair's partner is the neighbour lane).
+template <int VPL>
+__device__ __forceinline__ void post_row(float (&acc)[VPL], bool active, int D, const NormRope& nr,
+                                         int64_t position) {
+  const int lane = threadIdx.x % kWave;
+  if (nr.gain) {
+    float ss = 0.0f;
+    if (active) {
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) ss = fmaf(acc[v], acc[v], ss);
+    }
+    ss = wave_sum(ss);
+    const float r = 1.0f / sqrtf(ss / (float)D + nr.eps);
+    if (active) {
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) acc[v] = acc[v] * r * nr.gain[lane * VPL + v];
+    }
+  }
+  if (nr.rope_dims > 0) {
+    const int d0 = D - nr.rope_dims;
+    const float pf = (float)position;
+    if constexpr (VPL >= 2) {
+      if (active) {
+#pragma unroll
+        for (int v = 0; v < VPL; v += 2) {
+          const int d = lane * VPL + v;
+          if (d >= d0) rope_pair(acc[v], acc[v + 1], pf, nr.theta[(d - d0) >> 1]);
+        }
+      }
+    } else {
+      float other = __shfl_xor(acc[0], 1);
+      const int d = lane;
+      if (active && d >= d0) {
+        float x = (d & 1) ? other : acc[0], y = (d & 1) ? acc[0] : other;
+        rope_pair(x, y, pf, nr.theta[(d - d0) >> 1]);
+        acc[0] = (d & 1) ? y : x;
+      }
+    }
+  }
+}
+
 // One output entry per wavefront: the m token rows are row(0) .. row(m-1)
 // (lane l owns dims [l*VPL, l*VPL + VPL)); the entry goes to row `row_out`
 // of `out`.  Called by every wavefront of the workgroup (the block
@@ -114,7 +158,7 @@ __device__ __forceinline__ void store_entry(const float (&acc)[VPL], bool active
 template <typename TIn, int VPL, typename RowFn>
 __device__ __forceinline__ void compress_entry(RowFn row, int m, const float* __restrict__ gate,
                                                const float* __restrict__ bias, StoreW out, int64_t row_out,
-                                               bool valid, float* alpha) {
+                                               bool valid, float* alpha, const NormRope& nr, int64_t position) {
   const int lane = threadIdx.x % kWave;
   const int D = out.dim;
   const bool active = valid && lane * VPL < D;
@@ -185,6 +229,7 @@ __device__ __forceinline__ void compress_entry(RowFn row, int m, const float* __
   }
 
   if (!valid) return;
+  post_row<VPL>(acc, active, D, nr, position);
   store_entry<VPL>(acc, active, out, row_out);
 }
 
@@ -192,7 +237,7 @@ template <typename TIn, int VPL>
 __global__ __launch_bounds__(kWave * kCompressWaves) void compress_kernel(
     const TIn* __restrict__ tok, int B, int64_t T, int64_t bstride, int m,
     const float* __restrict__ gate, const float* __restrict__ bias, StoreW out, int64_t row0,
-    int64_t N) {
+    int64_t N, NormRope nr) {
   __shared__ float s_alpha[kCompressWaves][kMaxM];
   const int wave = threadIdx.x / kWave;
   int64_t e = (int64_t)blockIdx.x * kCompressWaves + wave;
@@ -204,7 +249,7 @@ __global__ __launch_bounds__(kWave * kCompressWaves) void compress_kernel(
   const int D = out.dim;
   const TIn* base = tok + (int64_t)b * bstride + j * m * (int64_t)D;
   compress_entry<TIn, VPL>([&](int i) { return base + (int64_t)i * D; }, m, gate, bias, out,
-                           (int64_t)b * out.cap + row0 + j, valid, s_alpha[wave]);
+                           (int64_t)b * out.cap + row0 + j, valid, s_alpha[wave], nr, nr.pos0 + (j + 1) * m - 1);
 }
 
 // Decode-time cache maintenance, one wavefront per sequence b at position
@@ -218,7 +263,7 @@ __global__ __launch_bounds__(kWave * kCompressWaves) void compress_kernel(
 template <typename TIn, int VPL>
 __global__ __launch_bounds__(kWave * kCompressWaves) void decode_append_kernel(
     const TIn* __restrict__ tok, int B, const int64_t* __restrict__ pos, TIn* tail, int R, int m,
-    const float* __restrict__ gate, const float* __restrict__ bias, StoreW out, StoreW win, int W) {
+    const float* __restrict__ gate, const float* __restrict__ bias, StoreW out, StoreW win, int W, NormRope nr) {
   __shared__ float s_alpha[kCompressWaves][kMaxM];
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   int b = (int)blockIdx.x * kCompressWaves + wave;
@@ -241,6 +286,7 @@ __global__ __launch_bounds__(kWave * kCompressWaves) void decode_append_kernel(
 #pragma unroll
       for (int v = 0; v < VPL; ++v) xv[v] = 0.0f;
     }
+    post_row<VPL>(xv, act, D, nr, p);
     store_entry<VPL>(xv, act, win, (int64_t)b * win.cap + p % W);
   }
   const bool close = live && (p + 1) % m == 0 && (p + 1) / m - 1 < out.cap;
@@ -248,26 +294,26 @@ __global__ __launch_bounds__(kWave * kCompressWaves) void decode_append_kernel(
   const int64_t j = close ? (p + 1) / m - 1 : 0;
   const int64_t r0 = close ? (p + 1 - m) % R : 0;      // first row of the block in the ring
   compress_entry<TIn, VPL>([&](int i) { return (const TIn*)tb + ((r0 + i) % R) * D; }, m, gate, bias, out,
-                           (int64_t)b * out.cap + j, close, s_alpha[wave]);
+                           (int64_t)b * out.cap + j, close, s_alpha[wave], nr, p);
 }
 
 template <typename TIn, int VPL>
 static hipError_t launch_append_t(const void* tok, int B, const int64_t* pos, void* tail, int R, int m,
                                   const float* gate, const float* bias, const csa_store& out, const csa_store& win,
-                                  int W, hipStream_t st) {
+                                  int W, const NormRope& nr, hipStream_t st) {
   if (B == 0) return hipSuccess;
   const StoreW w = win.rows ? wview(win) : StoreW{nullptr, nullptr, 0, out.dim, 0, out.fmt, 0};
   hipLaunchKernelGGL((decode_append_kernel<TIn, VPL>), dim3((unsigned)((B + kCompressWaves - 1) / kCompressWaves)),
                      dim3(kWave * kCompressWaves), 0, st, (const TIn*)tok, B, pos, (TIn*)tail, R, m, gate, bias,
-                     wview(out), w, W);
+                     wview(out), w, W, nr);
   return hipGetLastError();
 }
 
 hipError_t launch_decode_append(const void* tok, int tok_fmt, int B, const int64_t* pos, void* tail, int R, int m,
                                 const float* gate, const float* bias, const csa_store& out, const csa_store& win,
-                                int W, hipStream_t st) {
+                                int W, const NormRope& nr, hipStream_t st) {
   const int vpl = out.dim >= 64 ? out.dim / 64 : 1;
-#define CSA_APP(TT, V) return launch_append_t<TT, V>(tok, B, pos, tail, R, m, gate, bias, out, win, W, st)
+#define CSA_APP(TT, V) return launch_append_t<TT, V>(tok, B, pos, tail, R, m, gate, bias, out, win, W, nr, st)
   if (tok_fmt == CSA_F32) {
     switch (vpl) { case 1: CSA_APP(float, 1); case 2: CSA_APP(float, 2); case 4: CSA_APP(float, 4); default: CSA_APP(float, 8); }
   } else {
@@ -291,7 +337,7 @@ __device__ __forceinline__ void load8<float>(const float* p, float (&v)[8]) { lo
 
 template <typename TIn, int LPR>
 __global__ __launch_bounds__(kWave * kCompressWaves) void quant_rows_kernel(
-    const TIn* __restrict__ tok, int B, int64_t bstride, StoreW out, int64_t row0, int64_t N) {
+    const TIn* __restrict__ tok, int B, int64_t bstride, StoreW out, int64_t row0, int64_t N, NormRope nr) {
   constexpr int RPW = kWave / LPR;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int li = lane % LPR;
@@ -306,6 +352,22 @@ __global__ __launch_bounds__(kWave * kCompressWaves) void quant_rows_kernel(
   const int d0 = li * 8;
   float x[8];
   load8<TIn>(tok + (int64_t)b * bstride + j * D + d0, x);
+  if (nr.gain) {                                // RMSNorm over the row's lane group
+    float ss = 0.0f;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) ss = fmaf(x[v], x[v], ss);
+    ss = wave_sum<LPR>(ss);
+    const float r = 1.0f / sqrtf(ss / (float)D + nr.eps);
+#pragma unroll
+    for (int v = 0; v < 8; ++v) x[v] = x[v] * r * nr.gain[d0 + v];
+  }
+  if (nr.rope_dims > 0) {                       // pairs start at even dims: within the lane
+    const int dr = D - nr.rope_dims;
+    const float pf = (float)(nr.pos0 + j);
+#pragma unroll
+    for (int v = 0; v < 8; v += 2)
+      if (d0 + v >= dr) rope_pair(x[v], x[v + 1], pf, nr.theta[(d0 + v - dr) >> 1]);
+  }
   const int64_t row = (int64_t)b * out.cap + row0 + j;
   uint8_t* dst = out.rows + row * out.row_bytes;
   if (out.fmt == CSA_F32) {
@@ -365,25 +427,25 @@ __global__ __launch_bounds__(kWave * kCompressWaves) void quant_rows_kernel(
 
 template <typename TIn, int LPR>
 static hipError_t launch_quant_t(const void* tok, int B, int64_t T, int64_t bstride, const csa_store& out,
-                                 int64_t row0, hipStream_t st) {
+                                 int64_t row0, const NormRope& nr, hipStream_t st) {
   const int64_t items = (int64_t)B * T;
   if (items == 0) return hipSuccess;
   constexpr int rows_per_block = kCompressWaves * (kWave / LPR);
   const int64_t blocks = (items + rows_per_block - 1) / rows_per_block;
   hipLaunchKernelGGL((quant_rows_kernel<TIn, LPR>), dim3((unsigned)blocks), dim3(kWave * kCompressWaves), 0, st,
-                     (const TIn*)tok, B, bstride, wview(out), row0, T);
+                     (const TIn*)tok, B, bstride, wview(out), row0, T, nr);
   return hipGetLastError();
 }
 
 template <typename TIn>
 static hipError_t launch_quant(const void* tok, int B, int64_t T, int64_t bstride, const csa_store& out,
-                               int64_t row0, hipStream_t st) {
+                               int64_t row0, const NormRope& nr, hipStream_t st) {
   switch (out.dim / 8) {
-    case 4: return launch_quant_t<TIn, 4>(tok, B, T, bstride, out, row0, st);
-    case 8: return launch_quant_t<TIn, 8>(tok, B, T, bstride, out, row0, st);
-    case 16: return launch_quant_t<TIn, 16>(tok, B, T, bstride, out, row0, st);
-    case 32: return launch_quant_t<TIn, 32>(tok, B, T, bstride, out, row0, st);
-    default: return launch_quant_t<TIn, 64>(tok, B, T, bstride, out, row0, st);
+    case 4: return launch_quant_t<TIn, 4>(tok, B, T, bstride, out, row0, nr, st);
+    case 8: return launch_quant_t<TIn, 8>(tok, B, T, bstride, out, row0, nr, st);
+    case 16: return launch_quant_t<TIn, 16>(tok, B, T, bstride, out, row0, nr, st);
+    case 32: return launch_quant_t<TIn, 32>(tok, B, T, bstride, out, row0, nr, st);
+    default: return launch_quant_t<TIn, 64>(tok, B, T, bstride, out, row0, nr, st);
   }
 }
 
@@ -407,24 +469,24 @@ static bool quant_rows_ok(const void* tok, int tok_fmt, int64_t bstride, const c
 template <typename TIn, int VPL>
 static hipError_t launch_compress_t(const void* tok, int B, int64_t T, int64_t bstride, int m,
                                     const float* gate, const float* bias, const csa_store& out,
-                                    int64_t row0, hipStream_t st) {
+                                    int64_t row0, const NormRope& nr, hipStream_t st) {
   const int64_t N = T / m;
   const int64_t items = (int64_t)B * N;
   if (items == 0) return hipSuccess;
   const int64_t blocks = (items + kCompressWaves - 1) / kCompressWaves;
   hipLaunchKernelGGL((compress_kernel<TIn, VPL>), dim3((unsigned)blocks), dim3(kWave * kCompressWaves),
-                     0, st, (const TIn*)tok, B, T, bstride, m, gate, bias, wview(out), row0, N);
+                     0, st, (const TIn*)tok, B, T, bstride, m, gate, bias, wview(out), row0, N, nr);
   return hipGetLastError();
 }
 
 hipError_t launch_compress(const void* tok, int tok_fmt, int B, int64_t T, int64_t bstride, int m,
                            const float* gate, const float* bias, const csa_store& out, int64_t row0,
-                           hipStream_t st) {
+                           const NormRope& nr, hipStream_t st) {
   if (m == 1 && quant_rows_ok(tok, tok_fmt, bstride, out))
-    return tok_fmt == CSA_F32 ? launch_quant<float>(tok, B, T, bstride, out, row0, st)
-                              : launch_quant<uint16_t>(tok, B, T, bstride, out, row0, st);
+    return tok_fmt == CSA_F32 ? launch_quant<float>(tok, B, T, bstride, out, row0, nr, st)
+                              : launch_quant<uint16_t>(tok, B, T, bstride, out, row0, nr, st);
   const int vpl = out.dim >= 64 ? out.dim / 64 : 1;
-#define CSA_CMP(TT, V) return launch_compress_t<TT, V>(tok, B, T, bstride, m, gate, bias, out, row0, st)
+#define CSA_CMP(TT, V) return launch_compress_t<TT, V>(tok, B, T, bstride, m, gate, bias, out, row0, nr, st)
   if (tok_fmt == CSA_F32) {
     switch (vpl) { case 1: CSA_CMP(float, 1); case 2: CSA_CMP(float, 2); case 4: CSA_CMP(float, 4); default: CSA_CMP(float, 8); }
   } else {

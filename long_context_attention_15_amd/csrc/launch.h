@@ -6,16 +6,17 @@
 #include <stdint.h>
 
 #include "../../include/csa.h"
+#include "common.h"
 
 namespace csa {
 
 hipError_t launch_compress(const void* tok, int tok_fmt, int B, int64_t T, int64_t bstride, int m,
                            const float* gate, const float* bias, const csa_store& out, int64_t row0,
-                           hipStream_t st);
+                           const NormRope& nr, hipStream_t st);
 int compress_max_m();
 hipError_t launch_decode_append(const void* tok, int tok_fmt, int B, const int64_t* pos, void* tail, int R, int m,
                                 const float* gate, const float* bias, const csa_store& out, const csa_store& win,
-                                int W, hipStream_t st);
+                                int W, const NormRope& nr, hipStream_t st);
 
 // Indexer: chunk size and chunk count chosen for a call; workspace bytes.
 struct IdxPlan {
@@ -51,13 +52,13 @@ struct AttnCall {
   void* out; float* lse; int partial;
   void* ws; size_t ws_bytes;
   int allow_split;                                 // split long lists over workgroups (needs ws)
+  NormRope qn;                                     // RMSNorm / partial RoPE of the queries
 };
 enum { kModeNone = 0, kModeSel = 1, kModeRange = 2 };
 size_t attn_workspace(int B, int Tq, int H, int D, int64_t max_list);
 bool attn_supported(int H, int D);
 hipError_t launch_attn(const AttnCall& c, hipStream_t st);
 bool attn_mfma_eligible(int q_fmt, int H, int D, const csa_store& kv, bool has_prior, float tau);
-hipError_t launch_attn_mfma(const AttnCall& c, int nsplit, int split_len, hipStream_t st);
 hipError_t launch_attn_m32(const AttnCall& c, int nsplit, int split_len, hipStream_t st);
 
 }  // namespace csa

@@ -93,7 +93,7 @@ def rms_normalize(x: np.ndarray, eps: float = 1e-6) -> np.ndarray:
 # LAYER_STRIDE to each.
 STREAMS = {
     "q": 1, "kv": 2, "idx_k": 3, "idx_q": 4, "head_w": 5,
-    "gate": 6, "bias": 7, "idx_gate": 8, "idx_bias": 9, "sink": 10,
+    "gate": 6, "bias": 7, "idx_gate": 8, "idx_bias": 9, "sink": 10, "norm_gain": 11,
 }
 LAYER_STRIDE = 100
 

@@ -199,3 +199,49 @@ def random_selection(T, m, N, k, seed):
         pick = np.sort(rng.permutation(nt)[:k])
         sel[t, : len(pick)] = pick
     return sel
+
+
+# ------------------------------------------------- RMSNorm / RoPE rule
+def rope_theta(R, base=10000.0):
+    """Standard rotary frequencies base^(-2i/R), i < R/2, as float32."""
+    return (base ** (-2.0 * np.arange(R // 2) / R)).astype(np.float32)
+
+
+def post_error_bound(c, e, gain, eps, theta, rope_dims):
+    """Bound on |post_gpu(c') - post(c)| per element when the kernel's input
+    row c' lies within e of c (c [n, D] float64, e like c or None) and the
+    kernel works in float32: first-order propagation through RMSNorm,
+    y = c / r * g with r = sqrt(mean(c^2) + eps), so
+    |dy_d| <= |g_d| (e_d / r + |c_d| |dr| / r^2), |dr| <= sum|c_i| e_i / (D r),
+    plus the float32 rounding of the norm ((D + 8) u relative); then each
+    rotated pair, whose outputs move by at most ea + eb (|cos|, |sin| <= 1)
+    plus (|a| + |b|) 16 u for sincosf of the binary32 angle and the products."""
+    c = np.asarray(c, np.float64)
+    n, D = c.shape
+    ey = np.zeros_like(c) if e is None else np.broadcast_to(np.asarray(e, np.float64), c.shape).copy()
+    y = c
+    if gain is not None:
+        g = np.abs(np.asarray(gain, np.float64))
+        r = np.sqrt(np.mean(c * c, axis=1, keepdims=True) + eps)
+        y = O.rms_norm(c, np.asarray(gain, np.float64), eps)
+        dr = (np.abs(c) * ey).sum(axis=1, keepdims=True) / (D * r)
+        ey = 1.01 * g * (ey / r + np.abs(c) * dr / r ** 2) + (D + 8) * U * np.abs(y)
+    if theta is not None and rope_dims:
+        d0 = D - rope_dims
+        mag = np.abs(y[:, d0::2]) + np.abs(y[:, d0 + 1::2])
+        et = ey[:, d0::2] + ey[:, d0 + 1::2] + 16 * U * mag
+        ey = ey.copy()
+        ey[:, d0::2] = et
+        ey[:, d0 + 1::2] = et
+    return ey + 1e-30
+
+
+def post_queries(qv, positions, gain, eps, theta, rope_dims, bf16):
+    """Oracle view of queries after RMSNorm / partial RoPE: qv [n, H, D] at
+    positions [n] (every head of a row shares its position), rounded back to
+    BF16 for BF16 queries."""
+    n, H, D = qv.shape
+    pos = np.repeat(np.asarray(positions, np.int64), H)
+    y = O.post_rows(qv.reshape(n * H, D), pos, None if gain is None else np.asarray(gain, np.float64), eps,
+                    theta, rope_dims).reshape(n, H, D)
+    return bf16_vals(y) if bf16 else y

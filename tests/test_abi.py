@@ -45,7 +45,7 @@ def test_noalloc_decode_rejects_sizes_beyond_its_scratch(lib):
     kv = _store(P, 100, 512, 64, csa.FP8_E4M3, P)
     ring = _store(P, 128, 512, 64, csa.FP8_E4M3, P)
     assert lib.csa_attn_workspace(73, 1, 224, 512, 1024 + 128) > 48 << 20
-    st = lib.csa_sparse_attn_decode_noalloc(P, csa.BF16, 73, 224, kv, 100, P, 1024, ring, P, 128, 0, 0.04, P, 0, 0,
+    st = lib.csa_sparse_attn_decode_noalloc(P, csa.BF16, 73, 224, kv, 100, P, 1024, ring, P, 128, 0, 0.04, P, 0, 0, None,
                                             None)
     assert st == 1 and "scratch" in lib.csa_last_error().decode()
 
@@ -73,40 +73,40 @@ def test_decode_append_rejects_bad_arguments(lib):
     out = _store(P, 8, 64)
     nowin = csa._CStore(None, None, 0, 0, 0, 0, 0)
     # null pos, tail rows not a multiple of m, m out of range, unaligned tail
-    assert lib.csa_decode_append(P, csa.F32, 2, 0, P, 8, 4, P, P, out, nowin, 0, None) == 1
-    assert lib.csa_decode_append(P, csa.F32, 2, P, P, 6, 4, P, P, out, nowin, 0, None) == 1
+    assert lib.csa_decode_append(P, csa.F32, 2, 0, P, 8, 4, P, P, out, nowin, 0, None, None) == 1
+    assert lib.csa_decode_append(P, csa.F32, 2, P, P, 6, 4, P, P, out, nowin, 0, None, None) == 1
     assert "multiple of m" in lib.csa_last_error().decode()
-    assert lib.csa_decode_append(P, csa.F32, 2, P, P, 8, 0, P, P, out, nowin, 0, None) == 1
-    assert lib.csa_decode_append(P, csa.F32, 2, P, P + 4, 8, 4, P, P, out, nowin, 0, None) == 1
+    assert lib.csa_decode_append(P, csa.F32, 2, P, P, 8, 0, P, P, out, nowin, 0, None, None) == 1
+    assert lib.csa_decode_append(P, csa.F32, 2, P, P + 4, 8, 4, P, P, out, nowin, 0, None, None) == 1
     # unsupported token format, window of another dim, W beyond the window store
-    assert lib.csa_decode_append(P, csa.MXFP4, 2, P, P, 8, 4, P, P, out, nowin, 0, None) == 2
-    assert lib.csa_decode_append(P, csa.F32, 2, P, P, 8, 4, P, P, out, _store(P, 8, 128), 4, None) == 1
-    assert lib.csa_decode_append(P, csa.F32, 2, P, P, 8, 4, P, P, out, _store(P, 8, 64), 9, None) == 1
+    assert lib.csa_decode_append(P, csa.MXFP4, 2, P, P, 8, 4, P, P, out, nowin, 0, None, None) == 2
+    assert lib.csa_decode_append(P, csa.F32, 2, P, P, 8, 4, P, P, out, _store(P, 8, 128), 4, None, None) == 1
+    assert lib.csa_decode_append(P, csa.F32, 2, P, P, 8, 4, P, P, out, _store(P, 8, 64), 9, None, None) == 1
     assert "W = 9" in lib.csa_last_error().decode()
 
 
 def test_compress_rejects_bad_arguments(lib):
     out = _store(P, 8, 64)
     # m out of range
-    assert lib.csa_compress_kv(P, csa.F32, 1, 32, 32 * 64, 0, P, P, out, 0, None) == 1
-    assert lib.csa_compress_kv(P, csa.F32, 1, 32, 32 * 64, 4096, P, P, out, 0, None) == 1
+    assert lib.csa_compress_kv(P, csa.F32, 1, 32, 32 * 64, 0, P, P, out, 0, None, None) == 1
+    assert lib.csa_compress_kv(P, csa.F32, 1, 32, 32 * 64, 4096, P, P, out, 0, None, None) == 1
     assert "m = 4096" in lib.csa_last_error().decode()
     # null gate, unaligned token pointer, unsupported token format
-    assert lib.csa_compress_kv(P, csa.F32, 1, 32, 32 * 64, 4, 0, P, out, 0, None) == 1
-    assert lib.csa_compress_kv(P + 4, csa.F32, 1, 32, 32 * 64, 4, P, P, out, 0, None) == 1
-    assert lib.csa_compress_kv(P, csa.FP8_E4M3, 1, 32, 32 * 64, 4, P, P, out, 0, None) == 2
+    assert lib.csa_compress_kv(P, csa.F32, 1, 32, 32 * 64, 4, 0, P, out, 0, None, None) == 1
+    assert lib.csa_compress_kv(P + 4, csa.F32, 1, 32, 32 * 64, 4, P, P, out, 0, None, None) == 1
+    assert lib.csa_compress_kv(P, csa.FP8_E4M3, 1, 32, 32 * 64, 4, P, P, out, 0, None, None) == 2
     # output rows beyond the store
-    assert lib.csa_compress_kv(P, csa.F32, 1, 64, 64 * 64, 4, P, P, out, 0, None) == 1
+    assert lib.csa_compress_kv(P, csa.F32, 1, 64, 64 * 64, 4, P, P, out, 0, None, None) == 1
     # bad store: wrong row_bytes, unsupported dim, FP8 without scales
     bad = _store(P, 8, 64)
     bad.row_bytes = 100
-    assert lib.csa_compress_kv(P, csa.F32, 1, 32, 32 * 64, 4, P, P, bad, 0, None) == 1
-    assert lib.csa_compress_kv(P, csa.F32, 1, 32, 32 * 48, 4, P, P, _store(P, 8, 48), 0, None) == 2
-    assert lib.csa_compress_kv(P, csa.F32, 1, 32, 32 * 64, 4, P, P, _store(P, 8, 64, 16, csa.FP8_E4M3), 0,
+    assert lib.csa_compress_kv(P, csa.F32, 1, 32, 32 * 64, 4, P, P, bad, 0, None, None) == 1
+    assert lib.csa_compress_kv(P, csa.F32, 1, 32, 32 * 48, 4, P, P, _store(P, 8, 48), 0, None, None) == 2
+    assert lib.csa_compress_kv(P, csa.F32, 1, 32, 32 * 64, 4, P, P, _store(P, 8, 64, 16, csa.FP8_E4M3), 0, None,
                                None) == 1
     # MXFP4 output of 512 dims
     mx = _store(P, 8, 512, 0, csa.MXFP4, P)
-    assert lib.csa_compress_kv(P, csa.F32, 1, 32, 32 * 512, 4, P, P, mx, 0, None) == 2
+    assert lib.csa_compress_kv(P, csa.F32, 1, 32, 32 * 512, 4, P, P, mx, 0, None, None) == 2
 
 
 def test_indexer_rejects_bad_arguments(lib):
@@ -136,7 +136,7 @@ def test_attention_rejects_bad_arguments(lib):
     f32win = _store(P, 300, 512, 0, csa.F32)
     pre = lambda **kw: lib.csa_sparse_attn_prefill(
         kw.get("q", P), kw.get("qf", csa.BF16), 1, kw.get("T", 256), kw.get("H", 64), kv, kw.get("n", 100),
-        kw.get("sel", P), kw.get("k", 64), kw.get("win", win), 128, 0, 0.04, P, 0, kw.get("flags", 0), None)
+        kw.get("sel", P), kw.get("k", 64), kw.get("win", win), 128, 0, 0.04, P, 0, kw.get("flags", 0), None, None)
     assert pre(q=0) == 1
     assert pre(sel=0) == 1
     assert pre(qf=csa.FP8_E4M3) == 2
@@ -149,18 +149,49 @@ def test_attention_rejects_bad_arguments(lib):
     # q and out move in 16-byte pieces: a bf16 view offset by 2 or 4 elements is rejected
     assert pre(q=P + 4) == 1 and "16-byte" in lib.csa_last_error().decode()
     assert pre(q=P + 8) == 1
-    assert lib.csa_sparse_attn_prefill(P, csa.BF16, 1, 256, 64, kv, 100, P, 64, win, 128, 0, 0.04, P + 4, 0, 0,
+    assert lib.csa_sparse_attn_prefill(P, csa.BF16, 1, 256, 64, kv, 100, P, 64, win, 128, 0, 0.04, P + 4, 0, 0, None,
                                        None) == 1
-    assert lib.swa_merge(P, csa.BF16, 1, 8, 64, win, 0, 128, 0, P + 8, P, 0, 0.04, P, None) == 1
+    assert lib.swa_merge(P, csa.BF16, 1, 8, 64, win, 0, 128, 0, P + 8, P, 0, 0.04, P, None, None) == 1
     # decode: workspace required for few queries
     ring = _store(P, 128, 512, 64, csa.FP8_E4M3, P)
-    st = lib.csa_sparse_attn_decode(P, csa.BF16, 4, 128, kv, 100, P, 64, ring, P, 128, 0, 0.04, P, 0, 0, P, 16,
+    st = lib.csa_sparse_attn_decode(P, csa.BF16, 4, 128, kv, 100, P, 64, ring, P, 128, 0, 0.04, P, 0, 0, P, 16, None,
                                     None)
     assert st == 3                                    # a workspace was given but is too small
     assert lib.csa_attn_workspace(4, 1, 128, 512, 64 + 128) > 0
     # hca: ring without positions
-    assert lib.hca_attn(P, csa.BF16, 1, 8, 64, kv, 128, 100, 0, ring, 128, 0, 0.04, P, 0, csa.WIN_RING, 0, 0,
+    assert lib.hca_attn(P, csa.BF16, 1, 8, 64, kv, 128, 100, 0, ring, 128, 0, 0.04, P, 0, csa.WIN_RING, 0, 0, None,
                         None) == 1
     # swa_merge: partial flag is not allowed, null partials rejected
-    assert lib.swa_merge(P, csa.BF16, 1, 8, 64, win, 0, 128, csa.ATTN_PARTIAL, P, P, 0, 0.04, P, None) == 1
-    assert lib.swa_merge(P, csa.BF16, 1, 8, 64, win, 0, 128, 0, 0, P, 0, 0.04, P, None) == 1
+    assert lib.swa_merge(P, csa.BF16, 1, 8, 64, win, 0, 128, csa.ATTN_PARTIAL, P, P, 0, 0.04, P, None, None) == 1
+    assert lib.swa_merge(P, csa.BF16, 1, 8, 64, win, 0, 128, 0, 0, P, 0, 0.04, P, None, None) == 1
+
+
+def test_norm_rope_blocks_are_validated(lib):
+    """RMSNorm / RoPE blocks: gain 16-byte aligned, eps finite and >= 0,
+    rope_dims even and within the row, theta given when rotating; checked on
+    every entry point that takes one, before any GPU work."""
+    out = _store(P, 8, 64)
+    nowin = csa._CStore(None, None, 0, 0, 0, 0, 0)
+    bad = [csa._CNormRope(P + 4, 1e-6, 0, None, 0),           # unaligned gain
+           csa._CNormRope(P, float("nan"), 0, None, 0),        # eps not finite
+           csa._CNormRope(P, -1.0, 0, None, 0),                # negative eps
+           csa._CNormRope(None, 0.0, 3, P, 0),                 # odd rope_dims
+           csa._CNormRope(None, 0.0, 66, P, 0),                # beyond the row
+           csa._CNormRope(None, 0.0, 16, None, 0)]             # no theta
+    for nr in bad:
+        r = ctypes.byref(nr)
+        assert lib.csa_compress_kv(P, csa.F32, 1, 32, 32 * 64, 4, P, P, out, 0, r, None) == 1
+        assert "post" in lib.csa_last_error().decode()
+        assert lib.csa_decode_append(P, csa.F32, 2, P, P, 8, 4, P, P, out, nowin, 0, r, None) == 1
+    kv = _store(P, 100, 64, 16, csa.FP8_E4M3, P)
+    win = _store(P, 300, 64, 16, csa.FP8_E4M3, P)
+    for nr in bad:
+        r = ctypes.byref(nr)
+        assert lib.csa_sparse_attn_prefill(P, csa.BF16, 1, 256, 4, kv, 100, P, 64, win, 128, 0, 0.04, P, 0, 0, r,
+                                           None) == 1
+        assert "q_post" in lib.csa_last_error().decode()
+        assert lib.hca_attn(P, csa.BF16, 1, 256, 4, kv, 128, 2, 0, win, 128, 0, 0.04, P, 0, 0, 0, 0, r, None) == 1
+        assert lib.swa_merge(P, csa.BF16, 1, 8, 4, win, 0, 128, 0, P, P, 0, 0.04, P, r, None) == 1
+    ok = csa._CNormRope(P, 1e-6, 16, P, 0)
+    assert lib.csa_compress_kv(P, csa.F32, 1, 32, 32 * 64, 0, P, P, out, 0, ctypes.byref(ok), None) == 1
+    assert "m = 0" in lib.csa_last_error().decode()      # a valid block passes on to the other checks
