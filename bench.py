@@ -385,9 +385,18 @@ def cpu_baseline(T=131072, n_sample=512, budget_s=15.0):
     from oracle import csa as O
     try:
         from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        pool = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:
-        cores = os.cpu_count() or 1
+        pool = os.cpu_count() or 1
+    allowed = len(os.sched_getaffinity(0))
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     H, D, R, W, k, HI, dI, m, mh = 64, 512, 64, 128, 512, 8, 64, 4, 128
     N, Nh = T // m, T // mh
     tau = 1.0 / math.sqrt(D)
@@ -396,6 +405,7 @@ def cpu_baseline(T=131072, n_sample=512, budget_s=15.0):
     kvh = synth.tensor(0, "kv", (T, D), rmsnorm=True, layer=1)
     xi = synth.tensor(0, "idx_k", (T, dI), rmsnorm=True)
     t_gen = time.perf_counter() - t0
+    cpu0, wall0 = time.process_time(), time.perf_counter()
     t0 = time.perf_counter()
     ckv = O.quantize(O.compress(kv, synth.tensor(0, "gate", (D,), std=0.02),
                                 synth.tensor(0, "bias", (m,), std=0.02), m), "fp8", R)
@@ -427,8 +437,11 @@ def cpu_baseline(T=131072, n_sample=512, budget_s=15.0):
         if time.perf_counter() - t0 > budget_s:
             break
     t_rows = time.perf_counter() - t0
+    busy = (time.process_time() - cpu0) / (time.perf_counter() - wall0)   # threads kept busy on average
     total = t_compress + t_rows * T / done
-    return {"value": T / total, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+    return {"value": T / total, "unit": "tokens/s", "cores": int(min(pool, allowed)), "kind": "oracle",
+            "cpu_model": model, "threads_busy_avg": round(busy, 2), "blas_threads": int(pool),
+            "cpus_allowed": allowed,
             "sample": f"{done} of {T} query rows (stride sample) of the 128K CSA+HCA prefill, all tokens "
                       f"compressed; per-row time extrapolated to {T} rows (compress {t_compress:.1f} s, "
                       f"rows {t_rows:.1f} s, input generation {t_gen:.1f} s excluded)"}

@@ -125,18 +125,28 @@ __global__ __launch_bounds__(kAttnThreads) void attn_valu_kernel(AttnArgs a) {
       for (int r = 0; r < DPT; ++r) qv[r] = qv[r] * rr * a.qn.gain[p + TPH * r];
     }
     if (a.qn.rope_dims > 0) {                     // the pair partner of dim d is dim d ^ 1, in thread p ^ 1
-      const int d0 = D - a.qn.rope_dims;
-      const float pf = (float)t;
+      // The workgroup's rows share one position: cos / sin of each pair are
+      // formed once, by a rolled loop, into the entry buffer (free until the
+      // first tile), rather than by a sincos per dim in the unrolled loop.
+      const int d0 = D - a.qn.rope_dims, npair = a.qn.rope_dims >> 1;
+      float* const tab = &s_e[0][0];              // cos of pair i at [i], sin at [D / 2 + i]
+      for (int i = tid; i < npair; i += blockDim.x) {
+        float sn, cs;
+        sincos_angle(__fmul_rn((float)t, a.qn.theta[i]), &sn, &cs);
+        tab[i] = cs;
+        tab[D / 2 + i] = sn;
+      }
+      __syncthreads();
 #pragma unroll
       for (int r = 0; r < DPT; ++r) {
         const int d = p + TPH * r;
         const float other = __shfl_xor(qv[r], 1, TPH);
         if (d >= d0) {
-          float x = (d & 1) ? other : qv[r], y = (d & 1) ? qv[r] : other;
-          rope_pair(x, y, pf, a.qn.theta[(d - d0) >> 1]);
-          qv[r] = (d & 1) ? y : x;
+          const float cs = tab[(d - d0) >> 1], sn = tab[D / 2 + ((d - d0) >> 1)];
+          qv[r] = (d & 1) ? other * sn + qv[r] * cs : qv[r] * cs - other * sn;
         }
       }
+      __syncthreads();                            // the buffer holds entries next
     }
     if (!a.q_f32) {                               // BF16 queries stay BF16
 #pragma unroll

@@ -117,6 +117,7 @@ __device__ __forceinline__ float swap32_sum(float x) {
   return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
+template <bool kQPost>
 __global__ __launch_bounds__(kThreads, 1) void attn_m32_kernel(Args a) {
   __shared__ __attribute__((aligned(16))) uint8_t Raw[kStages][kTileBytes];
   __shared__ const uint8_t* Tptr[kSlots][kT];                     // row address (zero row if empty)
@@ -193,51 +194,106 @@ __global__ __launch_bounds__(kThreads, 1) void attn_m32_kernel(Args a) {
   // wave, K-step ks = dims 32 ks .. +32; lane l holds head 16 hq + l % 16,
   // dims 32 ks + 8 (l / 16) .. +8.)
   const int g = lane >> 4, i16 = lane & 15;
+  // Lane (g, i16) holds head 16 hq + i16, dims 32 ks + 8 g .. +8: 16 bytes at
+  // q_src + hq * 16 kD + 32 ks.
+  const uint16_t* const q_src = a.q + (bq * a.H + blockIdx.y * 64 + wave * 32 + i16) * (int64_t)kD + 8 * g;
+  // RMSNorm / partial RoPE of the query rows (kQPost).  The rows are loaded
+  // as in the plain path and processed in registers; the cos / sin of rotation
+  // pair p come from a per-wavefront table (lane l forms pairs l, l + 64, ...),
+  // so no sincos is replicated in the unrolled code.  The processed BF16
+  // operands go through the wavefront's half of the raw tile buffers (free
+  // until the first row DMA below), chunk (ks, hq) of lane l at byte
+  // 16 (64 (2 ks + hq) + l), and are read back from there: the operand
+  // registers have a single source, and the processing temporaries are dead
+  // before they are loaded, so the tile loop keeps the plain path's register
+  // allocation (operands merged from two sources, a replicated sincos, or
+  // processing in place inside the prologue push some of them to scratch
+  // inside the loop).
   bf16x8 qf[16][2];
-  {
+  if constexpr (kQPost) {
+    uint8_t* const q_stage = &Raw[0][0] + wave * (32 * kD * 2);
+    // after the staging (64 KiB): per wavefront, 2 KiB of cos / sin, then 2 KiB of gain
+    float2* const rot_tab = (float2*)(&Raw[0][0] + 2 * (32 * kD * 2)) + wave * 256;
+    float* const gain_tab = (float*)(&Raw[0][0] + 2 * (32 * kD * 2) + 4096) + wave * kD;
+    for (int pp = lane; pp < (a.qn.rope_dims >> 1); pp += 64) {   // before the rows: few values live
+      float sn, cs;
+      sincos_angle(__fmul_rn((float)t, a.qn.theta[pp]), &sn, &cs);
+      rot_tab[pp] = make_float2(cs, sn);
+    }
+    bf16x8 qx[16][2];
+#pragma unroll
+    for (int hq = 0; hq < 2; ++hq)
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks)
+        qx[ks][hq] = __builtin_bit_cast(bf16x8, *(const u32x4*)(q_src + hq * 16 * kD + 32 * ks));
+    float4 gl0 = make_float4(1.0f, 1.0f, 1.0f, 1.0f), gl1 = gl0;
+    if (a.qn.gain) {
+      gl0 = *(const float4*)(a.qn.gain + 8 * lane);
+      gl1 = *(const float4*)(a.qn.gain + 8 * lane + 4);
+    }
+    const int d0 = kD - a.qn.rope_dims, npair = a.qn.rope_dims >> 1;
+    *(float4*)(gain_tab + 8 * lane) = gl0;
+    *(float4*)(gain_tab + 8 * lane + 4) = gl1;
+    float rr[2] = {1.0f, 1.0f};
+    if (a.qn.gain) {                              // a head's 512 dims: 4 lanes (i16 + 16 g) x 128
+#pragma unroll
+      for (int hq = 0; hq < 2; ++hq) {
+        float ss = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < 16; ++ks)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ss = fmaf((float)qx[ks][hq][e], (float)qx[ks][hq][e], ss);
+        ss += __shfl_xor(ss, 16);
+        ss += __shfl_xor(ss, 32);
+        rr[hq] = 1.0f / sqrtf(ss / (float)kD + a.qn.eps);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));    // lgkmcnt(0): the tables are written
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int ks = 0; ks < 16; ++ks) {
+      const int dd = 32 * ks + 8 * g;             // this lane's 8 dims of K-step ks
+      const float4 g0 = *(const float4*)(gain_tab + dd), g1 = *(const float4*)(gain_tab + dd + 4);
+      const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+      float2 cs[4];                               // pair (dd + 2 e2, dd + 2 e2 + 1), both head halves
+      bool on[4];
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        on[e2] = npair > 0 && dd + 2 * e2 >= d0;
+        cs[e2] = make_float2(1.0f, 0.0f);
+        if (npair > 0 && 32 * ks + 32 > d0) {     // uniform: K-step ks holds rotated dims
+          const float2 tv = rot_tab[on[e2] ? (dd + 2 * e2 - d0) >> 1 : 0];
+          if (on[e2]) cs[e2] = tv;
+        }
+      }
+#pragma unroll
+      for (int hq = 0; hq < 2; ++hq) {
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (float)qx[ks][hq][e] * rr[hq] * gv[e];
+        bf16x8 y;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const float c = cs[e2].x, sv = cs[e2].y, x0 = v[2 * e2], x1 = v[2 * e2 + 1];
+          y[2 * e2] = (__bf16)(on[e2] ? x0 * c - x1 * sv : x0);   // BF16 queries stay BF16
+          y[2 * e2 + 1] = (__bf16)(on[e2] ? x0 * sv + x1 * c : x1);
+        }
+        *(u32x4*)(q_stage + 16 * (64 * (2 * ks + hq) + lane)) = __builtin_bit_cast(u32x4, y);
+      }
+    }
+#pragma unroll
+    for (int hq = 0; hq < 2; ++hq)
+#pragma unroll
+      for (int ks = 0; ks < 16; ++ks)
+        qf[ks][hq] = __builtin_bit_cast(bf16x8, *(const u32x4*)(q_stage + 16 * (64 * (2 * ks + hq) + lane)));
+    // operands in registers before any row DMA may overwrite the staging
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));    // lgkmcnt(0)
+  } else {
 #pragma unroll
     for (int hq = 0; hq < 2; ++hq) {
       const uint16_t* qp = a.q + (bq * a.H + blockIdx.y * 64 + wave * 32 + 16 * hq + i16) * (int64_t)kD + 8 * g;
 #pragma unroll
       for (int ks = 0; ks < 16; ++ks) qf[ks][hq] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qp + 32 * ks));
-    }
-  }
-  if (a.qn.gain || a.qn.rope_dims > 0) {          // uniform: RMSNorm / partial RoPE of the query rows
-    const float pf = (float)t;
-    const int d0 = kD - a.qn.rope_dims;
-#pragma unroll
-    for (int hq = 0; hq < 2; ++hq) {
-      float rr = 1.0f;
-      if (a.qn.gain) {                            // a head's 512 dims: 4 lanes (i16 + 16 g) x 128
-        float ss = 0.0f;
-#pragma unroll
-        for (int ks = 0; ks < 16; ++ks)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) ss = fmaf((float)qf[ks][hq][e], (float)qf[ks][hq][e], ss);
-        ss += __shfl_xor(ss, 16);
-        ss += __shfl_xor(ss, 32);
-        rr = 1.0f / sqrtf(ss / (float)kD + a.qn.eps);
-      }
-#pragma unroll
-      for (int ks = 0; ks < 16; ++ks) {
-        const int dd = 32 * ks + 8 * g;           // this lane's 8 dims of K-step ks
-        float v[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = (float)qf[ks][hq][e];
-        if (a.qn.gain) {
-          const float4 g0 = *(const float4*)(a.qn.gain + dd), g1 = *(const float4*)(a.qn.gain + dd + 4);
-          const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = v[e] * rr * gv[e];
-        }
-        if (a.qn.rope_dims > 0) {
-#pragma unroll
-          for (int e = 0; e < 8; e += 2)
-            if (dd + e >= d0) rope_pair(v[e], v[e + 1], pf, a.qn.theta[(dd + e - d0) >> 1]);
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qf[ks][hq][e] = (__bf16)v[e];   // BF16 queries stay BF16
-      }
     }
   }
   // LDS byte offsets of this lane's reads within a raw tile.
@@ -583,7 +639,10 @@ hipError_t launch_attn_m32(const AttnCall& c, int nsplit, int split_len, hipStre
   a.nsplit = nsplit; a.split_len = split_len; a.ws = (float*)c.ws;
   a.qn = c.qn;
   const dim3 grid((unsigned)((int64_t)c.B * c.Tq), c.H / 64, nsplit);
-  hipLaunchKernelGGL(attn_m32_kernel, grid, dim3(kThreads), 0, st, a);
+  if (c.qn.gain || c.qn.rope_dims > 0)
+    hipLaunchKernelGGL(attn_m32_kernel<true>, grid, dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(attn_m32_kernel<false>, grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

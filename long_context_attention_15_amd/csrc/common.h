@@ -49,10 +49,42 @@ inline NormRope norm_rope_of(const csa_norm_rope* p) {
            : NormRope{nullptr, 0.0f, 0, nullptr, 0};
 }
 
+// sin and cos of a binary32 angle x, to binary32 rounding.  For |x| < 1.6e6:
+// Cody-Waite argument reduction (Cody and Waite, "Software Manual for the
+// Elementary Functions", 1980) by pi/2 in binary64, pi/2 split into
+// P1 + P2 + P3 with P1 and P2 of 33 significant bits (k P1 and k P2 are exact
+// for |k| < 2^20), then the Taylor series of sin and cos in binary64 on the
+// reduced argument |r| <= pi/4 (terms to r^17 and r^16: truncation error
+// below 1e-19).  Larger arguments take sincosf.  (sincosf reduces arguments
+// above about 2^15 with a routine that keeps a small array in scratch memory,
+// a few memory round trips per call; positions of long contexts reach there.)
+__device__ __forceinline__ void sincos_angle(float x, float* s, float* c) {
+  if (!(fabsf(x) < 1.6e6f)) {
+    sincosf(x, s, c);
+    return;
+  }
+  const double xd = (double)x;
+  const double k = rint(xd * 0.6366197723675814);           // nearest multiple of pi/2
+  const double r = ((xd - k * 1.5707963267341256) - k * 6.077100506303966e-11) - k * 2.0222662487959506e-21;
+  const double r2 = r * r;
+  const double sp = r * (1.0 + r2 * (-1.0 / 6 + r2 * (1.0 / 120 + r2 * (-1.0 / 5040 + r2 * (1.0 / 362880 +
+                    r2 * (-1.0 / 39916800 + r2 * (1.0 / 6227020800.0 + r2 * (-1.0 / 1307674368000.0 +
+                    r2 * (1.0 / 355687428096000.0)))))))));
+  const double cp = 1.0 + r2 * (-1.0 / 2 + r2 * (1.0 / 24 + r2 * (-1.0 / 720 + r2 * (1.0 / 40320 +
+                    r2 * (-1.0 / 3628800 + r2 * (1.0 / 479001600.0 + r2 * (-1.0 / 87178291200.0 +
+                    r2 * (1.0 / 20922789888000.0))))))));
+  switch ((int)k & 3) {                                     // x = k pi/2 + r
+    case 0: *s = (float)sp; *c = (float)cp; break;
+    case 1: *s = (float)cp; *c = (float)-sp; break;
+    case 2: *s = (float)-sp; *c = (float)-cp; break;
+    default: *s = (float)-cp; *c = (float)sp; break;
+  }
+}
+
 // Turn the pair (x, y) by the binary32 angle fl32(pos * theta).
 __device__ __forceinline__ void rope_pair(float& x, float& y, float pos, float theta) {
   float sn, cs;
-  sincosf(__fmul_rn(pos, theta), &sn, &cs);
+  sincos_angle(__fmul_rn(pos, theta), &sn, &cs);
   const float nx = x * cs - y * sn, ny = x * sn + y * cs;
   x = nx;
   y = ny;

@@ -53,6 +53,8 @@ POST_COMPRESS_CASES = [
     ("f32_f32_D32_m7_rope_only", "f32", "f32", 32, 0, 7, 500, 1, 8, False, 0),
     ("idx_bf16_mxfp4_D64_m4_norm_only", "bf16", "mxfp4", 64, 0, 4, 2050, 1, 0, True, 0),
     ("f32_fp8_D64_R16_m4", "f32", "fp8", 64, 16, 4, 999, 2, 16, True, 1 << 20),
+    # angles beyond 1.6e6 (the kernels' library-sincos fallback) next to smaller ones
+    ("f32_f32_D64_m4_far_positions", "f32", "f32", 64, 0, 4, 999, 1, 16, True, 3_000_000),
     # m = 1: the packed quantise-only kernel (8 dims per lane)
     ("win_bf16_fp8_D512_m1", "bf16", "fp8", 512, 64, 1, 777, 1, 64, True, 100000),
     ("f32_fp8_D64_R16_m1", "f32", "fp8", 64, 16, 1, 777, 2, 16, True, 7),
