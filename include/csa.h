@@ -196,6 +196,40 @@ csa_status csa_decode_append(const void* tok, int tok_fmt, int B, const int64_t*
                              const csa_norm_rope* post, hipStream_t stream);
 
 /*
+ * csa_decode_rebuild -- a sequence's decode state recomputed from raw tokens
+ * (kenelite analysis, section 十六: compressed CSA / HCA caches restored for
+ * a shared prefix need the tail of the incomplete compression block
+ * recomputed, and with zero SWA caching the recent window is rebuilt rather
+ * than stored).  After the caller restores the entries of the complete
+ * blocks into `out`, this call recomputes the rest from the raw tokens of
+ * the prefix's last positions.
+ * For each b, rows tok[b][0 .. nb) (row i at tok + b * bstride + i * dim
+ * elements; nb = min(n, n_valid[b]) with n_valid a DEVICE int32 [B], or n
+ * when n_valid is NULL) are the raw tokens at positions p0[b] .. p0[b] +
+ * nb - 1, where p0[b] (DEVICE int64 [B]) is a multiple of m; a sequence with
+ * p0[b] < 0 or not a multiple of m is skipped (nothing written).  The stores
+ * then hold, byte for byte, what nb calls of csa_decode_append at those
+ * positions leave:
+ *   - tail slot q mod tail_rows: the last min(nb, tail_rows) rows;
+ *   - win (when win.rows != NULL) slot q mod W: the last min(nb, W) rows,
+ *     quantised (and processed by post at position q);
+ *   - out entry (q + 1)/m - 1 for every row q that ends a block (entries at
+ *     or past out.cap are skipped); entries of earlier blocks are untouched.
+ * To continue decoding at position P after restoring the entries of the
+ * complete blocks below P, pass the raw tokens of positions p0 .. P - 1 with
+ * p0 = the largest multiple of m at or below max(0, min(P - W, P)): the
+ * window and the incomplete block are then rebuilt, and the blocks in
+ * between recomputed with the bytes they were restored with.
+ * tok: CSA_F32 or CSA_BF16, 16-byte aligned (bstride in elements keeps rows
+ * aligned); tail, m, gate, bias, out, win, W and post as for
+ * csa_decode_append.  Returns CSA_EINVAL on NULL or misaligned pointers,
+ * n < 0, or bad store / window sizes.
+ */
+csa_status csa_decode_rebuild(const void* tok, int tok_fmt, int B, int n, int64_t bstride, const int64_t* p0,
+                              const int32_t* n_valid, void* tail, int tail_rows, int m, const float* gate, const float* bias, csa_store out,
+                              csa_store win, int W, const csa_norm_rope* post, hipStream_t stream);
+
+/*
  * csa_indexer_topk -- Lightning Indexer scores and top-k selection
  * (llm-tech overview, CSA section: the indexer picks the top-k compressed
  * entries; kenelite analysis 5.3: top-512 Flash, top-1024 Pro).

@@ -69,6 +69,7 @@ _SIGS = {
     "csa_last_error": ([], ctypes.c_char_p),
     "csa_compress_kv": ([_P, _I, _I, _I64, _I64, _I, _P, _P, _CStore, _I64, _P, _P], _I),
     "csa_decode_append": ([_P, _I, _I, _P, _P, _I, _I, _P, _P, _CStore, _CStore, _I, _P, _P], _I),
+    "csa_decode_rebuild": ([_P, _I, _I, _I, _I64, _P, _P, _P, _I, _I, _P, _P, _CStore, _CStore, _I, _P, _P], _I),
     "csa_indexer_topk_workspace": ([_I, _I, _I64, _I], _SZ),
     "csa_indexer_topk": ([_CStore, _P, _CStore, _I64, _P, _I, _I, _I, _I, _I, _P, _P, _SZ, _P], _I),
     "csa_attn_workspace": ([_I, _I, _I, _I, _I64], _SZ),
@@ -207,6 +208,22 @@ def decode_append(tok, pos, tail, m: int, gate, bias, out: Store, win: Optional[
     _check(load().csa_decode_append(_ptr(tok), _fmt_of(tok), B, _ptr(pos), _ptr(tail), int(tail.shape[1]), m,
                                     _ptr(gate), _ptr(bias), out.c(), wc, W, _post(post), _stream(stream)),
            "csa_decode_append")
+
+
+def decode_rebuild(tok, p0, tail, m: int, gate, bias, out: Store, win: Optional[Store] = None, W: int = 0,
+                   post: Optional[NormRope] = None, n_valid=None, stream=None):
+    """csa_decode_rebuild: tok [B][n][dim] float32 or bfloat16 (rows contiguous), p0 int64 [B] (positions of
+    row 0, multiples of m), n_valid int32 [B] or None; leaves tail, window and entries as decode appends at
+    p0 .. p0 + n_valid - 1 would."""
+    B, n, D = tok.shape
+    assert tok.stride(2) == 1 and tok.stride(1) == D, "token rows must be contiguous"
+    assert tail.is_contiguous() and tail.dtype == tok.dtype and tail.shape[0] == B and tail.shape[2] == D
+    assert p0.dtype.itemsize == 8 and p0.numel() == B
+    wc = win.c() if win is not None else _CStore(None, None, 0, 0, 0, 0, 0)
+    assert n_valid is None or (n_valid.dtype.itemsize == 4 and n_valid.numel() == B)
+    _check(load().csa_decode_rebuild(_ptr(tok), _fmt_of(tok), B, n, tok.stride(0), _ptr(p0), _ptr(n_valid), _ptr(tail),
+                                     int(tail.shape[1]), m, _ptr(gate), _ptr(bias), out.c(), wc, W, _post(post),
+                                     _stream(stream)), "csa_decode_rebuild")
 
 
 def indexer_topk_workspace(B: int, Tq: int, n_entries: int, k: int) -> int:

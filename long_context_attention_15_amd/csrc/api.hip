@@ -211,6 +211,37 @@ csa_status csa_decode_append(const void* tok, int tok_fmt, int B, const int64_t*
                   stream, "csa_decode_append launch");
 }
 
+csa_status csa_decode_rebuild(const void* tok, int tok_fmt, int B, int n, int64_t bstride, const int64_t* p0,
+                              const int32_t* n_valid, void* tail, int tail_rows, int m, const float* gate, const float* bias, csa_store out,
+                              csa_store win, int W, const csa_norm_rope* post, hipStream_t stream) {
+  g_err[0] = 0;
+  if (B < 0 || n < 0) return fail(CSA_EINVAL, "B and n must be >= 0");
+  if (m < 1 || m > csa::compress_max_m()) return fail(CSA_EINVAL, "m = %d outside [1, %d]", m, csa::compress_max_m());
+  if (!tok || !p0 || !tail || !gate || !bias) return fail(CSA_EINVAL, "tok, p0, tail, gate and bias must be non-NULL");
+  if (tok_fmt != CSA_F32 && tok_fmt != CSA_BF16) return fail(CSA_EUNSUPPORTED, "tok_fmt must be CSA_F32 or CSA_BF16");
+  if (!aligned(tok, 16) || !aligned(tail, 16)) return fail(CSA_EINVAL, "tok and tail must be 16-byte aligned");
+  if (!aligned(p0, 8) || !aligned(n_valid, 4)) return fail(CSA_EINVAL, "p0 must be 8-byte and n_valid 4-byte aligned");
+  if (tail_rows < m || tail_rows % m != 0) return fail(CSA_EINVAL, "tail_rows = %d is not a positive multiple of m", tail_rows);
+  CSA_TRY(check_store(out, "out"));
+  const int esz = tok_fmt == CSA_F32 ? 4 : 2;
+  if (B > 1 && bstride < (int64_t)n * out.dim) return fail(CSA_EINVAL, "bstride below n * dim");
+  if ((bstride * esz) % 16 != 0) return fail(CSA_EINVAL, "bstride must keep rows 16-byte aligned");
+  const int vpl = out.dim >= 64 ? out.dim / 64 : 1;
+  if (out.fmt == CSA_FP8_E4M3 && out.rope_dim % vpl != 0)
+    return fail(CSA_EUNSUPPORTED, "rope_dim must be a multiple of dim / 64");
+  if (win.rows) {
+    CSA_TRY(check_store(win, "win"));
+    if (win.dim != out.dim) return fail(CSA_EINVAL, "win.dim != out.dim");
+    if (W < 1 || W > win.cap) return fail(CSA_EINVAL, "W = %d outside [1, win.cap]", W);
+    if (win.fmt == CSA_FP8_E4M3 && win.rope_dim % vpl != 0)
+      return fail(CSA_EUNSUPPORTED, "win.rope_dim must be a multiple of dim / 64");
+  }
+  CSA_TRY(check_post(post, out.dim, "post"));
+  return launched(csa::launch_decode_rebuild(tok, tok_fmt, B, n, bstride, p0, n_valid, tail, tail_rows, m, gate, bias,
+                                             out, win, W, csa::norm_rope_of(post), stream),
+                  stream, "csa_decode_rebuild launch");
+}
+
 size_t csa_indexer_topk_workspace(int B, int Tq, int64_t n_entries, int k) {
   if (B < 0 || Tq < 0 || k < 1) return 0;
   csa::IdxPlan p = csa::indexer_plan(B, Tq, n_entries, k);

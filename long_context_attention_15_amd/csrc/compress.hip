@@ -297,6 +297,85 @@ __global__ __launch_bounds__(kWave * kCompressWaves) void decode_append_kernel(
                            (int64_t)b * out.cap + j, close, s_alpha[wave], nr, p);
 }
 
+// Rebuild of a sequence's decode state from raw tokens: rows 0 .. nb-1 of
+// sequence b (nb = min(n, n_valid[b]), or n) are the tokens at positions
+// p0[b] .. p0[b] + nb - 1 (p0[b] a multiple of m; otherwise, or p0[b] < 0,
+// the sequence is skipped).  One
+// wavefront per (sequence, row), with the arithmetic of decode_append_kernel,
+// so the stores end byte for byte as n decode appends at those positions
+// leave them: the row goes to tail slot q mod R if it is among the last R
+// rows, its processed row to window slot q mod W if among the last W, and a
+// block that ends at the row is compressed from the rows themselves (they
+// hold the same values the appends read back from the tail ring).
+template <typename TIn, int VPL>
+__global__ __launch_bounds__(kWave * kCompressWaves) void decode_rebuild_kernel(
+    const TIn* __restrict__ tok, int B, int n, int64_t bstride, const int64_t* __restrict__ p0,
+    const int32_t* __restrict__ n_valid, TIn* tail, int R, int m, const float* __restrict__ gate,
+    const float* __restrict__ bias, StoreW out, StoreW win, int W, NormRope nr) {
+  __shared__ float s_alpha[kCompressWaves][kMaxM];
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int64_t item = (int64_t)blockIdx.x * kCompressWaves + wave;
+  const bool in_range = item < (int64_t)B * n;
+  const int b = in_range ? (int)(item / n) : 0;
+  const int i = in_range ? (int)(item % n) : 0;
+  const int64_t q0 = in_range ? p0[b] : -1;
+  const int nb = in_range && n_valid ? (n_valid[b] < n ? n_valid[b] : n) : n;
+  const bool live = in_range && q0 >= 0 && q0 % m == 0 && i < nb;
+  const int64_t q = q0 + i;
+  const int D = out.dim;
+  const TIn* x = tok + (int64_t)b * bstride + (int64_t)i * D;
+  if (live && i >= nb - R && lane * VPL < D) {
+    TIn* tb = tail + (int64_t)b * R * D;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) tb[(q % R) * D + lane * VPL + v] = x[lane * VPL + v];
+  }
+  if (win.rows && live && i >= nb - W) {                // uniform per wavefront
+    float xv[VPL];
+    const bool act = lane * VPL < D;
+    if (act) load_vals<TIn, VPL>(x + lane * VPL, xv);
+    else {
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) xv[v] = 0.0f;
+    }
+    post_row<VPL>(xv, act, D, nr, q);
+    store_entry<VPL>(xv, act, win, (int64_t)b * win.cap + q % W);
+  }
+  const bool close = live && (q + 1) % m == 0 && (q + 1) / m - 1 < out.cap;   // then i >= m - 1
+  if (!__syncthreads_or(close)) return;                // no block closes in this workgroup
+  const int64_t j = close ? (q + 1) / m - 1 : 0;
+  const TIn* first = close ? x - (int64_t)(m - 1) * D : x;
+  compress_entry<TIn, VPL>([&](int k) { return first + (int64_t)k * D; }, m, gate, bias, out,
+                           (int64_t)b * out.cap + j, close, s_alpha[wave], nr, q);
+}
+
+template <typename TIn, int VPL>
+static hipError_t launch_rebuild_t(const void* tok, int B, int n, int64_t bstride, const int64_t* p0,
+                                   const int32_t* n_valid, void* tail, int R, int m, const float* gate, const float* bias, const csa_store& out,
+                                   const csa_store& win, int W, const NormRope& nr, hipStream_t st) {
+  const int64_t items = (int64_t)B * n;
+  if (items == 0) return hipSuccess;
+  const StoreW w = win.rows ? wview(win) : StoreW{nullptr, nullptr, 0, out.dim, 0, out.fmt, 0};
+  hipLaunchKernelGGL((decode_rebuild_kernel<TIn, VPL>), dim3((unsigned)((items + kCompressWaves - 1) / kCompressWaves)),
+                     dim3(kWave * kCompressWaves), 0, st, (const TIn*)tok, B, n, bstride, p0, n_valid, (TIn*)tail, R, m,
+                     gate, bias, wview(out), w, W, nr);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_rebuild(const void* tok, int tok_fmt, int B, int n, int64_t bstride, const int64_t* p0,
+                                 const int32_t* n_valid, void* tail, int R, int m, const float* gate, const float* bias,
+                                 const csa_store& out, const csa_store& win, int W, const NormRope& nr,
+                                 hipStream_t st) {
+  const int vpl = out.dim >= 64 ? out.dim / 64 : 1;
+#define CSA_RB(TT, V) \
+  return launch_rebuild_t<TT, V>(tok, B, n, bstride, p0, n_valid, tail, R, m, gate, bias, out, win, W, nr, st)
+  if (tok_fmt == CSA_F32) {
+    switch (vpl) { case 1: CSA_RB(float, 1); case 2: CSA_RB(float, 2); case 4: CSA_RB(float, 4); default: CSA_RB(float, 8); }
+  } else {
+    switch (vpl) { case 1: CSA_RB(uint16_t, 1); case 2: CSA_RB(uint16_t, 2); case 4: CSA_RB(uint16_t, 4); default: CSA_RB(uint16_t, 8); }
+  }
+#undef CSA_RB
+}
+
 template <typename TIn, int VPL>
 static hipError_t launch_append_t(const void* tok, int B, const int64_t* pos, void* tail, int R, int m,
                                   const float* gate, const float* bias, const csa_store& out, const csa_store& win,

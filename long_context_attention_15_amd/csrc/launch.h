@@ -17,6 +17,10 @@ int compress_max_m();
 hipError_t launch_decode_append(const void* tok, int tok_fmt, int B, const int64_t* pos, void* tail, int R, int m,
                                 const float* gate, const float* bias, const csa_store& out, const csa_store& win,
                                 int W, const NormRope& nr, hipStream_t st);
+hipError_t launch_decode_rebuild(const void* tok, int tok_fmt, int B, int n, int64_t bstride, const int64_t* p0,
+                                 const int32_t* n_valid, void* tail, int R, int m, const float* gate, const float* bias,
+                                 const csa_store& out, const csa_store& win, int W, const NormRope& nr,
+                                 hipStream_t st);
 
 // Indexer: chunk size and chunk count chosen for a call; workspace bytes.
 struct IdxPlan {

@@ -95,6 +95,33 @@ def decode_append(x: np.ndarray, gate: np.ndarray, bias: np.ndarray, m: int, W: 
     return entries, window
 
 
+def restore_state(restored: np.ndarray, x_recent: np.ndarray, gate: np.ndarray, bias: np.ndarray, m: int, W: int,
+                  p0: int):
+    """Decode state of one sequence at position P rebuilt for prefix reuse
+    (kenelite analysis 16, inference infrastructure: compressed CSA / HCA
+    entries are restored from storage, the incomplete compression block at
+    the end is recomputed, and under zero SWA caching the recent window is
+    rebuilt from recomputed raw tokens instead of being stored).
+
+    restored [n_r, D]: entries of the first n_r complete blocks, as stored.
+    x_recent [P - p0, D]: raw tokens of positions p0 .. P-1 (p0 a multiple
+    of m, p0 <= n_r m).  Returns (entries [P // m, D]: the restored ones,
+    then blocks p0/m .. compressed from x_recent (the restored value is kept
+    for a block that is both); window {slot q mod W: position q} for the
+    last min(W, P) positions; tail: positions of the incomplete block).
+    """
+    x_recent = np.asarray(x_recent, np.float64)
+    P = p0 + x_recent.shape[0]
+    n_r = np.asarray(restored).shape[0]
+    entries = [np.asarray(restored[j], np.float64) for j in range(min(n_r, P // m))]
+    for j in range(len(entries), P // m):
+        entries.append(compress(x_recent[j * m - p0: (j + 1) * m - p0], gate, bias, m)[0])
+    window = {q % W: q for q in range(max(0, P - W), P)}
+    tail = list(range((P // m) * m, P))
+    D = x_recent.shape[1]
+    return (np.stack(entries) if entries else np.zeros((0, D))), window, tail
+
+
 # ---------------------------------------------- RMSNorm and partial RoPE
 def rms_norm(x: np.ndarray, gain, eps: float) -> np.ndarray:
     """RMSNorm of every last-axis row (10100 analysis, section 3 item 1,

@@ -195,3 +195,20 @@ def test_norm_rope_blocks_are_validated(lib):
     ok = csa._CNormRope(P, 1e-6, 16, P, 0)
     assert lib.csa_compress_kv(P, csa.F32, 1, 32, 32 * 64, 0, P, P, out, 0, ctypes.byref(ok), None) == 1
     assert "m = 0" in lib.csa_last_error().decode()      # a valid block passes on to the other checks
+
+
+def test_decode_rebuild_rejects_bad_arguments(lib):
+    out = _store(P, 64, 64)
+    nowin = csa._CStore(None, None, 0, 0, 0, 0, 0)
+    call = lambda **kw: lib.csa_decode_rebuild(kw.get("tok", P), csa.F32, 2, kw.get("n", 8), kw.get("bs", 8 * 64),
+                                               kw.get("p0", P), kw.get("nv", None), kw.get("tail", P),
+                                               kw.get("R", 8), kw.get("m", 4), P, P, out, kw.get("win", nowin),
+                                               kw.get("W", 0), None, None)
+    assert call(n=-1) == 1
+    assert call(p0=0) == 1 and "non-NULL" in lib.csa_last_error().decode()
+    assert call(tok=P + 4) == 1
+    assert call(R=6) == 1 and "multiple of m" in lib.csa_last_error().decode()
+    assert call(bs=8 * 64 - 1) == 1                    # rows of batch element 1 overlap element 0
+    assert call(nv=P + 2) == 1                         # n_valid not 4-byte aligned
+    assert call(m=0) == 1
+    assert call(win=_store(P, 8, 64), W=9) == 1        # W beyond the window store

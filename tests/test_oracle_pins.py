@@ -611,3 +611,30 @@ def test_compressed_entry_takes_the_position_of_its_block_end():
     np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
     # m = 1 gives every token its own position
     assert list(O.entry_positions(4, 1, pos0=3)) == [3, 4, 5, 6]
+
+
+def test_restore_state_equals_the_uninterrupted_state():
+    """Prefix reuse (kenelite analysis 16): restoring the entries of the
+    complete blocks, recomputing the incomplete block and rebuilding the
+    window from the last raw tokens gives the state that processing every
+    position leaves: entries = compression of all complete blocks, the
+    window = the last W positions, the tail = the incomplete block."""
+    rng = np.random.default_rng(41)
+    for m, W, P in [(4, 16, 103), (4, 16, 100), (128, 128, 700), (3, 8, 5), (4, 128, 64)]:
+        D = 8
+        x = rng.standard_normal((P + 40, D))
+        g = rng.standard_normal(D) * 0.3
+        b = rng.standard_normal(m) * 0.3
+        p0 = (max(0, min(P - W, P)) // m) * m
+        n_r = rng.integers(p0 // m, P // m + 1)              # restored blocks: at least those below p0
+        restored = O.compress(x[: n_r * m], g, b, m)
+        entries, window, tail = O.restore_state(restored, x[p0:P], g, b, m, W, p0)
+        full = O.compress(x[:P], g, b, m)
+        assert entries.shape == full.shape
+        np.testing.assert_allclose(entries, full, rtol=0, atol=1e-12)
+        e_dec, w_dec = O.decode_append(x, g, b, m, W, 0, P)
+        assert window == {s: q for s, q in w_dec.items() if q >= P - W}
+        assert sorted(window.values()) == list(range(max(0, P - W), P))
+        assert tail == list(range((P // m) * m, P))
+        if e_dec:
+            np.testing.assert_allclose(entries[sorted(e_dec)], np.stack([e_dec[j] for j in sorted(e_dec)]), atol=1e-12)
