@@ -36,6 +36,7 @@ namespace csa {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
@@ -127,7 +128,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_m32_kernel(Args a) {
   __shared__ int s_over;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);    // uniform: scalar registers
   const int hcol = lane & 31, hh = lane >> 5;        // head column, lane half
   const int64_t bq = xcd_remap(blockIdx.x, gridDim.x);   // query row (b * Tq + q)
   const int b = (int)(bq / a.Tq);
@@ -296,34 +298,26 @@ __global__ __launch_bounds__(kThreads, 1) void attn_m32_kernel(Args a) {
       for (int ks = 0; ks < 16; ++ks) qf[ks][hq] = __builtin_bit_cast(bf16x8, *(const u32x4*)(qp + 32 * ks));
     }
   }
-  // LDS byte offsets of this lane's reads within a raw tile.
+  // LDS byte offsets of this lane's reads within a raw tile.  The XOR in
+  // unit_off touches bit 3 of the row only, so 16 rows (entry half, PV step)
+  // are +256 bytes, 4 rows +64 and 4 units +2048 for every lane: one base
+  // register per operand, the rest in the read's immediate offset.
   // K (S^T A operand of entry half eh, K-step ks): row 16 eh + i16, FP8
-  // bytes 32 ks + 8 g .. +8 (unit 2 ks + g / 2, half g & 1): k_fp8[eh] + 1024
-  // ks; RoPE step ks = 14 + j: BF16 dims 448 + 32 j + 8 g (unit 28 + 4 j + g).
-  int k_fp8[2], k_rope[2][2];
-#pragma unroll
-  for (int eh = 0; eh < 2; ++eh) {
-    k_fp8[eh] = unit_off(16 * eh + i16, g >> 1) + 8 * (g & 1);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) k_rope[eh][j] = unit_off(16 * eh + i16, 28 + 4 * j + g);
-  }
+  // bytes 32 ks + 8 g .. +8 (unit 2 ks + g / 2, half g & 1):
+  // k_fp8 + 256 eh + 1024 ks; RoPE step ks = 14 + j: BF16 dims 448 + 32 j +
+  // 8 g (unit 28 + 4 j + g): k_rope + 256 eh + 2048 j.
+  const int k_fp8 = unit_off(i16, g >> 1) + 8 * (g & 1);
+  const int k_rope = unit_off(i16, 28 + g);
   // V^T FP8 (8-bit transposing reads): 16-lane group g = lane >> 4 covers
   // dims 16 (g & 1) .. +16 of a 32-dim block (unit 2 db + (g & 1)), entries
   // of half hh = g >> 1; source lane i16 reads 8 bytes of row
-  // pv_entry(c, hh, i16 >> 1), half i16 & 1: v_fp8[c] + 1024 db.
-  int v_fp8[2];
-#pragma unroll
-  for (int c = 0; c < 2; ++c) v_fp8[c] = unit_off(pv_entry(c, hh, i16 >> 1), g & 1) + 8 * (i16 & 1);
+  // pv_entry(c, hh, i16 >> 1), half i16 & 1: v_fp8 + 256 c + 1024 db.
+  const int v_fp8 = unit_off(pv_entry(0, hh, i16 >> 1), g & 1) + 8 * (i16 & 1);
   // V^T RoPE (16-bit transposing reads): row pv_entry(c, hh, 4 rd + (i16 >> 2)),
   // bf16 dims 448 + 32 bb + 16 (g & 1) + 4 (i16 & 3) .. +4, i.e. unit
-  // 28 + 4 bb + 2 (g & 1) + (i16 & 3) / 2, half i16 & 1: v_rope[c][rd] + 2048 bb.
-  int v_rope[2][2];
-#pragma unroll
-  for (int c = 0; c < 2; ++c)
-#pragma unroll
-    for (int rd = 0; rd < 2; ++rd)
-      v_rope[c][rd] = unit_off(pv_entry(c, hh, 4 * rd + (i16 >> 2)), 28 + 2 * (g & 1) + ((i16 & 3) >> 1)) +
-                      8 * (i16 & 1);
+  // 28 + 4 bb + 2 (g & 1) + (i16 & 3) / 2, half i16 & 1:
+  // v_rope + 256 c + 64 rd + 2048 bb.
+  const int v_rope = unit_off(pv_entry(0, hh, i16 >> 2), 28 + 2 * (g & 1) + ((i16 & 3) >> 1)) + 8 * (i16 & 1);
 
   f32x16 acc[16];
 #pragma unroll
@@ -358,13 +352,24 @@ __global__ __launch_bounds__(kThreads, 1) void attn_m32_kernel(Args a) {
     }
     table2(2 * wave, (&Tsel[0][0])[2 * wave * kT + lane]);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // the first kLead tiles' rows go out even past a short list's end (the
+    // zero row), so this wait has one form; in the tile loop row loads go out
+    // for the list's tiles only, and each wait counts the row loads issued
+    // after the tile it waits for (loads complete in order; the sel-entry
+    // loads in between only make a wait stricter)
 #pragma unroll
     for (int pt = 0; pt < kLead; ++pt) {
       const uint8_t* src = dma_src(pt);
 #pragma unroll
       for (int jj = 0; jj < kLoadsW; ++jj) dma_rows(src, pt, jj);
     }
-    M32_WAIT_VMCNT((kLead - 1) * kLoadsW);      // tile 0 in (loads complete in order)
+    static_assert(kLead == 3, "the waits count kLead - 1 tiles of loads");
+    M32_WAIT_VMCNT((kLead - 1) * kLoadsW);      // tile 0 in
+    // the first tiles' rows, issued back to back, follow within a few
+    // hundred cycles; waiting for them here tells the compiler that the
+    // query operand loads (issued before any row) have landed, so it puts no
+    // waits for them into the tile loop, where they would count row loads
+    M32_WAIT_VMCNT(0);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
     for (int it = 0; it < ntiles; ++it) {
@@ -400,8 +405,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_m32_kernel(Args a) {
       u32x4 kb[4];
       auto kread = [&](int r) {
         const int ks = r >> 1, eh = r & 1;
-        if (ks < 14) kf[r] = *(const u32x2*)(raw + k_fp8[eh] + 1024 * ks);
-        else kb[r - 28] = *(const u32x4*)(raw + k_rope[eh][ks - 14]);
+        if (ks < 14) kf[r] = *(const u32x2*)(raw + k_fp8 + 256 * eh + 1024 * ks);
+        else kb[r - 28] = *(const u32x4*)(raw + k_rope + 256 * eh + 2048 * (ks - 14));
       };
       // The operand of read r is converted during step r - 1, into the
       // other of two register sets, so that a conversion never writes the
@@ -432,7 +437,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_m32_kernel(Args a) {
       v2i32 vf[2][14];
 #pragma unroll
       for (int db = 0; db < kVD; ++db)
-        vf[0][db] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32*)(raw + v_fp8[0] + 1024 * db));
+        vf[0][db] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32*)(raw + v_fp8 + 1024 * db));
       __builtin_amdgcn_sched_barrier(0);
 
       // ---- softmax: lane holds entries 8 (r >> 2) + 4 hh + (r & 3) of head h
@@ -495,7 +500,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_m32_kernel(Args a) {
       // converted during product f - 1 into the other of two register sets.
       u32x4 vop[2];
       auto vread = [&](int n) {                  // FP8 block n of the 28 (step n / 14, block n % 14)
-        vf[n / 14][n % 14] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32*)(raw + v_fp8[n / 14] + 1024 * (n % 14)));
+        vf[n / 14][n % 14] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32*)(raw + v_fp8 + 256 * (n / 14) + 1024 * (n % 14)));
       };
       auto vconv = [&](int f) {
         const int c = f >> 4, db = f & 15;
@@ -503,8 +508,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_m32_kernel(Args a) {
           vop[f & 1] = cvt8(u32x2{(unsigned)vf[c][db].x, (unsigned)vf[c][db].y}, 1.0f);
         } else {
           const int bb = db - 14;
-          const u32x2 r0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(raw + v_rope[c][0] + 2048 * bb)));
-          const u32x2 r1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(raw + v_rope[c][1] + 2048 * bb)));
+          const u32x2 r0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(raw + v_rope + 256 * c + 2048 * bb)));
+          const u32x2 r1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(raw + v_rope + 256 * c + 64 + 2048 * bb)));
           vop[f & 1] = u32x4{r0.x, r0.y, r1.x, r1.y};
         }
       };
@@ -518,13 +523,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_m32_kernel(Args a) {
         if (f + 1 < 32) vconv(f + 1);
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vop[f & 1]), db < 14 ? ps[c] : pr[c],
                                                           acc[db], 0, 0, 0);
-        if (f % 3 == 1 && f / 3 < kLoadsW) dma_rows(dsrc, it + kLead, f / 3);   // 9 row loads, every third product
+        if (f % 3 == 1 && f / 3 < kLoadsW && it + kLead < ntiles)       // 9 row loads, every third product
+          dma_rows(dsrc, it + kLead, f / 3);
         __builtin_amdgcn_sched_barrier(0);
       }
-      // rows of tile it+1 are in before the barrier: loads complete in
-      // order, and after them every wave issued the loads of tiles it+2 and
-      // it+3 (and the table loads, which only make the wait stricter)
-      M32_WAIT_VMCNT(2 * kLoadsW);
+      // rows of tile it+1 are in before the barrier: after its loads every
+      // wave issued those of tiles it+2 and it+3 that exist (and the table
+      // loads, which only make the wait stricter)
+      if (it + 3 < ntiles) M32_WAIT_VMCNT(2 * kLoadsW);
+      else if (it + 2 < ntiles) M32_WAIT_VMCNT(kLoadsW);
+      else {
+        asm volatile("; last tiles of the list" ::: "memory");
+        M32_WAIT_VMCNT(0);
+      }
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
     // every LDS DMA of this pass has landed before anything reuses LDS
@@ -588,10 +599,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_m32_kernel(Args a) {
       for (int db = 0; db < 16; ++db)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          u32x2 w;
-          w.x = f32_to_bf16(acc[db][4 * q4 + 0] * scale) | (f32_to_bf16(acc[db][4 * q4 + 1] * scale) << 16);
-          w.y = f32_to_bf16(acc[db][4 * q4 + 2] * scale) | (f32_to_bf16(acc[db][4 * q4 + 3] * scale) << 16);
-          *(u32x2*)(stg + hcol * kStageRow + 2 * (32 * db + 8 * q4 + 4 * hh)) = w;
+          bf16x4 w;                              // packed hardware conversion, round to nearest even
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc[db][4 * q4 + e] * scale);
+          *(u32x2*)(stg + hcol * kStageRow + 2 * (32 * db + 8 * q4 + 4 * hh)) = __builtin_bit_cast(u32x2, w);
         }
     }
     // (each wave writes and reads only its own rows: its LDS accesses stay in order)

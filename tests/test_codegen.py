@@ -5,7 +5,9 @@ explicit vmcnt waits for LDS DMAs issued several tiles ahead.  A register
 spill inside the tile loop brings a scratch reload and a full vmcnt(0) wait
 into every tile, which drains that pipeline (a 40 % slowdown when it last
 happened, with identical results), so it is checked here rather than by the
-timing."""
+timing.  The tile loop of the recompute pass (run only after a logit
+overflowed the running reference) may reload one spilled value; the
+kernel's own full wait for the list's last tiles is marked in its text.""" 
 import os
 import re
 import shutil
@@ -19,12 +21,18 @@ SRC = os.path.join(B.CSRC, "attn_m32.hip")
 
 
 def _tile_loops(asm):
-    """{label: body lines} of the innermost loops (backward branches) whose
-    body holds at least 96 MFMA instructions: the tile loops, one per pass
-    of each instantiation."""
+    """[(kernel, label, body lines)] of the innermost loops (backward
+    branches) whose body holds at least 96 MFMA instructions, in program
+    order: per kernel instantiation, the main pass's tile loop, then the
+    recompute pass's."""
     lines = asm.split("\n")
-    labels = {}
+    labels, kernel_at = {}, []
+    kernel = None
     for i, line in enumerate(lines):
+        m = re.match(r"^(_Z\w*attn_m32_kernel\w*):", line)
+        if m:
+            kernel = m.group(1)
+        kernel_at.append(kernel)
         m = re.match(r"^(\.LBB\d+_\d+):", line)
         if m:
             labels[m.group(1)] = i
@@ -37,7 +45,12 @@ def _tile_loops(asm):
                 spans.append((a, i, m.group(1)))
     inner = [s for s in spans if not any(o != s and s[0] <= o[0] and o[1] <= s[1] and (o[0], o[1]) != (s[0], s[1])
                                          for o in spans)]
-    return {name: lines[a: e + 1] for a, e, name in inner}
+    seen, out = set(), []
+    for a, e, name in sorted(inner):
+        if name not in seen:
+            seen.add(name)
+            out.append((kernel_at[a], name, lines[a: e + 1]))
+    return out
 
 
 @pytest.mark.skipif(not os.path.exists(B.HIPCC) and shutil.which("hipcc") is None, reason="hipcc not available")
@@ -47,9 +60,30 @@ def test_attention_tile_loops_have_no_spills_or_full_waits(tmp_path):
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
     loops = _tile_loops(out.read_text())
-    assert len(loops) >= 4, f"expected the tile loops of both instantiations, found {len(loops)}"
-    for name, body in loops.items():
-        scratch = [x.strip() for x in body if "scratch_" in x]
-        full = [x.strip() for x in body if re.search(r"s_waitcnt\s+vmcnt\(0\)", x)]
-        assert not scratch, f"{name}: scratch accesses in the tile loop: {scratch[:4]}"
-        assert not full, f"{name}: full vmcnt waits in the tile loop: {full[:4]}"
+    kernels = sorted(set(k for k, _, _ in loops))
+    assert len(kernels) == 2, f"expected two instantiations, found {kernels}"
+    for kern in kernels:
+        mine = [(name, body) for k, name, body in loops if k == kern]
+        assert len(mine) == 2, f"{kern}: expected the main and recompute tile loops, found {len(mine)}"
+        for n, (name, body) in enumerate(mine):
+            scratch = [x.strip() for x in body if "scratch_" in x]
+            limit = 0 if n == 0 else 1
+            assert len(scratch) <= limit, f"{kern} {name}: scratch accesses in the tile loop: {scratch[:4]}"
+            # the loop's own waits: two tiles of row loads (18) in flight, one
+            # tile (9) near the end, none (marked) for the last tiles; any
+            # other count is the compiler waiting on something it loaded and
+            # would also wait for the row loads in flight
+            stray, n9, n0 = [], 0, 0
+            for i, x in enumerate(body):
+                m = re.search(r"s_waitcnt\s+vmcnt\((\d+)\)", x)
+                if not m:
+                    continue
+                c = int(m.group(1))
+                if c == 0 and any("last tiles of the list" in y for y in body[max(0, i - 4): i]):
+                    n0 += 1
+                elif c == 9:
+                    n9 += 1
+                elif c < 18:
+                    stray.append(x.strip())
+            assert len(stray) <= limit and n9 <= 1 and n0 <= 1, \
+                f"{kern} {name}: waits on the row loads in flight: {stray[:6]} (vmcnt(9) x{n9}, marked x{n0})"
