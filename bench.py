@@ -168,9 +168,13 @@ class Prefill128K:
         csa_pairs = self.pairs(self.m, self.N, self.k)
         hca_pairs = self.pairs(self.mh, self.Nh)
         fl = lambda p: 4.0 * H * D * p          # QK^T and PV, 2 flops per MAC
+        # indexer: every (query, visible compressed entry) pair scores H_I dot
+        # products of d_I dims (the head-weighted ReLU sum is VALU work)
+        idx_pairs = self.pairs(self.m, self.N) - (self.W * (self.W + 1) // 2 + (self.T - self.W) * self.W)
         return {
             "csa_sparse_attn_prefill": {"flops": fl(csa_pairs), "pairs": csa_pairs},
             "hca_attn": {"flops": fl(hca_pairs), "pairs": hca_pairs},
+            "csa_indexer_topk": {"flops": 2.0 * self.HI * self.dI * idx_pairs, "pairs": idx_pairs},
         }
 
 
@@ -517,11 +521,17 @@ def main():
         result["ms_per_step"] = ms
         kernels.update({f"prefill/{n}": v for n, v in per.items()})
         alg = pf.algorithmic()
-        dom = max(alg, key=lambda n: per[n])
+        dom = max((n for n in alg if n != "csa_indexer_topk"), key=lambda n: per[n])
         ach = alg[dom]["flops"] / (per[dom] * 1e-3) / 1e12
         result["roofline"] = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": MFMA_BF16_TFLOPS,
                               "unit": "TFLOP/s", "frac": ach / MFMA_BF16_TFLOPS, "traffic": recorded_traffic(dom)}
         result["prefill_ops_tflops"] = {n: alg[n]["flops"] / (per[n] * 1e-3) / 1e12 for n in alg}
+        # the indexer scores FP8 keys on bf16 MFMAs (exact conversion), so its
+        # peak is the bf16 one; top-k selection rides along in the same kernel
+        ia = alg["csa_indexer_topk"]["flops"] / (per["csa_indexer_topk"] * 1e-3) / 1e12
+        result["indexer_roofline"] = {"kernel": "csa_indexer_topk", "bound": "mfma", "achieved": ia,
+                                      "peak": MFMA_BF16_TFLOPS, "unit": "TFLOP/s", "frac": ia / MFMA_BF16_TFLOPS,
+                                      "flops": alg["csa_indexer_topk"]["flops"]}
         # RMSNorm + partial RoPE fused into the step (stored rows and queries)
         ms_p, per_p = time_ops(pf.ops(pf.post), args.steps, args.warmup)
         result["norm_rope_prefill"] = {"ms_per_step": ms_p, "added_ms": ms_p - ms,

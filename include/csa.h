@@ -121,12 +121,14 @@ typedef struct {
                                entries, lse = ln sum_e exp(l_e) (-inf if none)  */
 #define CSA_WIN_RING 2      /* the window store is a ring of W slots per batch
                                element; position p lives in slot p mod W      */
-#define CSA_BATCH_INVARIANT 4  /* one workgroup per (query row, 64 heads) over
-                               the whole entry list, never a split list: a
-                               row's result bits depend on its own inputs
+#define CSA_BATCH_INVARIANT 4  /* a row's result bits depend on its own inputs
                                only, whatever else is in the batch (the
                                default splits few-query calls to fill the
-                               chip, and the split count follows B)          */
+                               chip, and the split count follows B).  Calls
+                               with Tq = 1 and a workspace split every list
+                               at a fixed 512 entries and merge the splits in
+                               a fixed order; other calls run one workgroup
+                               per (query row, 64 heads) over the whole list */
 
 /* diagnostic event counters (csa_diag_counters) */
 #define CSA_DIAG_INDEXER_GIVEUPS 0      /* one-pass long-list indexer workgroups that

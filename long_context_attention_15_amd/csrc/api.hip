@@ -298,7 +298,8 @@ static csa_status run_attn(csa::AttnCall& c, int flags, const csa_norm_rope* q_p
   if (need > 0 && c.ws && c.ws_bytes < need)
     return fail(CSA_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, c.ws_bytes);
   if (need > 0 && c.ws && !aligned(c.ws, 16)) return fail(CSA_EINVAL, "ws must be 16-byte aligned");
-  c.allow_split = need > 0 && c.ws != nullptr && !(flags & CSA_BATCH_INVARIANT);
+  c.invariant = (flags & CSA_BATCH_INVARIANT) != 0;
+  c.allow_split = need > 0 && c.ws != nullptr && (!c.invariant || c.Tq == 1);
   return launched(csa::launch_attn(c, stream), stream, what);
 }
 

@@ -368,6 +368,24 @@ static int attn_nsplit(int B, int Tq, int H, int D, int64_t max_list, bool mfma,
   return attn_nsplit_for(B, Tq, H, s.hg ? s.hg : 1, max_list, 64, 512, split_len);
 }
 
+// Batch-invariant splits of one-query-per-sequence calls: a fixed length
+// (a function of the list length only, never of the batch), so a row's
+// splits, and the fixed-order merge of their partials, are the same whatever
+// else is in the batch.
+constexpr int kInvSplit = 512;
+
+static int attn_nsplit_invariant(int Tq, int64_t max_list, int& split_len) {
+  split_len = 0;
+  if (Tq != 1 || max_list <= kInvSplit) return 1;
+  int64_t len = kInvSplit, ns = (max_list + len - 1) / len;
+  if (ns > kMaxSplit) {
+    len = ((max_list + kMaxSplit - 1) / kMaxSplit + 31) / 32 * 32;
+    ns = (max_list + len - 1) / len;
+  }
+  split_len = (int)len;
+  return (int)ns;
+}
+
 size_t attn_workspace(int B, int Tq, int H, int D, int64_t max_list) {
   if (!attn_supported(H, D)) return 0;
   int len;
@@ -377,6 +395,8 @@ size_t attn_workspace(int B, int Tq, int H, int D, int64_t max_list) {
     const int ns2 = attn_nsplit(B, Tq, H, D, max_list, true, len);
     ns = ns2 > ns ? ns2 : ns;
   }
+  const int ns3 = attn_nsplit_invariant(Tq, max_list, len);   // CSA_BATCH_INVARIANT
+  ns = ns3 > ns ? ns3 : ns;
   if (ns <= 1) return 0;
   return (size_t)B * Tq * H * ns * (D + 2) * sizeof(float);
 }
@@ -394,7 +414,10 @@ hipError_t launch_attn(const AttnCall& c, hipStream_t st) {
   const int64_t max_list = (c.mode == kModeSel ? c.k : (c.mode == kModeRange ? c.n_entries : 0)) + c.W;
   int len = 0;
   const bool mfma = attn_mfma_eligible(c.q_fmt, c.H, c.D, c.ckv.rows ? c.ckv : c.win, c.prior_o != nullptr, c.tau);
-  a.nsplit = c.allow_split ? attn_nsplit(c.B, c.Tq, c.H, c.D, max_list, mfma, len) : 1;
+  // a prior partial is merged into the final output, so its calls do not split
+  a.nsplit = !c.allow_split || c.prior_o ? 1
+            : (c.invariant ? attn_nsplit_invariant(c.Tq, max_list, len)
+                           : attn_nsplit(c.B, c.Tq, c.H, c.D, max_list, mfma, len));
   a.split_len = len;
   a.ws = (float*)c.ws;
   if ((int64_t)c.B * c.Tq == 0) return hipSuccess;

@@ -69,6 +69,7 @@ struct Args {
   void* out; int out_f32; float* lse; int partial;
   int nsplit; int split_len; float* ws;
   NormRope qn;
+  const float* prior_o; const float* prior_lse;   // kPrior: partial (o, lse) merged in the epilogue
 };
 
 // Zero row that empty slots gather from (device globals start zeroed).
@@ -118,7 +119,7 @@ __device__ __forceinline__ float swap32_sum(float x) {
   return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
 }
 
-template <bool kQPost>
+template <bool kQPost, bool kPrior>
 __global__ __launch_bounds__(kThreads, 1) void attn_m32_kernel(Args a) {
   __shared__ __attribute__((aligned(16))) uint8_t Raw[kStages][kTileBytes];
   __shared__ const uint8_t* Tptr[kSlots][kT];                     // row address (zero row if empty)
@@ -564,16 +565,28 @@ __global__ __launch_bounds__(kThreads, 1) void attn_m32_kernel(Args a) {
   // instruction writes one contiguous piece of a head row.
   const bool split = a.nsplit > 1;
   float scale = 1.0f, lse = -INFINITY;
+  float pscale = 0.0f;                           // kPrior: weight of the prior partial's output
   if (!split) {
-    const float M = fmaxf(mrun, sig2);
+    // kPrior: the partial enters as one more term with logit lse_p and value
+    // o_p (a merge of softmax sums over disjoint entry sets)
+    const float lp2 = kPrior ? a.prior_lse[bq * a.H + h] * kLog2e : -INFINITY;
+    const float M = fmaxf(fmaxf(mrun, sig2), lp2);
     scale = 0.0f;
     if (M > -INFINITY) {
       const float fm = mrun > -INFINITY ? exp2f(mrun - M) : 0.0f;
-      const float Z = lrun * fm + (sig2 > -INFINITY ? exp2f(sig2 - M) : 0.0f);
+      const float fp = lp2 > -INFINITY ? exp2f(lp2 - M) : 0.0f;
+      const float Z = lrun * fm + fp + (sig2 > -INFINITY ? exp2f(sig2 - M) : 0.0f);
       scale = fm / Z;
+      pscale = fp / Z;
       lse = (M + log2f(Z)) * kLn2;
     }
   }
+  const float* const po = kPrior ? a.prior_o + (bq * a.H + h) * (int64_t)kD + 4 * hh : nullptr;
+  auto prior4 = [&](int d) {                     // o_p of dims d .. d + 3 (this lane's), or 0
+    float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (kPrior && pscale != 0.0f) v = *(const float4*)(po + d);
+    return v;
+  };
   const bool f32 = split || a.out_f32;
   constexpr int kStageRow = 1024 + 16;
   uint8_t* const stg = &Raw[0][0] + wave * 32 * kStageRow;
@@ -588,9 +601,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_m32_kernel(Args a) {
         const int db = 8 * half + k8;
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 pv = prior4(32 * db + 8 * q4);
           float4 v;
-          v.x = acc[db][4 * q4 + 0] * scale; v.y = acc[db][4 * q4 + 1] * scale;
-          v.z = acc[db][4 * q4 + 2] * scale; v.w = acc[db][4 * q4 + 3] * scale;
+          v.x = acc[db][4 * q4 + 0] * scale + pv.x * pscale; v.y = acc[db][4 * q4 + 1] * scale + pv.y * pscale;
+          v.z = acc[db][4 * q4 + 2] * scale + pv.z * pscale; v.w = acc[db][4 * q4 + 3] * scale + pv.w * pscale;
           *(float4*)(stg + hcol * kStageRow + 4 * (32 * k8 + 8 * q4 + 4 * hh)) = v;
         }
       }
@@ -599,9 +613,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_m32_kernel(Args a) {
       for (int db = 0; db < 16; ++db)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 pv = prior4(32 * db + 8 * q4);
+          const float pe[4] = {pv.x, pv.y, pv.z, pv.w};
           bf16x4 w;                              // packed hardware conversion, round to nearest even
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc[db][4 * q4 + e] * scale);
+          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(acc[db][4 * q4 + e] * scale + pe[e] * pscale);
           *(u32x2*)(stg + hcol * kStageRow + 2 * (32 * db + 8 * q4 + 4 * hh)) = __builtin_bit_cast(u32x2, w);
         }
     }
@@ -633,7 +649,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_m32_kernel(Args a) {
 // exp2 can resolve, so it takes scales above 1e4 / (1e30 log2 e) only; other
 // scales (tiny, zero or negative) take the general kernel.
 bool attn_mfma_eligible(int q_fmt, int H, int D, const csa_store& kv, bool has_prior, float tau) {
-  return !has_prior && tau * kLog2e * 1.0e30f >= 1.0e4f && q_fmt == CSA_BF16 && D == kD && H % 64 == 0 &&
+  (void)has_prior;                               // a prior partial is merged in the epilogue
+  return tau * kLog2e * 1.0e30f >= 1.0e4f && q_fmt == CSA_BF16 && D == kD && H % 64 == 0 &&
          kv.fmt == CSA_FP8_E4M3 && kv.row_bytes == kRow;
 }
 
@@ -649,11 +666,14 @@ hipError_t launch_attn_m32(const AttnCall& c, int nsplit, int split_len, hipStre
   a.out = c.out; a.out_f32 = c.partial; a.lse = c.lse; a.partial = c.partial;
   a.nsplit = nsplit; a.split_len = split_len; a.ws = (float*)c.ws;
   a.qn = c.qn;
+  a.prior_o = c.prior_o; a.prior_lse = c.prior_lse;
   const dim3 grid((unsigned)((int64_t)c.B * c.Tq), c.H / 64, nsplit);
-  if (c.qn.gain || c.qn.rope_dims > 0)
-    hipLaunchKernelGGL(attn_m32_kernel<true>, grid, dim3(kThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL(attn_m32_kernel<false>, grid, dim3(kThreads), 0, st, a);
+  const bool post = c.qn.gain || c.qn.rope_dims > 0, prior = c.prior_o != nullptr;
+  if (prior && nsplit != 1) return hipErrorInvalidValue;        // a prior merges into the final output only
+  if (post && prior) hipLaunchKernelGGL((attn_m32_kernel<true, true>), grid, dim3(kThreads), 0, st, a);
+  else if (post) hipLaunchKernelGGL((attn_m32_kernel<true, false>), grid, dim3(kThreads), 0, st, a);
+  else if (prior) hipLaunchKernelGGL((attn_m32_kernel<false, true>), grid, dim3(kThreads), 0, st, a);
+  else hipLaunchKernelGGL((attn_m32_kernel<false, false>), grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 

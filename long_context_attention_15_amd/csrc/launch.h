@@ -56,6 +56,7 @@ struct AttnCall {
   void* out; float* lse; int partial;
   void* ws; size_t ws_bytes;
   int allow_split;                                 // split long lists over workgroups (needs ws)
+  int invariant;                                   // splits independent of the batch (CSA_BATCH_INVARIANT)
   NormRope qn;                                     // RMSNorm / partial RoPE of the queries
 };
 enum { kModeNone = 0, kModeSel = 1, kModeRange = 2 };
