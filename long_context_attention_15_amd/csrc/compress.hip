@@ -21,6 +21,10 @@ constexpr int kRowBatch = 8;   // token rows whose loads are in flight together
 template <typename TIn, int VPL>
 __device__ __forceinline__ void load_vals(const TIn* p, float (&v)[VPL]);
 
+// one element as float (BF16 widened exactly, as load_vals does)
+__device__ __forceinline__ float ldf(const float* p) { return *p; }
+__device__ __forceinline__ float ldf(const uint16_t* p) { return bf16_to_f32(*p); }
+
 template <>
 __device__ __forceinline__ void load_vals<float, 1>(const float* p, float (&v)[1]) { v[0] = *p; }
 template <>
@@ -292,9 +296,10 @@ __global__ __launch_bounds__(kWave * kCompressWaves) void decode_append_kernel(
   const bool close = live && (p + 1) % m == 0 && (p + 1) / m - 1 < out.cap;
   if (!__syncthreads_or(close)) return;               // no block closes in this workgroup
   const int64_t j = close ? (p + 1) / m - 1 : 0;
-  const int64_t r0 = close ? (p + 1 - m) % R : 0;      // first row of the block in the ring
-  compress_entry<TIn, VPL>([&](int i) { return (const TIn*)tb + ((r0 + i) % R) * D; }, m, gate, bias, out,
-                           (int64_t)b * out.cap + j, close, s_alpha[wave], nr, p);
+  const int r0 = close ? (int)((p + 1 - m) % R) : 0;   // first row of the block in the ring
+  compress_entry<TIn, VPL>(
+      [&](int i) { return (const TIn*)tb + (int64_t)(r0 + i >= R ? r0 + i - R : r0 + i) * D; }, m, gate, bias, out,
+      (int64_t)b * out.cap + j, close, s_alpha[wave], nr, p);
 }
 
 // Rebuild of a sequence's decode state from raw tokens: rows 0 .. nb-1 of
@@ -376,6 +381,129 @@ hipError_t launch_decode_rebuild(const void* tok, int tok_fmt, int B, int n, int
 #undef CSA_RB
 }
 
+// Decode-time maintenance for long blocks (m >= kWideMinM, the HCA cache):
+// one workgroup of kWideWaves wavefronts per sequence, so a block close does
+// not walk all m rows twice in one wavefront.  Wavefront 0 does the tail and
+// window rows as decode_append_kernel does.  A close stays byte-identical to
+// compress_entry: the wavefronts share the logits row by row with its per-row
+// code (lane layout, FMA chain and reduction of one row do not depend on
+// which wavefront runs them), wavefront 0 runs its softmax code, each thread
+// forms one dim's weighted sum in its order over the rows, and wavefront 0
+// takes the sums back into its lane layout for post_row and store_entry.
+// The block's last row is the token itself (read from tok, so no thread reads
+// another thread's fresh tail write).
+constexpr int kWideWaves = 8;
+constexpr int kWideMinM = 32;
+
+template <typename TIn, int VPL>
+__global__ __launch_bounds__(kWave * kWideWaves) void decode_append_wide_kernel(
+    const TIn* __restrict__ tok, int B, const int64_t* __restrict__ pos, TIn* tail, int R, int m,
+    const float* __restrict__ gate, const float* __restrict__ bias, StoreW out, StoreW win, int W, NormRope nr) {
+  __shared__ float s_alpha[kMaxM];
+  __shared__ float s_acc[512];
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int b = blockIdx.x;
+  const int64_t p = pos[b];
+  const bool live = p >= 0;
+  const int D = out.dim;
+  const TIn* x = tok + (int64_t)b * D;
+  TIn* tb = tail + (int64_t)b * R * D;
+  const bool active = lane * VPL < D;
+  if (wave == 0) {
+    if (live && active) {
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) tb[(p % R) * D + lane * VPL + v] = x[lane * VPL + v];
+    }
+    if (win.rows && live) {
+      float xv[VPL];
+      if (active) load_vals<TIn, VPL>(x + lane * VPL, xv);
+      else {
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) xv[v] = 0.0f;
+      }
+      post_row<VPL>(xv, active, D, nr, p);
+      store_entry<VPL>(xv, active, win, (int64_t)b * win.cap + p % W);
+    }
+  }
+  const bool close = live && (p + 1) % m == 0 && (p + 1) / m - 1 < out.cap;   // uniform in the workgroup
+  if (!close) return;
+  const int r0 = (int)((p + 1 - m) % R);              // ring row of the block's first token
+  auto row = [&](int i) {                             // r0 + i < 2R: one conditional subtraction
+    const int ri = r0 + i >= R ? r0 + i - R : r0 + i;
+    return i == m - 1 ? x : (const TIn*)tb + (int64_t)ri * D;
+  };
+  // logits: rows wave * kWideRows .. +kWideRows, then every kWideWaves * kWideRows
+  // on, all of a wavefront's rows in flight together
+  constexpr int kWideRows = 16;
+  float g[VPL];
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) g[v] = active ? gate[lane * VPL + v] : 0.0f;
+  const int lo = active ? lane * VPL : 0;
+  for (int i0 = wave * kWideRows; i0 < m; i0 += kWideWaves * kWideRows) {
+    float xr[kWideRows][VPL];
+#pragma unroll
+    for (int u = 0; u < kWideRows; ++u) load_vals<TIn, VPL>(row(i0 + u < m ? i0 + u : m - 1) + lo, xr[u]);
+#pragma unroll
+    for (int u = 0; u < kWideRows; ++u) {
+      if (i0 + u >= m) break;                    // uniform
+      float pr = 0.0f;
+      if (active) {
+#pragma unroll
+        for (int v = 0; v < VPL; ++v) pr = fmaf(xr[u][v], g[v], pr);
+      }
+      pr = wave_sum(pr);
+      if (lane == 0) s_alpha[i0 + u] = pr + bias[i0 + u];
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {                                // the softmax weights, as compress_entry forms them
+    float mx = -INFINITY;
+    for (int i = lane; i < m; i += kWave) mx = fmaxf(mx, s_alpha[i]);
+    mx = wave_max(mx);
+    float sum = 0.0f;
+    for (int i = lane; i < m; i += kWave) {
+      const float ev = expf(s_alpha[i] - mx);
+      s_alpha[i] = ev;
+      sum += ev;
+    }
+    sum = wave_sum(sum);
+    for (int i = lane; i < m; i += kWave) s_alpha[i] = s_alpha[i] / sum;
+  }
+  __syncthreads();
+  // weighted sum: thread t owns dim t, the terms in block order
+  for (int d = threadIdx.x; d < D; d += kWave * kWideWaves) {
+    float acc = s_alpha[0] * ldf(row(0) + d);
+    for (int i0 = 1; i0 < m; i0 += 64) {        // 64 rows' loads in flight
+      float xv[64];
+#pragma unroll
+      for (int u = 0; u < 64; ++u) xv[u] = ldf(row(i0 + u < m ? i0 + u : m - 1) + d);
+#pragma unroll
+      for (int u = 0; u < 64; ++u)
+        if (i0 + u < m) acc = fmaf(s_alpha[i0 + u], xv[u], acc);
+    }
+    s_acc[d] = acc;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    float acc[VPL];
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) acc[v] = active ? s_acc[lane * VPL + v] : 0.0f;
+    post_row<VPL>(acc, active, D, nr, p);
+    store_entry<VPL>(acc, active, out, (int64_t)b * out.cap + (p + 1) / m - 1);
+  }
+}
+
+template <typename TIn, int VPL>
+static hipError_t launch_append_wide_t(const void* tok, int B, const int64_t* pos, void* tail, int R, int m,
+                                       const float* gate, const float* bias, const csa_store& out,
+                                       const csa_store& win, int W, const NormRope& nr, hipStream_t st) {
+  if (B == 0) return hipSuccess;
+  const StoreW w = win.rows ? wview(win) : StoreW{nullptr, nullptr, 0, out.dim, 0, out.fmt, 0};
+  hipLaunchKernelGGL((decode_append_wide_kernel<TIn, VPL>), dim3((unsigned)B), dim3(kWave * kWideWaves), 0, st,
+                     (const TIn*)tok, B, pos, (TIn*)tail, R, m, gate, bias, wview(out), w, W, nr);
+  return hipGetLastError();
+}
+
 template <typename TIn, int VPL>
 static hipError_t launch_append_t(const void* tok, int B, const int64_t* pos, void* tail, int R, int m,
                                   const float* gate, const float* bias, const csa_store& out, const csa_store& win,
@@ -392,7 +520,9 @@ hipError_t launch_decode_append(const void* tok, int tok_fmt, int B, const int64
                                 const float* gate, const float* bias, const csa_store& out, const csa_store& win,
                                 int W, const NormRope& nr, hipStream_t st) {
   const int vpl = out.dim >= 64 ? out.dim / 64 : 1;
-#define CSA_APP(TT, V) return launch_append_t<TT, V>(tok, B, pos, tail, R, m, gate, bias, out, win, W, nr, st)
+#define CSA_APP(TT, V)                                                                          \
+  return m >= kWideMinM ? launch_append_wide_t<TT, V>(tok, B, pos, tail, R, m, gate, bias, out, win, W, nr, st) \
+                        : launch_append_t<TT, V>(tok, B, pos, tail, R, m, gate, bias, out, win, W, nr, st)
   if (tok_fmt == CSA_F32) {
     switch (vpl) { case 1: CSA_APP(float, 1); case 2: CSA_APP(float, 2); case 4: CSA_APP(float, 4); default: CSA_APP(float, 8); }
   } else {
