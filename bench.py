@@ -443,7 +443,7 @@ def cpu_baseline(T=131072, n_sample=512, budget_s=15.0):
     t_rows = time.perf_counter() - t0
     busy = (time.process_time() - cpu0) / (time.perf_counter() - wall0)   # threads kept busy on average
     total = t_compress + t_rows * T / done
-    return {"value": T / total, "unit": "tokens/s", "cores": int(min(pool, allowed)), "kind": "oracle",
+    return {"value": T / total, "unit": "tokens/s", "cores": max(1, math.ceil(busy)), "kind": "oracle",
             "cpu_model": model, "threads_busy_avg": round(busy, 2), "blas_threads": int(pool),
             "cpus_allowed": allowed,
             "sample": f"{done} of {T} query rows (stride sample) of the 128K CSA+HCA prefill, all tokens "

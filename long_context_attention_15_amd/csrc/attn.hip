@@ -359,7 +359,7 @@ static int attn_nsplit_for(int B, int Tq, int H, int hpw, int64_t max_list, int 
 
 // The MFMA kernel runs one workgroup per CU (its LDS tiles take most of the
 // 160 KB), so decode splits aim at one round of workgroups over the 256 CUs.
-constexpr int kMfmaTargetWgs = 256;
+constexpr int kMfmaTargetWgs = 512;
 constexpr int kMfmaMinSplit = 256;
 
 static int attn_nsplit(int B, int Tq, int H, int D, int64_t max_list, bool mfma, int& split_len) {
