@@ -546,6 +546,7 @@ def main():
             log(f"{name}: building caches")
             d = Decode1M(csa, hybrid)
             torch.cuda.synchronize()
+            csa.diag_counters(reset=True)
             ms, per = time_ops(d.ops(), args.decode_steps, 2, flush=d.flush)
             ms_g = time_graph(d.ops(), args.decode_steps, flush=d.flush)
             ab = d.algorithmic_bytes()
@@ -577,6 +578,13 @@ def main():
             # the attention with batch-invariant results (no split lists)
             _, per_inv = time_ops(d.invariant_ops(), args.decode_steps, 2, flush=d.flush)
             dec[name]["batch_invariant_attn_us"] = {n: v * 1e3 for n, v in per_inv.items()}
+            # indexer workgroups that stopped waiting for their query's threshold
+            # (exact either way, only slower) and final selects past their LDS budget
+            diag = csa.diag_counters(reset=True)
+            dec[name]["indexer_giveups"] = int(diag[csa.DIAG_INDEXER_GIVEUPS])
+            dec[name]["indexer_wide_selects"] = int(diag[csa.DIAG_INDEXER_WIDE_SELECT])
+            if diag[csa.DIAG_INDEXER_GIVEUPS]:
+                log(f"{name}: {diag[csa.DIAG_INDEXER_GIVEUPS]} indexer workgroups gave up waiting")
             del d
             torch.cuda.empty_cache()
         result["decode"] = dec
