@@ -353,11 +353,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_m32_kernel(Args a) {
     }
     table2(2 * wave, (&Tsel[0][0])[2 * wave * kT + lane]);
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    // the first kLead tiles' rows go out even past a short list's end (the
-    // zero row), so this wait has one form; in the tile loop row loads go out
-    // for the list's tiles only, and each wait counts the row loads issued
-    // after the tile it waits for (loads complete in order; the sel-entry
-    // loads in between only make a wait stricter)
+    // row loads go out for every tile, past the list's end too (the tables
+    // of slots beyond it hold the zero row), so each wait has one form: it
+    // counts the row loads issued after the tile it waits for (loads
+    // complete in order; the sel-entry loads in between only make a wait
+    // stricter)
 #pragma unroll
     for (int pt = 0; pt < kLead; ++pt) {
       const uint8_t* src = dma_src(pt);
@@ -389,15 +389,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_m32_kernel(Args a) {
       // hq), four independent accumulator chains; each starts at the slot
       // bias, so empty slots drop out of the softmax.
       f32x4 sblk[2][2];
-      bool filled = false;                       // some slot of the tile holds an entry
+      float bmax = kEmpty;                       // 0 if some slot of the tile holds an entry
 #pragma unroll
       for (int eh = 0; eh < 2; ++eh) {
         const float4 bv = *(const float4*)(Tbias[ts] + 16 * eh + 4 * g);
         sblk[eh][0] = f32x4{bv.x, bv.y, bv.z, bv.w};
         sblk[eh][1] = sblk[eh][0];
-        filled = filled || bv.x == 0.0f || bv.y == 0.0f || bv.z == 0.0f || bv.w == 0.0f;
+        bmax = fmaxf(bmax, fmaxf(fmaxf(bv.x, bv.y), fmaxf(bv.z, bv.w)));
       }
-      const bool tile_filled = __ballot(filled) != 0ull;
+      const bool tile_filled = __ballot(bmax == 0.0f) != 0ull;
       const float ksc[2] = {Tscl[ts][i16], Tscl[ts][16 + i16]};
       // K operand reads in order r = 2 ks + eh: FP8 (8 bytes) for ks < 14,
       // BF16 (16 bytes) for the RoPE steps
@@ -417,19 +417,40 @@ __global__ __launch_bounds__(kThreads, 1) void attn_m32_kernel(Args a) {
         const int ks = r >> 1, eh = r & 1;
         kop[r & 1] = ks < 14 ? cvt8(kf[r], ksc[eh]) : kb[r - 28];
       };
+      // the same conversion in two parts (the first word, then the other
+      // three), placed around the first product of a step
+      auto kconv_a = [&](int r) {
+        const int ks = r >> 1, eh = r & 1;
+        if (ks < 14) kop[r & 1].x = __builtin_bit_cast(unsigned int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kf[r].x, ksc[eh], false));
+        else kop[r & 1] = kb[r - 28];
+      };
+      auto kconv_b = [&](int r) {
+        const int ks = r >> 1, eh = r & 1;
+        if (ks < 14) {
+          kop[r & 1].y = __builtin_bit_cast(unsigned int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kf[r].x, ksc[eh], true));
+          kop[r & 1].z = __builtin_bit_cast(unsigned int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kf[r].y, ksc[eh], false));
+          kop[r & 1].w = __builtin_bit_cast(unsigned int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(kf[r].y, ksc[eh], true));
+        }
+      };
 #pragma unroll
       for (int r = 0; r < kSD; ++r) kread(r);
       kconv(0);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int r = 0; r < 32; ++r) {
-        if (r + kSD < 32) kread(r + kSD);
-        if (r + 1 < 32) kconv(r + 1);
+        // issue order: read, one conversion word, product, three words,
+        // product (eight issue slots in the two products' 32 cycles)
         const int ks = r >> 1, eh = r & 1;
-#pragma unroll
-        for (int hq = 0; hq < 2; ++hq)
-          sblk[eh][hq] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kop[r & 1]), qf[ks][hq],
-                                                               sblk[eh][hq], 0, 0, 0);
+        if (r + kSD < 32) kread(r + kSD);
+        if (r + 1 < 32) kconv_a(r + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        sblk[eh][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kop[r & 1]), qf[ks][0],
+                                                            sblk[eh][0], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (r + 1 < 32) kconv_b(r + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        sblk[eh][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kop[r & 1]), qf[ks][1],
+                                                            sblk[eh][1], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
 
@@ -522,21 +543,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_m32_kernel(Args a) {
         const int nf = 14 * c + (db < 14 ? db : 13) + kVD;      // FP8 read kVD blocks ahead
         if (db < 14 && nf < 28) vread(nf);
         if (f + 1 < 32) vconv(f + 1);
+        __builtin_amdgcn_sched_barrier(0);       // the next operand's conversion before this product
         acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vop[f & 1]), db < 14 ? ps[c] : pr[c],
                                                           acc[db], 0, 0, 0);
-        if (f % 3 == 1 && f / 3 < kLoadsW && it + kLead < ntiles)       // 9 row loads, every third product
+        if (f % 3 == 1 && f / 3 < kLoadsW)       // 9 row loads, every third product (no branch)
           dma_rows(dsrc, it + kLead, f / 3);
         __builtin_amdgcn_sched_barrier(0);
       }
       // rows of tile it+1 are in before the barrier: after its loads every
-      // wave issued those of tiles it+2 and it+3 that exist (and the table
-      // loads, which only make the wait stricter)
-      if (it + 3 < ntiles) M32_WAIT_VMCNT(2 * kLoadsW);
-      else if (it + 2 < ntiles) M32_WAIT_VMCNT(kLoadsW);
-      else {
-        asm volatile("; last tiles of the list" ::: "memory");
-        M32_WAIT_VMCNT(0);
-      }
+      // wave issued those of tiles it+2 and it+3 (and the table loads, which
+      // only make the wait stricter)
+      M32_WAIT_VMCNT(2 * kLoadsW);
       asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     }
     // every LDS DMA of this pass has landed before anything reuses LDS

@@ -6,8 +6,9 @@ spill inside the tile loop brings a scratch reload and a full vmcnt(0) wait
 into every tile, which drains that pipeline (a 40 % slowdown when it last
 happened, with identical results), so it is checked here rather than by the
 timing.  The tile loop of the recompute pass (run only after a logit
-overflowed the running reference) may reload one spilled value; the
-kernel's own full wait for the list's last tiles is marked in its text.""" 
+overflowed the running reference) may reload one spilled value.  Row loads
+go out for every tile (past the list's end they read the zero row), so the
+loop's only own wait keeps two tiles of row loads (18) in flight.""" 
 import os
 import re
 import shutil
@@ -69,21 +70,9 @@ def test_attention_tile_loops_have_no_spills_or_full_waits(tmp_path):
             scratch = [x.strip() for x in body if "scratch_" in x]
             limit = 0 if n == 0 else 1
             assert len(scratch) <= limit, f"{kern} {name}: scratch accesses in the tile loop: {scratch[:4]}"
-            # the loop's own waits: two tiles of row loads (18) in flight, one
-            # tile (9) near the end, none (marked) for the last tiles; any
-            # other count is the compiler waiting on something it loaded and
-            # would also wait for the row loads in flight
-            stray, n9, n0 = [], 0, 0
-            for i, x in enumerate(body):
-                m = re.search(r"s_waitcnt\s+vmcnt\((\d+)\)", x)
-                if not m:
-                    continue
-                c = int(m.group(1))
-                if c == 0 and any("last tiles of the list" in y for y in body[max(0, i - 4): i]):
-                    n0 += 1
-                elif c == 9:
-                    n9 += 1
-                elif c < 18:
-                    stray.append(x.strip())
-            assert len(stray) <= limit and n9 <= 1 and n0 <= 1, \
-                f"{kern} {name}: waits on the row loads in flight: {stray[:6]} (vmcnt(9) x{n9}, marked x{n0})"
+            # the loop's own wait keeps two tiles of row loads (18) in flight;
+            # a smaller count is the compiler waiting on something it loaded,
+            # which also waits for the row loads in flight
+            stray = [x.strip() for x in body
+                     if (m := re.search(r"s_waitcnt\s+vmcnt\((\d+)\)", x)) and int(m.group(1)) < 18]
+            assert len(stray) <= limit, f"{kern} {name}: waits on the row loads in flight: {stray[:6]}"
