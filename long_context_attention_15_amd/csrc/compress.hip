@@ -401,6 +401,10 @@ __global__ __launch_bounds__(kWave * kWideWaves) void decode_append_wide_kernel(
     const float* __restrict__ gate, const float* __restrict__ bias, StoreW out, StoreW win, int W, NormRope nr) {
   __shared__ float s_alpha[kMaxM];
   __shared__ float s_acc[512];
+  // BF16 blocks of up to 128 rows x 512 dims stay in LDS between the logits
+  // and the weighted sum (one round trip to memory instead of three)
+  constexpr int kLdsRows = 128, kLdsDim = 512;
+  __shared__ __attribute__((aligned(16))) uint16_t s_rows[sizeof(TIn) == 2 ? kLdsRows * kLdsDim : 8];
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int b = blockIdx.x;
   const int64_t p = pos[b];
@@ -439,6 +443,7 @@ __global__ __launch_bounds__(kWave * kWideWaves) void decode_append_wide_kernel(
 #pragma unroll
   for (int v = 0; v < VPL; ++v) g[v] = active ? gate[lane * VPL + v] : 0.0f;
   const int lo = active ? lane * VPL : 0;
+  const bool in_lds = sizeof(TIn) == 2 && m <= kLdsRows && D <= kLdsDim;   // uniform
   for (int i0 = wave * kWideRows; i0 < m; i0 += kWideWaves * kWideRows) {
     float xr[kWideRows][VPL];
 #pragma unroll
@@ -446,6 +451,16 @@ __global__ __launch_bounds__(kWave * kWideWaves) void decode_append_wide_kernel(
 #pragma unroll
     for (int u = 0; u < kWideRows; ++u) {
       if (i0 + u >= m) break;                    // uniform
+      if (in_lds && active) {                    // the row's BF16 values (exact: they were BF16)
+        uint32_t w[(VPL + 1) / 2];
+#pragma unroll
+        for (int v = 0; v < VPL; v += 2)
+          w[v / 2] = (__float_as_uint(xr[u][v]) >> 16) | (VPL > 1 ? (__float_as_uint(xr[u][v + 1 < VPL ? v + 1 : v]) & 0xffff0000u) : 0u);
+        if constexpr (VPL == 8) *(uint4*)(s_rows + (i0 + u) * kLdsDim + lo) = make_uint4(w[0], w[1], w[2], w[3]);
+        else
+#pragma unroll
+          for (int v = 0; v < VPL; ++v) s_rows[(i0 + u) * kLdsDim + lo + v] = (uint16_t)(__float_as_uint(xr[u][v]) >> 16);
+      }
       float pr = 0.0f;
       if (active) {
 #pragma unroll
@@ -471,6 +486,13 @@ __global__ __launch_bounds__(kWave * kWideWaves) void decode_append_wide_kernel(
   }
   __syncthreads();
   // weighted sum: thread t owns dim t, the terms in block order
+  if (in_lds) {
+    for (int d = threadIdx.x; d < D; d += kWave * kWideWaves) {
+      float acc = s_alpha[0] * bf16_to_f32(s_rows[d]);
+      for (int i = 1; i < m; ++i) acc = fmaf(s_alpha[i], bf16_to_f32(s_rows[i * kLdsDim + d]), acc);
+      s_acc[d] = acc;
+    }
+  } else
   for (int d = threadIdx.x; d < D; d += kWave * kWideWaves) {
     float acc = s_alpha[0] * ldf(row(0) + d);
     for (int i0 = 1; i0 < m; i0 += 64) {        // 64 rows' loads in flight
