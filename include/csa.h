@@ -25,6 +25,10 @@
  *     invalid call returns CSA_EINVAL / CSA_EUNSUPPORTED / CSA_EWORKSPACE and
  *     writes nothing; a failed launch returns CSA_EHIP.  csa_last_error()
  *     gives a message for the last failure on the calling thread.
+ *   - A call with no rows to process (B == 0, or T / Tq / n == 0 where the
+ *     entry point takes one) enqueues nothing and returns CSA_OK as soon as
+ *     its sizes are checked to be >= 0; no other argument is looked at, so
+ *     its pointers may be NULL.
  *   - Results are deterministic: fixed reduction orders, no float atomics.
  *   - Query, output and partial-result arrays of the attention entry points
  *     (q, out, part_out) must be 16-byte aligned; lse arrays 4-byte aligned.

@@ -1,5 +1,7 @@
 // C ABI of libcsa.so: host-side validation of every argument, then the
-// launch.  Nothing is enqueued unless all checks pass.
+// launch.  Nothing is enqueued unless all checks pass.  A call with no rows
+// to process returns CSA_OK once its sizes are known to be >= 0, before any
+// pointer is looked at (zero-element arrays often have NULL addresses).
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -164,6 +166,7 @@ csa_status csa_compress_kv(const void* tok, int tok_fmt, int B, int64_t T, int64
                            const csa_norm_rope* post, hipStream_t stream) {
   g_err[0] = 0;
   if (B < 0 || T < 0) return fail(CSA_EINVAL, "B and T must be >= 0");
+  if ((int64_t)B * T == 0) return CSA_OK;
   if (m < 1 || m > csa::compress_max_m()) return fail(CSA_EINVAL, "m = %d outside [1, %d]", m, csa::compress_max_m());
   if (!tok || !gate || !bias) return fail(CSA_EINVAL, "tok, gate and bias must be non-NULL");
   if (tok_fmt != CSA_F32 && tok_fmt != CSA_BF16) return fail(CSA_EUNSUPPORTED, "tok_fmt must be CSA_F32 or CSA_BF16");
@@ -188,6 +191,7 @@ csa_status csa_decode_append(const void* tok, int tok_fmt, int B, const int64_t*
                              const csa_norm_rope* post, hipStream_t stream) {
   g_err[0] = 0;
   if (B < 0) return fail(CSA_EINVAL, "B must be >= 0");
+  if (B == 0) return CSA_OK;
   if (m < 1 || m > csa::compress_max_m()) return fail(CSA_EINVAL, "m = %d outside [1, %d]", m, csa::compress_max_m());
   if (!tok || !pos || !tail || !gate || !bias) return fail(CSA_EINVAL, "tok, pos, tail, gate and bias must be non-NULL");
   if (tok_fmt != CSA_F32 && tok_fmt != CSA_BF16) return fail(CSA_EUNSUPPORTED, "tok_fmt must be CSA_F32 or CSA_BF16");
@@ -216,6 +220,7 @@ csa_status csa_decode_rebuild(const void* tok, int tok_fmt, int B, int n, int64_
                               csa_store win, int W, const csa_norm_rope* post, hipStream_t stream) {
   g_err[0] = 0;
   if (B < 0 || n < 0) return fail(CSA_EINVAL, "B and n must be >= 0");
+  if ((int64_t)B * n == 0) return CSA_OK;
   if (m < 1 || m > csa::compress_max_m()) return fail(CSA_EINVAL, "m = %d outside [1, %d]", m, csa::compress_max_m());
   if (!tok || !p0 || !tail || !gate || !bias) return fail(CSA_EINVAL, "tok, p0, tail, gate and bias must be non-NULL");
   if (tok_fmt != CSA_F32 && tok_fmt != CSA_BF16) return fail(CSA_EUNSUPPORTED, "tok_fmt must be CSA_F32 or CSA_BF16");
@@ -253,6 +258,7 @@ csa_status csa_indexer_topk(csa_store q_idx, const float* head_w, csa_store keys
                             void* ws, size_t ws_bytes, hipStream_t stream) {
   g_err[0] = 0;
   if (B < 0 || Tq < 0) return fail(CSA_EINVAL, "B and Tq must be >= 0");
+  if ((int64_t)B * Tq == 0) return CSA_OK;
   if (H_I < 1 || H_I > 16) return fail(CSA_EUNSUPPORTED, "H_I = %d outside [1, 16]", H_I);
   if (k < 1 || k > 2048) return fail(CSA_EUNSUPPORTED, "k = %d outside [1, 2048]", k);
   if (m < 1) return fail(CSA_EINVAL, "m < 1");
@@ -318,6 +324,7 @@ csa_status csa_sparse_attn_prefill(const void* q, int q_fmt, int B, int T, int H
                                    const csa_norm_rope* q_post, hipStream_t stream) {
   g_err[0] = 0;
   if (B < 0 || T < 0) return fail(CSA_EINVAL, "B and T must be >= 0");
+  if ((int64_t)B * T == 0) return CSA_OK;
   CSA_TRY(check_store(ckv, "ckv"));
   CSA_TRY(check_store(win, "win"));
   CSA_TRY(check_kv_pair(ckv, "ckv", win, "win"));
@@ -339,6 +346,7 @@ csa_status csa_sparse_attn_decode(const void* q, int q_fmt, int B, int H, csa_st
                                   void* ws, size_t ws_bytes, const csa_norm_rope* q_post, hipStream_t stream) {
   g_err[0] = 0;
   if (B < 0) return fail(CSA_EINVAL, "B must be >= 0");
+  if (B == 0) return CSA_OK;
   CSA_TRY(check_store(ckv, "ckv"));
   CSA_TRY(check_store(ring, "ring"));
   CSA_TRY(check_kv_pair(ckv, "ckv", ring, "ring"));
@@ -358,7 +366,9 @@ csa_status csa_sparse_attn_decode_noalloc(const void* q, int q_fmt, int B, int H
                                           const float* sink, float sm_scale, void* out, float* lse, int flags,
                                           const csa_norm_rope* q_post, hipStream_t stream) {
   g_err[0] = 0;
-  if (B < 0 || H < 1 || k < 1) return fail(CSA_EINVAL, "B >= 0, H >= 1 and k >= 1 needed");
+  if (B < 0) return fail(CSA_EINVAL, "B must be >= 0");
+  if (B == 0) return CSA_OK;
+  if (H < 1 || k < 1) return fail(CSA_EINVAL, "H >= 1 and k >= 1 needed");
   const int64_t max_list = (int64_t)k + ((flags & CSA_ATTN_PARTIAL) ? 0 : (W > 0 ? W : 0));
   const size_t need = csa::attn_workspace(B, 1, H, ckv.dim, max_list);
   if (need > kScratchBytes)
@@ -376,6 +386,7 @@ csa_status hca_attn(const void* q, int q_fmt, int B, int Tq, int H, csa_store hk
                     const csa_norm_rope* q_post, hipStream_t stream) {
   g_err[0] = 0;
   if (B < 0 || Tq < 0) return fail(CSA_EINVAL, "B and Tq must be >= 0");
+  if ((int64_t)B * Tq == 0) return CSA_OK;
   if (m_prime < 1) return fail(CSA_EINVAL, "m_prime < 1");
   CSA_TRY(check_store(hkv, "hkv"));
   CSA_TRY(check_store(win, "win"));
@@ -399,6 +410,7 @@ csa_status swa_merge(const void* q, int q_fmt, int B, int Tq, int H, csa_store w
                      void* out, const csa_norm_rope* q_post, hipStream_t stream) {
   g_err[0] = 0;
   if (B < 0 || Tq < 0) return fail(CSA_EINVAL, "B and Tq must be >= 0");
+  if ((int64_t)B * Tq == 0) return CSA_OK;
   if (flags & CSA_ATTN_PARTIAL) return fail(CSA_EINVAL, "swa_merge takes no CSA_ATTN_PARTIAL flag");
   CSA_TRY(check_store(win, "win"));
   if (win.fmt == CSA_MXFP4) return fail(CSA_EUNSUPPORTED, "window rows must be F32 or FP8");

@@ -50,6 +50,43 @@ def test_noalloc_decode_rejects_sizes_beyond_its_scratch(lib):
     assert st == 1 and "scratch" in lib.csa_last_error().decode()
 
 
+def test_empty_calls_need_no_pointers(lib):
+    """A call with no rows to process returns CSA_OK once its sizes are
+    known to be >= 0, before any pointer or store is looked at, so the NULL
+    addresses of zero-element arrays pass; a negative size is still an error."""
+    z = csa._CStore(None, None, 0, 0, 0, 0, 0)
+    assert lib.csa_compress_kv(None, csa.F32, 0, 100, 0, 4, None, None, z, 0, None, None) == 0
+    assert lib.csa_compress_kv(None, csa.F32, 3, 0, 0, 4, None, None, z, 0, None, None) == 0
+    assert lib.csa_compress_kv(None, csa.F32, -1, 100, 0, 4, None, None, z, 0, None, None) == 1
+    assert lib.csa_decode_append(None, csa.F32, 0, None, None, 0, 4, None, None, z, z, 0, None, None) == 0
+    assert lib.csa_decode_append(None, csa.F32, -1, None, None, 0, 4, None, None, z, z, 0, None, None) == 1
+    assert lib.csa_decode_rebuild(None, csa.F32, 0, 8, 0, None, None, None, 0, 4, None, None, z, z, 0, None, None) == 0
+    assert lib.csa_decode_rebuild(None, csa.F32, 2, 0, 0, None, None, None, 0, 4, None, None, z, z, 0, None, None) == 0
+    assert lib.csa_decode_rebuild(None, csa.F32, 2, -1, 0, None, None, None, 0, 4, None, None, z, z, 0, None,
+                                  None) == 1
+    assert lib.csa_indexer_topk(z, None, z, 0, None, 0, 1, 8, 4, 64, None, None, 0, None) == 0
+    assert lib.csa_indexer_topk(z, None, z, 0, None, 2, 0, 8, 4, 64, None, None, 0, None) == 0
+    assert lib.csa_indexer_topk(z, None, z, 0, None, 2, -1, 8, 4, 64, None, None, 0, None) == 1
+    assert lib.csa_sparse_attn_prefill(None, csa.BF16, 1, 0, 64, z, 0, None, 64, z, 128, None, 0.04, None, None, 0,
+                                       None, None) == 0
+    assert lib.csa_sparse_attn_prefill(None, csa.BF16, 0, 9, 64, z, 0, None, 64, z, 128, None, 0.04, None, None, 0,
+                                       None, None) == 0
+    assert lib.csa_sparse_attn_prefill(None, csa.BF16, 1, -1, 64, z, 0, None, 64, z, 128, None, 0.04, None, None, 0,
+                                       None, None) == 1
+    assert lib.csa_sparse_attn_decode(None, csa.BF16, 0, 64, z, 0, None, 64, z, None, 128, None, 0.04, None, None, 0,
+                                      None, 0, None, None) == 0
+    assert lib.csa_sparse_attn_decode_noalloc(None, csa.BF16, 0, 64, z, 0, None, 64, z, None, 128, None, 0.04, None,
+                                              None, 0, None, None) == 0
+    assert lib.csa_sparse_attn_decode_noalloc(None, csa.BF16, -1, 64, z, 0, None, 64, z, None, 128, None, 0.04, None,
+                                              None, 0, None, None) == 1
+    assert lib.hca_attn(None, csa.BF16, 0, 8, 64, z, 128, 0, None, z, 128, None, 0.04, None, None, 0, None, 0, None,
+                        None) == 0
+    assert lib.hca_attn(None, csa.BF16, 2, 0, 64, z, 128, 0, None, z, 128, None, 0.04, None, None, 0, None, 0, None,
+                        None) == 0
+    assert lib.swa_merge(None, csa.BF16, 2, 0, 64, z, None, 128, 0, None, None, None, 0.04, None, None, None) == 0
+    assert lib.swa_merge(None, csa.BF16, -2, 0, 64, z, None, 128, 0, None, None, None, 0.04, None, None, None) == 1
+
+
 def test_diag_counters_reject_a_null_array(lib):
     assert lib.csa_diag_counters(None, 2, 0) == 1
 

@@ -170,6 +170,49 @@ def test_compress_short_input_writes_nothing(lib):
     assert bool((out.rows == 0xAB).all())
 
 
+def test_empty_calls_write_nothing(lib):
+    """Calls with no rows to process (B == 0, or zero tokens or queries)
+    return without error through every entry point and leave the buffers
+    around them untouched; zero-element tensors may carry NULL addresses."""
+    import torch
+    dev = Hx.dev()
+    H, D, R, m = 64, 512, 64, 4
+    kv = lib.alloc_store(1, 8, D, "fp8", R, device=dev)
+    win = lib.alloc_store(1, 128, D, "fp8", R, device=dev)
+    for st in (kv, win):
+        st.rows.fill_(0xAB)
+        st.scales.fill_(3.0)
+    out = torch.full((2, 4, H, D), 7.0, dtype=torch.bfloat16, device=dev)
+    lse = torch.full((2, 4, H), 5.0, dtype=torch.float32, device=dev)
+    sink = Hx.to_dev(np.zeros(H, np.float32))
+    gate = Hx.to_dev(np.zeros(D, np.float32))
+    bias = Hx.to_dev(np.zeros(m, np.float32))
+    bf = dict(dtype=torch.bfloat16, device=dev)
+    q0 = torch.empty((1, 0, H, D), **bf)
+    lib.sparse_attn_prefill(q0, kv, 8, torch.empty((1, 0, 64), dtype=torch.int32, device=dev), 64, win, 128, sink,
+                            0.04, out, lse)
+    lib.hca_attn(q0, kv, 128, 8, None, win, 128, sink, 0.04, out, lse)
+    lib.swa_merge(q0, win, None, 128, 0, torch.empty((1, 0, H, D), dtype=torch.float32, device=dev),
+                  torch.empty((1, 0, H), dtype=torch.float32, device=dev), sink, 0.04, out)
+    qd0 = torch.empty((0, H, D), **bf)
+    sel0 = torch.empty((0, 1, 64), dtype=torch.int32, device=dev)
+    pos0 = torch.empty(0, dtype=torch.int64, device=dev)
+    lib.sparse_attn_decode(qd0, kv, 8, sel0, 64, win, pos0, 128, sink, 0.04, out, lse)
+    lib.sparse_attn_decode_noalloc(qd0, kv, 8, sel0, 64, win, pos0, 128, sink, 0.04, out, lse)
+    lib.compress_kv(torch.empty((1, 0, D), **bf), m, gate, bias, kv)
+    lib.decode_append(torch.empty((0, D), **bf), pos0, torch.empty((0, m, D), **bf), m, gate, bias, kv, win, 128)
+    p0 = torch.zeros(1, dtype=torch.int64, device=dev)
+    lib.decode_rebuild(torch.empty((1, 0, D), **bf), p0, torch.zeros((1, m, D), **bf), m, gate, bias, kv, win, 128)
+    iq = lib.alloc_store(1, 8, 64, "fp8", 0, device=dev)
+    ik = lib.alloc_store(1, 8, 64, "fp8", 0, device=dev)
+    isel = torch.full((1, 1, 64), -7, dtype=torch.int32, device=dev)
+    lib.indexer_topk(iq, Hx.to_dev(np.ones(8, np.float32)), ik, 8, None, 1, 0, 8, m, 64, isel)
+    _sync()
+    assert bool((out == 7.0).all()) and bool((lse == 5.0).all()) and bool((isel == -7).all())
+    for st in (kv, win):
+        assert bool((st.rows == 0xAB).all()) and bool((st.scales == 3.0).all())
+
+
 # ================================================================== indexer
 def _indexer_inputs(B, Tq, N, H_I, d_I, fmt, seed_shift=0, positions=None):
     keys = synth.tensor(0, "idx_k", (B, N, d_I), rmsnorm=True, layer=seed_shift)
@@ -396,7 +439,8 @@ def _attn_inputs(B, Tq, H, D, R, fmt, qf, n_kv, n_win, layer=0):
 @pytest.mark.parametrize("fmt,qf,H,D,R,T,m,k,W", [("f32", "f32", 4, 64, 0, 2048, 4, 64, 128),
                                                   ("fp8", "bf16", 64, 512, 64, 700, 4, 64, 128),
                                                   ("fp8", "bf16", 32, 512, 64, 300, 4, 96, 40),
-                                                  ("fp8", "f32", 4, 64, 16, 500, 4, 32, 128)])
+                                                  ("fp8", "f32", 4, 64, 16, 500, 4, 32, 128),
+                                                  ("fp8", "bf16", 64, 512, 64, 333, 4, 128, 0)])
 def test_csa_prefill_parity(lib, fmt, qf, H, D, R, T, m, k, W):
     import torch
     N = T // m
