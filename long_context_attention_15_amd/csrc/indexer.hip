@@ -932,7 +932,7 @@ struct KeyRegs {
 };
 
 template <int CAP>
-__global__ __launch_bounds__(kWave) void idx_stream_kernel(StreamArgs a) {
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void idx_stream_kernel(StreamArgs a) {
   constexpr int NS = (CAP + kWave - 1) / kWave;   // list slots per lane when a list is in registers
   constexpr int kSRowCap = CAP + kWave;
   __shared__ StreamLds<CAP> S;
