@@ -31,6 +31,8 @@ COMPRESS_CASES = [
     ("bf16_to_mxfp4_D64_m4", "bf16", "mxfp4", 64, 0, 4, 2050, 2),
     ("f32_to_mxfp4_D32_m4", "f32", "mxfp4", 32, 0, 4, 1027, 1),
     ("f32_to_f32_D32_m7", "f32", "f32", 32, 0, 7, 500, 1),
+    ("bf16_to_fp8_D512_m1024", "bf16", "fp8", 512, 64, 1024, 1024 * 3 + 7, 1),     # the largest block length
+    ("f32_to_f32_D64_m1024", "f32", "f32", 64, 0, 1024, 2 * 1024 + 1, 2),
 ]
 
 
@@ -62,6 +64,11 @@ APPEND_CASES = [
     ("csa_idx_bf16_mxfp4_D64_m4_tail8", "bf16", "mxfp4", 64, 0, 4, 8, 0, 150),
     ("hca_kv_bf16_fp8_D512_m128", "bf16", "fp8", 512, 64, 128, 128, 0, 150),
     ("f32_f32_D32_m3_tail6_window16", "f32", "f32", 32, 0, 3, 6, 16, 60),
+    # long blocks whose rows do not stay in LDS (float32 tokens, or more than
+    # 128 rows): the close reads them from the tail again for the weighted sum
+    ("f32_f32_D64_m256", "f32", "f32", 64, 0, 256, 256, 0, 600),
+    ("bf16_fp8_D512_m256", "bf16", "fp8", 512, 64, 256, 256, 0, 300),
+    ("f32_f32_D32_m1024", "f32", "f32", 32, 0, 1024, 1024, 0, 1100),
 ]
 
 
@@ -272,6 +279,26 @@ def test_indexer_decode_parity(lib, fmt, B, N, k):
     assert flips <= 2
 
 
+@pytest.mark.parametrize("fmt,d_I,Tq,N", [("fp8", 64, 1, 30000), ("mxfp4", 32, 1, 30000), ("fp8", 32, 12000, 3000)])
+def test_indexer_largest_k_and_head_count(lib, fmt, d_I, Tq, N):
+    """k = 2048 and H_I = 16, the largest the entry point takes, on the decode
+    path (one query per sequence over several chunks) and on the prefill path
+    (queries past position 4k see more than k entries)."""
+    H_I, m, k = 16, 4, 2048
+    if Tq == 1:
+        B = 2
+        kst, kdeq, qst, qdeq, w = _indexer_inputs(B, 1, N, H_I, d_I, fmt, seed_shift=2)
+        pos = [[m * N + 3 - 7 * b] for b in range(B)]
+        sel = _run_indexer(lib, kst, qst, w, N, pos, B, 1, H_I, m, k)
+        assert _check_indexer(sel, kdeq, qdeq, w, N, m, k, pos) <= 2
+        return
+    kst, kdeq, qst, qdeq, w = _indexer_inputs(1, Tq, N, H_I, d_I, fmt, seed_shift=2)
+    sel = _run_indexer(lib, kst, qst, w, N, None, 1, Tq, H_I, m, k)
+    rows = sorted(set(list(range(0, Tq, 97)) + [0, m - 1, k * m - 1, k * m, Tq - 1]))
+    flips = _check_indexer(sel[:, rows], kdeq, qdeq[:, rows], w[:, rows], N, m, k, [rows])
+    assert flips <= max(2, len(rows) * k // 2000)
+
+
 def test_indexer_exact_ties_go_to_the_smaller_index(lib):
     """Integer-valued queries/keys with w = 1: every score is exact on both
     sides, with many exact ties (and exact zeros from the ReLU), so the
@@ -440,7 +467,9 @@ def _attn_inputs(B, Tq, H, D, R, fmt, qf, n_kv, n_win, layer=0):
                                                   ("fp8", "bf16", 64, 512, 64, 700, 4, 64, 128),
                                                   ("fp8", "bf16", 32, 512, 64, 300, 4, 96, 40),
                                                   ("fp8", "f32", 4, 64, 16, 500, 4, 32, 128),
-                                                  ("fp8", "bf16", 64, 512, 64, 333, 4, 128, 0)])
+                                                  ("fp8", "bf16", 64, 512, 64, 333, 4, 128, 0),
+                                                  ("fp8", "bf16", 64, 512, 64, 900, 4, 64, 700),
+                                                  ("fp8", "bf16", 64, 512, 64, 300, 4, 32, 65536)])
 def test_csa_prefill_parity(lib, fmt, qf, H, D, R, T, m, k, W):
     import torch
     N = T // m
