@@ -725,6 +725,7 @@ constexpr int stream_max_k() { return CAP - kSSlack - 2 * kSStep; }
 constexpr int kStreamMaxK = stream_max_k<kSCapLarge>();
 constexpr int64_t kStreamMaxN = 65536;    // candidate indices are 16-bit
 constexpr int64_t kStreamMinQueries = 2048;
+constexpr int kSRowBytes = 64;            // FP8 keys of 64 dims (indexer_stream_ok)
 
 // list slots + one spare slot per lane
 template <int CAP>
@@ -772,7 +773,8 @@ __device__ __forceinline__ float thr_float(uint32_t thr) {
 }
 
 // A candidate list held in registers: lane l owns positions 64 j + l; key 0
-// marks an empty slot (every real key is nonzero).
+// marks an empty slot (every real key is nonzero).  The lists in LDS hold the
+// scores' float bits; their keys are formed here, on the way in.
 template <int NS>
 struct RegList {
   uint32_t key[NS];
@@ -785,7 +787,7 @@ __device__ __forceinline__ void list_load(const uint32_t* keys, const uint16_t* 
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
     const int pos = kWave * j + lane;
-    r.key[j] = pos < n ? keys[pos] : 0u;
+    r.key[j] = pos < n ? key_of(__uint_as_float(keys[pos])) : 0u;
     r.id[j] = pos < n ? (uint32_t)ids[pos] : 0u;
   }
 }
@@ -873,8 +875,8 @@ __device__ void list_cut(const RegList<NS>& r, int kk, int slack, uint32_t* hist
   need_eq = need;
 }
 
-// Rewrite the list with the entries of key > T plus the first need_eq of
-// key == T, in order; returns the new length.
+// Rewrite the list (as scores) with the entries of key > T plus the first
+// need_eq of key == T, in order; returns the new length.
 template <int NS>
 __device__ int list_store_kept(const RegList<NS>& r, uint32_t T, int need_eq, uint32_t* keys, uint16_t* ids) {
   const int lane = threadIdx.x % kWave;
@@ -889,7 +891,7 @@ __device__ int list_store_kept(const RegList<NS>& r, uint32_t T, int need_eq, ui
     const uint64_t bk = __ballot(keep);
     if (keep) {
       const int d = out + __popcll(bk & lt);
-      keys[d] = k;
+      keys[d] = __float_as_uint(key_score(k));
       ids[d] = (uint16_t)r.id[j];
     }
     out += __popcll(bk);
@@ -998,6 +1000,10 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
   float thrA = -INFINITY, thrB = -INFINITY;
   uint32_t* ck = &S.ckey[0][0];
   uint16_t* ci = &S.cidx[0][0];
+  uint32_t* const ckA = ck + qA * kSRowCap;          // this lane's two lists
+  uint32_t* const ckB = ck + qB * kSRowCap;
+  uint16_t* const ciA = ci + qA * kSRowCap;
+  uint16_t* const ciB = ci + qB * kSRowCap;
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 
   const int64_t krow0 = (int64_t)b * a.keys.cap;
@@ -1006,7 +1012,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       const int e = min(it * kSStep + 32 * blk + l32, ntw - 1);
-      const uint8_t* kp = a.keys.rows + (krow0 + e) * a.keys.row_bytes + 32 * g;
+      const uint8_t* kp = a.keys.rows + (krow0 + e) * kSRowBytes + 32 * g;
       kr.w[blk][0] = *(const uint4*)kp;
       kr.w[blk][1] = *(const uint4*)(kp + 16);
       kr.sc[blk] = ((const float*)a.keys.scales)[krow0 + e];
@@ -1043,19 +1049,26 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
     sB = (__uint_as_float(r23[0]) + __uint_as_float(r23[1])) * sk;
   };
   // append the passing entries of one 32-entry block (entry index e for this
-  // lane); a lane's slot is its list length plus the passing lanes below it
-  // in its half of the wave.  Branch-free: a lane that does not pass writes
-  // to its own spare slot behind the list.
-  auto append = [&](bool pA, bool pB, float sA, float sB, int e) {
-    const uint64_t mA = __ballot(pA), mB = __ballot(pB);
+  // lane), as the scores' bits; a lane's slot is its list length plus the
+  // passing lanes below it in its half of the wave.  Branch-free: a lane that
+  // does not pass writes to its own spare slot behind the list.
+  auto append = [&](float sA, float sB, int e) {
+    // each mask is formed from the compares' own masks (a ballot of their
+    // conjunction would first turn it into a lane value)
+    const bool inA = e < ntA, inB = e < ntB, gtA = sA > thrA, gtB = sB > thrB;
+    const bool pA = inA && gtA, pB = inB && gtB;
+    const uint64_t mA = __builtin_amdgcn_ballot_w64(inA) & __builtin_amdgcn_ballot_w64(gtA);
+    const uint64_t mB = __builtin_amdgcn_ballot_w64(inB) & __builtin_amdgcn_ballot_w64(gtB);
     const int a_lo = __popcll(mA & 0xffffffffull), a_hi = __popcll(mA >> 32);
     const int b_lo = __popcll(mB & 0xffffffffull), b_hi = __popcll(mB >> 32);
-    const int dA = pA ? lane_rank(mA, g ? cnt[1] - a_lo : cnt[0]) : CAP + lane;
-    const int dB = pB ? lane_rank(mB, g ? cnt[3] - b_lo : cnt[2]) : CAP + lane;
-    ck[qA * kSRowCap + dA] = key_of(sA);
-    ci[qA * kSRowCap + dA] = (uint16_t)e;
-    ck[qB * kSRowCap + dB] = key_of(sB);
-    ci[qB * kSRowCap + dB] = (uint16_t)e;
+    const int rA = lane_rank(mA, g ? cnt[1] - a_lo : cnt[0]);
+    const int rB = lane_rank(mB, g ? cnt[3] - b_lo : cnt[2]);
+    const int dA = pA ? rA : CAP + lane;
+    const int dB = pB ? rB : CAP + lane;
+    ckA[dA] = __float_as_uint(sA);
+    ciA[dA] = (uint16_t)e;
+    ckB[dB] = __float_as_uint(sB);
+    ciB[dB] = (uint16_t)e;
     cnt[0] += a_lo;
     cnt[1] += a_hi;
     cnt[2] += b_lo;
@@ -1081,8 +1094,8 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
     block_scores(acc0, kr.sc[0], sA0, sB0);
     block_scores(acc1, kr.sc[1], sA1, sB1);
     const int e = it * kSStep + l32;
-    append(e < ntA && sA0 > thrA, e < ntB && sB0 > thrB, sA0, sB0, e);
-    append(e + 32 < ntA && sA1 > thrA, e + 32 < ntB && sB1 > thrB, sA1, sB1, e + 32);
+    append(sA0, sB0, e);
+    append(sA1, sB1, e + 32);
   };
 
   // two register sets, each reloaded right after use: iteration it + 2 is in
@@ -1137,7 +1150,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
 }
 
 bool indexer_stream_ok(const csa_store& keys, int H_I, int B, int Tq, int64_t n_entries, int k) {
-  return keys.fmt == CSA_FP8_E4M3 && keys.dim == 64 && keys.row_bytes == 64 && H_I <= 8 && k <= kStreamMaxK &&
+  return keys.fmt == CSA_FP8_E4M3 && keys.dim == 64 && keys.row_bytes == kSRowBytes && H_I <= 8 && k <= kStreamMaxK &&
          n_entries <= kStreamMaxN && (int64_t)B * Tq >= kStreamMinQueries;
 }
 
