@@ -773,8 +773,7 @@ __device__ __forceinline__ float thr_float(uint32_t thr) {
 }
 
 // A candidate list held in registers: lane l owns positions 64 j + l; key 0
-// marks an empty slot (every real key is nonzero).  The lists in LDS hold the
-// scores' float bits; their keys are formed here, on the way in.
+// marks an empty slot (every real key is nonzero).
 template <int NS>
 struct RegList {
   uint32_t key[NS];
@@ -787,7 +786,7 @@ __device__ __forceinline__ void list_load(const uint32_t* keys, const uint16_t* 
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
     const int pos = kWave * j + lane;
-    r.key[j] = pos < n ? key_of(__uint_as_float(keys[pos])) : 0u;
+    r.key[j] = pos < n ? keys[pos] : 0u;
     r.id[j] = pos < n ? (uint32_t)ids[pos] : 0u;
   }
 }
@@ -875,8 +874,8 @@ __device__ void list_cut(const RegList<NS>& r, int kk, int slack, uint32_t* hist
   need_eq = need;
 }
 
-// Rewrite the list (as scores) with the entries of key > T plus the first
-// need_eq of key == T, in order; returns the new length.
+// Rewrite the list with the entries of key > T plus the first need_eq of
+// key == T, in order; returns the new length.
 template <int NS>
 __device__ int list_store_kept(const RegList<NS>& r, uint32_t T, int need_eq, uint32_t* keys, uint16_t* ids) {
   const int lane = threadIdx.x % kWave;
@@ -891,7 +890,7 @@ __device__ int list_store_kept(const RegList<NS>& r, uint32_t T, int need_eq, ui
     const uint64_t bk = __ballot(keep);
     if (keep) {
       const int d = out + __popcll(bk & lt);
-      keys[d] = __float_as_uint(key_score(k));
+      keys[d] = k;
       ids[d] = (uint16_t)r.id[j];
     }
     out += __popcll(bk);
@@ -1049,9 +1048,9 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
     sB = (__uint_as_float(r23[0]) + __uint_as_float(r23[1])) * sk;
   };
   // append the passing entries of one 32-entry block (entry index e for this
-  // lane), as the scores' bits; a lane's slot is its list length plus the
-  // passing lanes below it in its half of the wave.  Branch-free: a lane that
-  // does not pass writes to its own spare slot behind the list.
+  // lane); a lane's slot is its list length plus the passing lanes below it
+  // in its half of the wave.  Branch-free: a lane that does not pass writes
+  // to its own spare slot behind the list.
   auto append = [&](float sA, float sB, int e) {
     // each mask is formed from the compares' own masks (a ballot of their
     // conjunction would first turn it into a lane value)
@@ -1065,9 +1064,9 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
     const int rB = lane_rank(mB, g ? cnt[3] - b_lo : cnt[2]);
     const int dA = pA ? rA : CAP + lane;
     const int dB = pB ? rB : CAP + lane;
-    ckA[dA] = __float_as_uint(sA);
+    ckA[dA] = key_of(sA);
     ciA[dA] = (uint16_t)e;
-    ckB[dB] = __float_as_uint(sB);
+    ckB[dB] = key_of(sB);
     ciB[dB] = (uint16_t)e;
     cnt[0] += a_lo;
     cnt[1] += a_hi;
