@@ -959,11 +959,14 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
     ntw = max(ntw, ntq[qq]);
   }
 
-  // A operand: rows = (query r >> 3, head r & 7); K-step j covers dims
-  // [32 g + 8 j, +8) (the same split as the B operand below)
+  // A operand: row r holds query qsel(r >> 4, (r >> 2) & 1), head 4 ((r >> 3)
+  // & 1) + (r & 3), so that the accumulator rows of lane half g (rows 8 j +
+  // 4 g + i) are all 8 heads of query g (j < 2) and of query 2 + g (j >= 2);
+  // K-step j covers dims [32 g + 8 j, +8) (the same split as the B operand)
+  auto qsel = [](int hi, int half) { return hi ? 2 + half : half; };
   sbf16x8 qa[4];
   {
-    const int qq = l32 >> 3, h = l32 & 7, q = q0 + qq;
+    const int qq = qsel(l32 >> 4, (l32 >> 2) & 1), h = 4 * ((l32 >> 3) & 1) + (l32 & 3), q = q0 + qq;
     const bool ok = q < a.Tq && h < a.H_I;
     const uint8_t* qp = a.qidx.rows + ((int64_t)b * a.qidx.cap + (int64_t)(ok ? q : 0) * a.H_I + (ok ? h : 0)) *
                                           a.qidx.row_bytes + 32 * g;
@@ -974,21 +977,21 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
     qa[2] = __builtin_bit_cast(sbf16x8, fp8x8_to_bf16(v1.x, v1.y));
     qa[3] = __builtin_bit_cast(sbf16x8, fp8x8_to_bf16(v1.z, v1.w));
   }
-  // head weights of this lane's accumulator rows (query r >> 2, head 4 g + (r & 3)),
-  // with the query row scales folded in
+  // head weights of this lane's accumulator values 4 j + i (query qsel(j >> 1,
+  // g), head 4 (j & 1) + i), with the query row scales folded in
   float wl[kSQW][4];
 #pragma unroll
-  for (int qq = 0; qq < kSQW; ++qq)
+  for (int j = 0; j < kSQW; ++j)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int q = q0 + qq, h = 4 * g + i;
+      const int q = q0 + qsel(j >> 1, g), h = 4 * (j & 1) + i;
       float w = 0.0f;
       if (q < a.Tq && h < a.H_I) {
         const int64_t bq = (int64_t)b * a.Tq + q;
         w = a.head_w[bq * a.H_I + h] *
             ((const float*)a.qidx.scales)[(int64_t)b * a.qidx.cap + (int64_t)q * a.H_I + h];
       }
-      wl[qq][i] = w;
+      wl[j][i] = w;
     }
 
   // lanes < 32 score queries 0 and 2, lanes >= 32 queries 1 and 3
@@ -1032,20 +1035,19 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
     }
     return acc;
   };
-  // head-weighted ReLU sums: lanes < 32 get queries 0 and 2, lanes >= 32 queries 1 and 3
+  // head-weighted ReLU sums, all 8 heads in the lane: lanes < 32 get queries
+  // 0 and 2, lanes >= 32 queries 1 and 3
   auto block_scores = [&](const sf32x16& acc, float sk, float& sA, float& sB) {
-    float p[kSQW];
+    float va = 0.0f, vb = 0.0f;
 #pragma unroll
-    for (int qq = 0; qq < kSQW; ++qq) {
-      float v = 0.0f;
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v = fmaf(wl[qq][i], relu_bits(acc[4 * qq + i]), v);
-      p[qq] = v;
-    }
-    const auto r01 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[0]), __float_as_uint(p[1]), false, false);
-    const auto r23 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p[2]), __float_as_uint(p[3]), false, false);
-    sA = (__uint_as_float(r01[0]) + __uint_as_float(r01[1])) * sk;
-    sB = (__uint_as_float(r23[0]) + __uint_as_float(r23[1])) * sk;
+      for (int i = 0; i < 4; ++i) {
+        va = fmaf(wl[j][i], relu_bits(acc[4 * j + i]), va);
+        vb = fmaf(wl[2 + j][i], relu_bits(acc[4 * (2 + j) + i]), vb);
+      }
+    sA = va * sk;
+    sB = vb * sk;
   };
   // append the passing entries of one 32-entry block (entry index e for this
   // lane); a lane's slot is its list length plus the passing lanes below it
