@@ -787,7 +787,7 @@ __device__ __forceinline__ void list_load(const uint32_t* keys, const uint16_t* 
   for (int j = 0; j < NS; ++j) {
     const int pos = kWave * j + lane;
     r.key[j] = pos < n ? keys[pos] : 0u;
-    r.id[j] = pos < n ? (uint32_t)ids[pos] : 0u;
+    r.id[j] = (uint32_t)ids[pos];                 // read only where the key is nonzero
   }
 }
 
@@ -881,6 +881,22 @@ __device__ int list_store_kept(const RegList<NS>& r, uint32_t T, int need_eq, ui
   const int lane = threadIdx.x % kWave;
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int out = 0, eqs = 0;
+  if (need_eq == 0) {                                // uniform: the usual cut, at a digit boundary
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const uint32_t k = r.key[j];
+      const bool keep = k > T;                       // T >= 0, so a kept key is nonzero
+      const uint64_t bk = __builtin_amdgcn_ballot_w64(keep);
+      if (keep) {
+        const int d = lane_rank(bk, out);
+        keys[d] = k;
+        ids[d] = (uint16_t)r.id[j];
+      }
+      out += __popcll(bk);
+    }
+    lds_wave_sync();
+    return __builtin_amdgcn_readfirstlane(out);
+  }
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
     const uint32_t k = r.key[j];
