@@ -793,14 +793,15 @@ __device__ __forceinline__ void list_load(const uint32_t* keys, const uint16_t* 
 
 template <int NS>
 __device__ __forceinline__ void list_minmax(const RegList<NS>& r, uint32_t& kmin, uint32_t& kmax) {
+  // the minimum over k - 1 skips empty slots (0 wraps to the largest value)
   uint32_t lo = 0xffffffffu, hi = 0u;
 #pragma unroll
   for (int j = 0; j < NS; ++j) {
     const uint32_t k = r.key[j];
-    lo = (k != 0u && k < lo) ? k : lo;
-    hi = k > hi ? k : hi;
+    lo = min(lo, k - 1u);
+    hi = max(hi, k);
   }
-  kmin = wave_total<2>(lo);
+  kmin = wave_total<2>(lo) + 1u;
   kmax = wave_total<1>(hi);
 }
 
