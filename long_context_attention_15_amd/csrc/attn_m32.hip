@@ -335,9 +335,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_m32_kernel(Args a) {
   if (tid == 0) s_over = 0;
 
   // One pass over the entry list: prologue and tile loop.  It runs a second
-  // time only when some logit exceeded the reference by 2^kMaxLift (written
-  // out twice rather than as a loop, so that nothing of the prologue is
-  // kept live across the tile loop for the next round).
+  // time only when some logit exceeded the reference by 2^kMaxLift, as a
+  // second trip through the same code, so that both passes share one
+  // register assignment (two inlined copies left the accumulators to be
+  // reshuffled, partly through scratch memory, between them).
   auto pass = [&]() {
     // ---- prologue: sel entries of tiles 0 .. 7, tables of tiles 0 .. 3,
     // rows of tiles 0 .. kLead-1.  With the window first in the list, the
@@ -561,18 +562,24 @@ __global__ __launch_bounds__(kThreads, 1) void attn_m32_kernel(Args a) {
     xmax = swap32_max(xmax);
     lrun = swap32_sum(lrun);
   };
-  pass();
-  if (__ballot(mset && xmax > kMaxLift) != 0ull && lane == 0) s_over = 1;
-  __syncthreads();
-  if (s_over) {                                  // uniform: recompute with the exact maximum
+  // the recompute pass runs the same code: a second trip of this loop
+#pragma nounroll
+  for (int round = 0; round < 2; ++round) {
+    if (round == 1) {
+      if (!s_over) break;                        // uniform
 #pragma unroll
-    for (int db = 0; db < 16; ++db)
+      for (int db = 0; db < 16; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
-    lrun = 0.0f;
-    if (mset) mref += xmax;
-    xmax = -INFINITY;
+        for (int r = 0; r < 16; ++r) acc[db][r] = 0.0f;
+      lrun = 0.0f;
+      if (mset) mref += xmax;
+      xmax = -INFINITY;
+    }
     pass();
+    if (round == 0) {
+      if (__ballot(mset && xmax > kMaxLift) != 0ull && lane == 0) s_over = 1;
+      __syncthreads();
+    }
   }
   __syncthreads();
   const float mrun = mset ? mref : -INFINITY;

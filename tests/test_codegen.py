@@ -5,10 +5,10 @@ explicit vmcnt waits for LDS DMAs issued several tiles ahead.  A register
 spill inside the tile loop brings a scratch reload and a full vmcnt(0) wait
 into every tile, which drains that pipeline (a 40 % slowdown when it last
 happened, with identical results), so it is checked here rather than by the
-timing.  The tile loop of the recompute pass (run only after a logit
-overflowed the running reference) may reload one spilled value.  Row loads
-go out for every tile (past the list's end they read the zero row), so the
-loop's only own wait keeps two tiles of row loads (18) in flight.""" 
+timing.  The recompute pass (run only after a logit overflowed the running
+reference) is a second trip through the same tile loop.  Row loads go out
+for every tile (past the list's end they read the zero row), so the loop's
+only own wait keeps two tiles of row loads (18) in flight.""" 
 import os
 import re
 import shutil
@@ -24,8 +24,7 @@ SRC = os.path.join(B.CSRC, "attn_m32.hip")
 def _tile_loops(asm):
     """[(kernel, label, body lines)] of the innermost loops (backward
     branches) whose body holds at least 96 MFMA instructions, in program
-    order: per kernel instantiation, the main pass's tile loop, then the
-    recompute pass's."""
+    order (one per kernel instantiation: both passes run it)."""
     lines = asm.split("\n")
     labels, kernel_at = {}, []
     kernel = None
@@ -65,10 +64,10 @@ def test_attention_tile_loops_have_no_spills_or_full_waits(tmp_path):
     assert len(kernels) == 4, f"expected four instantiations (query post-processing x prior partial), found {kernels}"
     for kern in kernels:
         mine = [(name, body) for k, name, body in loops if k == kern]
-        assert len(mine) == 2, f"{kern}: expected the main and recompute tile loops, found {len(mine)}"
-        for n, (name, body) in enumerate(mine):
+        assert len(mine) == 1, f"{kern}: expected one tile loop (both passes run it), found {len(mine)}"
+        for name, body in mine:
             scratch = [x.strip() for x in body if "scratch_" in x]
-            limit = 0 if n == 0 else 1
+            limit = 0
             assert len(scratch) <= limit, f"{kern} {name}: scratch accesses in the tile loop: {scratch[:4]}"
             # the loop's own wait keeps two tiles of row loads (18) in flight;
             # a smaller count is the compiler waiting on something it loaded,
