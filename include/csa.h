@@ -252,13 +252,20 @@ csa_status csa_decode_rebuild(const void* tok, int tok_fmt, int B, int n, int64_
  *   key store (dim d_I), first n_entries rows valid.
  * Limits: d_I in {32, 64}; 1 <= H_I <= 16; 1 <= k <= 2048;
  *   n_entries * k <= 32768 * 32768.
+ * sel_score: float32 [B][Tq][k] or NULL.  When given, slot i receives the
+ *   score I(t, sel[b][q][i]) exactly as the selection compared it (the
+ *   float32 value behind its order key; -0 reads as +0) and padded slots
+ *   -inf, so that the (score, index) pairs of several selections (of entry
+ *   ranges held by different devices) can be merged into the same top-k.
+ *   Queries that see at most k entries are then scored too (without it they
+ *   are selected whole, unscored).  The selection itself is the same either way.
  * ws: device workspace of at least csa_indexer_topk_workspace(...) bytes
  *   (may be 0 bytes, then ws may be NULL).
  */
 size_t csa_indexer_topk_workspace(int B, int Tq, int64_t n_entries, int k);
 csa_status csa_indexer_topk(csa_store q_idx, const float* head_w, csa_store keys,
                             int64_t n_entries, const int64_t* q_pos, int B, int Tq, int H_I,
-                            int m, int k, int32_t* sel, void* ws, size_t ws_bytes,
+                            int m, int k, int32_t* sel, float* sel_score, void* ws, size_t ws_bytes,
                             hipStream_t stream);
 
 /*

@@ -71,7 +71,7 @@ _SIGS = {
     "csa_decode_append": ([_P, _I, _I, _P, _P, _I, _I, _P, _P, _CStore, _CStore, _I, _P, _P], _I),
     "csa_decode_rebuild": ([_P, _I, _I, _I, _I64, _P, _P, _P, _I, _I, _P, _P, _CStore, _CStore, _I, _P, _P], _I),
     "csa_indexer_topk_workspace": ([_I, _I, _I64, _I], _SZ),
-    "csa_indexer_topk": ([_CStore, _P, _CStore, _I64, _P, _I, _I, _I, _I, _I, _P, _P, _SZ, _P], _I),
+    "csa_indexer_topk": ([_CStore, _P, _CStore, _I64, _P, _I, _I, _I, _I, _I, _P, _P, _P, _SZ, _P], _I),
     "csa_attn_workspace": ([_I, _I, _I, _I, _I64], _SZ),
     "csa_sparse_attn_prefill": ([_P, _I, _I, _I, _I, _CStore, _I64, _P, _I, _CStore, _I, _P, _F, _P, _P, _I,
                                  _P, _P], _I),
@@ -231,11 +231,12 @@ def indexer_topk_workspace(B: int, Tq: int, n_entries: int, k: int) -> int:
 
 
 def indexer_topk(q_idx: Store, head_w, keys: Store, n_entries: int, q_pos, B: int, Tq: int, H_I: int, m: int,
-                 k: int, sel, ws=None, stream=None):
-    """csa_indexer_topk: writes sel [B][Tq][k] int32."""
+                 k: int, sel, ws=None, stream=None, sel_score=None):
+    """csa_indexer_topk: writes sel [B][Tq][k] int32 (and, if given,
+    sel_score [B][Tq][k] float32)."""
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
     _check(load().csa_indexer_topk(q_idx.c(), _ptr(head_w), keys.c(), n_entries, _ptr(q_pos), B, Tq, H_I, m, k,
-                                   _ptr(sel), _ptr(ws), wsb, _stream(stream)), "csa_indexer_topk")
+                                   _ptr(sel), _ptr(sel_score), _ptr(ws), wsb, _stream(stream)), "csa_indexer_topk")
 
 
 def attn_workspace(B: int, Tq: int, H: int, dim: int, max_list: int) -> int:

@@ -255,7 +255,7 @@ size_t csa_indexer_topk_workspace(int B, int Tq, int64_t n_entries, int k) {
 
 csa_status csa_indexer_topk(csa_store q_idx, const float* head_w, csa_store keys, int64_t n_entries,
                             const int64_t* q_pos, int B, int Tq, int H_I, int m, int k, int32_t* sel,
-                            void* ws, size_t ws_bytes, hipStream_t stream) {
+                            float* sel_score, void* ws, size_t ws_bytes, hipStream_t stream) {
   g_err[0] = 0;
   if (B < 0 || Tq < 0) return fail(CSA_EINVAL, "B and Tq must be >= 0");
   if ((int64_t)B * Tq == 0) return CSA_OK;
@@ -276,8 +276,8 @@ csa_status csa_indexer_topk(csa_store q_idx, const float* head_w, csa_store keys
   if (plan.ws > 0 && (!ws || ws_bytes < plan.ws))
     return fail(CSA_EWORKSPACE, "workspace of %zu bytes needed, %zu given", plan.ws, ws ? ws_bytes : (size_t)0);
   if (plan.ws > 0 && !aligned(ws, 16)) return fail(CSA_EINVAL, "ws must be 16-byte aligned");
-  return launched(csa::launch_indexer(q_idx, head_w, keys, n_entries, q_pos, B, Tq, H_I, m, k, sel, ws, plan,
-                                      stream),
+  return launched(csa::launch_indexer(q_idx, head_w, keys, n_entries, q_pos, B, Tq, H_I, m, k, sel, sel_score, ws,
+                                      plan, stream),
                   stream, "csa_indexer_topk launch");
 }
 

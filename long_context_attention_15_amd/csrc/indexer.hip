@@ -228,6 +228,7 @@ struct IdxArgs {
   const int64_t* q_pos;
   int B, Tq, H_I, m, k, chunk, nchunk;
   int32_t* sel;
+  float* sel_score;        // nullable: score of each selected entry, -inf in padded slots
   uint32_t* ws_key;
   int32_t* ws_idx;
   // long lists: per-query workspace block and the offsets inside it
@@ -642,11 +643,13 @@ __global__ __launch_bounds__(kIdxThreads) void idx_chunk_kernel(IdxArgs a) {
   const bool direct = a.nchunk == 1;
   int32_t* out_idx = direct ? a.sel + bq * a.k : a.ws_idx + (bq * a.nchunk + c) * a.k;
   uint32_t* out_key = direct ? nullptr : a.ws_key + (bq * a.nchunk + c) * a.k;
+  float* out_score = direct && a.sel_score ? a.sel_score + bq * a.k : nullptr;
 
   // pad the slots that will not be filled
   for (int i = kk + tid; i < a.k; i += kIdxThreads) {
     out_idx[i] = -1;
     if (!direct) out_key[i] = 0u;
+    if (out_score) out_score[i] = -INFINITY;
   }
   if (kk == 0) return;                        // uniform over the workgroup
 
@@ -659,6 +662,7 @@ __global__ __launch_bounds__(kIdxThreads) void idx_chunk_kernel(IdxArgs a) {
   emit_selected(s_keys, cn, thr, need_eq, sh, [&](int pos, int rank) {
     out_idx[rank] = (int32_t)(c0 + pos);
     if (!direct) out_key[rank] = s_keys[pos];
+    if (out_score) out_score[rank] = key_score(s_keys[pos]);
   });
 }
 
@@ -684,12 +688,19 @@ __global__ __launch_bounds__(kIdxThreads) void idx_merge_kernel(IdxArgs a) {
   const int valid = (int)s_cnt;
   const int kk = valid < a.k ? valid : a.k;
   int32_t* out = a.sel + bq * a.k;
-  for (int i = kk + tid; i < a.k; i += kIdxThreads) out[i] = -1;
+  float* out_score = a.sel_score ? a.sel_score + bq * a.k : nullptr;
+  for (int i = kk + tid; i < a.k; i += kIdxThreads) {
+    out[i] = -1;
+    if (out_score) out_score[i] = -INFINITY;
+  }
   if (kk == 0) return;
   uint32_t thr;
   int need_eq;
   radix_select(s_keys, n, kk, sh, thr, need_eq);
-  emit_selected(s_keys, n, thr, need_eq, sh, [&](int pos, int rank) { out[rank] = ci[pos]; });
+  emit_selected(s_keys, n, thr, need_eq, sh, [&](int pos, int rank) {
+    out[rank] = ci[pos];
+    if (out_score) out_score[rank] = key_score(s_keys[pos]);
+  });
 }
 
 // ------------------------------------------------- streaming top-k (prefill)
@@ -940,6 +951,7 @@ struct StreamArgs {
   const int64_t* q_pos;
   int B, Tq, H_I, m, k, ngroups;
   int32_t* sel;
+  float* sel_score;
 };
 
 // Raw key bytes of one iteration for this lane: entry (32 blk + l32) of the
@@ -1137,14 +1149,21 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
     const int q = q0 + qq;
     if (q >= a.Tq) continue;                                        // uniform
     int32_t* out = a.sel + ((int64_t)b * a.Tq + q) * a.k;
+    float* out_score = a.sel_score ? a.sel_score + ((int64_t)b * a.Tq + q) * a.k : nullptr;
     const int n = cnt[qq];
     const int kk = n < a.k ? n : a.k;
-    for (int i = kk + lane; i < a.k; i += kWave) out[i] = -1;
+    for (int i = kk + lane; i < a.k; i += kWave) {
+      out[i] = -1;
+      if (out_score) out_score[i] = -INFINITY;
+    }
     if (kk == 0) continue;
     const uint32_t* keys = ck + qq * kSRowCap;
     const uint16_t* ids = ci + qq * kSRowCap;
     if (n <= a.k) {
-      for (int i = lane; i < n; i += kWave) out[i] = (int32_t)ids[i];
+      for (int i = lane; i < n; i += kWave) {
+        out[i] = (int32_t)ids[i];
+        if (out_score) out_score[i] = key_score(keys[i]);
+      }
       continue;
     }
     RegList<NS> r;
@@ -1160,7 +1179,10 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
       const uint64_t beq = __ballot(eq);
       const bool take = (k != 0u && k > T) || (eq && eqs + __popcll(beq & lt) < need_eq);
       const uint64_t bt = __ballot(take);
-      if (take) out[outn + __popcll(bt & lt)] = (int32_t)r.id[j];
+      if (take) {
+        out[outn + __popcll(bt & lt)] = (int32_t)r.id[j];
+        if (out_score) out_score[outn + __popcll(bt & lt)] = key_score(k);
+      }
       outn += __popcll(bt);
       eqs += __popcll(beq);
     }
@@ -1175,7 +1197,7 @@ bool indexer_stream_ok(const csa_store& keys, int H_I, int B, int Tq, int64_t n_
 static hipError_t launch_idx_stream(const IdxArgs& ia, hipStream_t st) {
   StreamArgs a;
   a.qidx = ia.qidx; a.keys = ia.keys; a.head_w = ia.head_w; a.n_entries = ia.n_entries; a.q_pos = ia.q_pos;
-  a.B = ia.B; a.Tq = ia.Tq; a.H_I = ia.H_I; a.m = ia.m; a.k = ia.k; a.sel = ia.sel;
+  a.B = ia.B; a.Tq = ia.Tq; a.H_I = ia.H_I; a.m = ia.m; a.k = ia.k; a.sel = ia.sel; a.sel_score = ia.sel_score;
   a.ngroups = (ia.Tq + kSQW - 1) / kSQW;
   const dim3 grid((unsigned)((int64_t)a.B * a.ngroups));
   if (a.k <= stream_max_k<kSCapSmall>()) hipLaunchKernelGGL(idx_stream_kernel<kSCapSmall>, grid, dim3(kWave), 0, st, a);
@@ -1273,7 +1295,8 @@ __global__ __launch_bounds__(kIdxThreads) void idx_long_compact_kernel(IdxArgs a
   uint2* region = (uint2*)(wq + a.off_region);
   const int64_t s0 = (int64_t)seg * kLSeg;
   const int64_t s1 = nt < s0 + kLSeg ? nt : s0 + kLSeg;
-  if (s1 <= s0 || nt <= a.k) {                  // uniform; short lists need no candidates
+  // uniform; short lists need no candidates unless their scores are asked for
+  if (s1 <= s0 || (nt <= a.k && !a.sel_score)) {
     if (tid == 0) counts[seg] = 0u;
     return;
   }
@@ -1366,7 +1389,7 @@ __global__ __launch_bounds__(kIdxThreads) void idx_long_fused_kernel(IdxArgs a) 
   const int64_t bq = blockIdx.y;
   const int b = (int)(bq / a.Tq), q = (int)(bq % a.Tq);
   const int64_t nt = idx_visible(a, bq);
-  if (nt <= a.k) return;                        // uniform per query: no candidates needed
+  if (nt <= a.k && !a.sel_score) return;        // uniform per query: no candidates needed
   const int64_t c0 = (int64_t)c * a.chunk;
   const int64_t cn64 = nt - c0;
   const int cn = cn64 < 0 ? 0 : (cn64 > a.chunk ? a.chunk : (int)cn64);
@@ -1493,7 +1516,8 @@ __global__ __launch_bounds__(kIdxThreads) void idx_long_final_kernel(IdxArgs a) 
   const uint32_t cnt_ld = tid < a.nseg ? counts[tid] : 0u;
   const int64_t nt = idx_visible(a, bq);
   int32_t* out = a.sel + bq * a.k;
-  if (nt <= a.k) {
+  float* out_score = a.sel_score ? a.sel_score + bq * a.k : nullptr;
+  if (nt <= a.k && !out_score) {                // every visible entry, unscored
     for (int i = tid; i < a.k; i += kIdxThreads) out[i] = i < nt ? i : -1;
     return;
   }
@@ -1512,7 +1536,10 @@ __global__ __launch_bounds__(kIdxThreads) void idx_long_final_kernel(IdxArgs a) 
   __syncthreads();
   const int ncand = (int)s_pre[kIdxThreads];
   const int kk = ncand < a.k ? ncand : a.k;
-  for (int i = kk + tid; i < a.k; i += kIdxThreads) out[i] = -1;
+  for (int i = kk + tid; i < a.k; i += kIdxThreads) {
+    out[i] = -1;
+    if (out_score) out_score[i] = -INFINITY;
+  }
   if (kk == 0) return;
   uint32_t thr;
   int need_eq;
@@ -1530,7 +1557,10 @@ __global__ __launch_bounds__(kIdxThreads) void idx_long_final_kernel(IdxArgs a) 
     }
     __syncthreads();
     radix_select(s_cand, ncand, kk, sh, thr, need_eq);
-    emit_selected(s_cand, ncand, thr, need_eq, sh, [&](int pos, int rank) { out[rank] = s_cidx[pos]; });
+    emit_selected(s_cand, ncand, thr, need_eq, sh, [&](int pos, int rank) {
+      out[rank] = s_cidx[pos];
+      if (out_score) out_score[rank] = key_score(s_cand[pos]);
+    });
     return;
   }
   // many candidates (heavy ties, or chunks that stopped waiting): concatenated in the workspace
@@ -1548,7 +1578,10 @@ __global__ __launch_bounds__(kIdxThreads) void idx_long_final_kernel(IdxArgs a) 
   }
   __syncthreads();
   radix_select(skey, ncand, kk, sh, thr, need_eq);
-  emit_selected(skey, ncand, thr, need_eq, sh, [&](int pos, int rank) { out[rank] = sidx[pos]; });
+  emit_selected(skey, ncand, thr, need_eq, sh, [&](int pos, int rank) {
+    out[rank] = sidx[pos];
+    if (out_score) out_score[rank] = key_score(skey[pos]);
+  });
 }
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -1667,7 +1700,7 @@ static hipError_t launch_idx_t(const IdxArgs& a, hipStream_t st) {
 
 hipError_t launch_indexer(const csa_store& qidx, const float* head_w, const csa_store& keys,
                           int64_t n_entries, const int64_t* q_pos, int B, int Tq, int H_I, int m,
-                          int k, int32_t* sel, void* ws, const IdxPlan& plan, hipStream_t st) {
+                          int k, int32_t* sel, float* sel_score, void* ws, const IdxPlan& plan, hipStream_t st) {
   IdxArgs a;
   a.qidx = view(qidx);
   a.keys = view(keys);
@@ -1683,6 +1716,7 @@ hipError_t launch_indexer(const csa_store& qidx, const float* head_w, const csa_
   a.rstride = plan.rstride;
   a.spin_max = indexer_spin_limit();
   a.sel = sel;
+  a.sel_score = sel_score;
   const size_t half = plan.ws / 2;
   a.ws_key = (uint32_t*)ws;
   a.ws_idx = (int32_t*)((uint8_t*)ws + half);

@@ -42,7 +42,7 @@ bool indexer_stream_ok(const csa_store& keys, int H_I, int B, int Tq, int64_t n_
 hipError_t diag_counters(uint64_t* out, int n, bool reset);
 hipError_t launch_indexer(const csa_store& qidx, const float* head_w, const csa_store& keys,
                           int64_t n_entries, const int64_t* q_pos, int B, int Tq, int H_I, int m,
-                          int k, int32_t* sel, void* ws, const IdxPlan& plan, hipStream_t st);
+                          int k, int32_t* sel, float* sel_score, void* ws, const IdxPlan& plan, hipStream_t st);
 
 // Attention: one launcher for every attention entry point.
 struct AttnCall {

@@ -64,9 +64,9 @@ def test_empty_calls_need_no_pointers(lib):
     assert lib.csa_decode_rebuild(None, csa.F32, 2, 0, 0, None, None, None, 0, 4, None, None, z, z, 0, None, None) == 0
     assert lib.csa_decode_rebuild(None, csa.F32, 2, -1, 0, None, None, None, 0, 4, None, None, z, z, 0, None,
                                   None) == 1
-    assert lib.csa_indexer_topk(z, None, z, 0, None, 0, 1, 8, 4, 64, None, None, 0, None) == 0
-    assert lib.csa_indexer_topk(z, None, z, 0, None, 2, 0, 8, 4, 64, None, None, 0, None) == 0
-    assert lib.csa_indexer_topk(z, None, z, 0, None, 2, -1, 8, 4, 64, None, None, 0, None) == 1
+    assert lib.csa_indexer_topk(z, None, z, 0, None, 0, 1, 8, 4, 64, None, None, None, 0, None) == 0
+    assert lib.csa_indexer_topk(z, None, z, 0, None, 2, 0, 8, 4, 64, None, None, None, 0, None) == 0
+    assert lib.csa_indexer_topk(z, None, z, 0, None, 2, -1, 8, 4, 64, None, None, None, 0, None) == 1
     assert lib.csa_sparse_attn_prefill(None, csa.BF16, 1, 0, 64, z, 0, None, 64, z, 128, None, 0.04, None, None, 0,
                                        None, None) == 0
     assert lib.csa_sparse_attn_prefill(None, csa.BF16, 0, 9, 64, z, 0, None, 64, z, 128, None, 0.04, None, None, 0,
@@ -152,7 +152,7 @@ def test_indexer_rejects_bad_arguments(lib):
     ok = dict(n=1000, B=1, Tq=8, H=8, m=4, k=64)
     call = lambda **kw: lib.csa_indexer_topk(kw.get("q", q), P, kw.get("keys", k), kw.get("n", 1000), 0,
                                              kw.get("B", 1), kw.get("Tq", 8), kw.get("H", 8), kw.get("m", 4),
-                                             kw.get("k", 64), P, 0, 0, None)
+                                             kw.get("k", 64), P, None, 0, 0, None)
     assert call(k=0) == 2 and call(k=4096) == 2
     assert call(H=17) == 2
     assert call(n=1001) == 1                       # beyond keys.cap
@@ -163,7 +163,7 @@ def test_indexer_rejects_bad_arguments(lib):
     big = _store(P, 1 << 18, 64, 0, csa.FP8_E4M3, P)
     need = lib.csa_indexer_topk_workspace(4, 1, 1 << 18, 1024)
     assert need > 0
-    assert lib.csa_indexer_topk(q, P, big, 1 << 18, P, 4, 1, 8, 4, 1024, P, 0, 0, None) == 3
+    assert lib.csa_indexer_topk(q, P, big, 1 << 18, P, 4, 1, 8, 4, 1024, P, None, 0, 0, None) == 3
     assert "workspace" in lib.csa_last_error().decode()
 
 
