@@ -127,3 +127,48 @@ def test_sel_score_three_kernel_long_lists(lib):
     kst, kdeq, qst, qdeq, w = _inputs(B, 1, N, H_I, d_I, "fp8", 9)
     pos = [[m * N - 2], [m * 700]]
     _check(lib, qst, w, kst, kdeq, qdeq, N, pos, B, 1, H_I, m, k)
+
+
+def _merge_pairs(parts, k):
+    """Host merge of (score, global index) lists: the k largest scores, ties
+    to the smaller index, returned in ascending index order (the order of the
+    entry point's output)."""
+    sc = np.concatenate([p[0] for p in parts])
+    ix = np.concatenate([p[1] for p in parts])
+    keep = ix >= 0
+    sc, ix = sc[keep], ix[keep]
+    order = np.lexsort((ix, -sc.astype(np.float64)))[:k]
+    return np.sort(ix[order])
+
+
+@pytest.mark.parametrize("N,k,split", [(50000, 1024, 23456), (3000, 512, 1000)])
+def test_range_selections_merge_to_the_whole_selection(lib, N, k, split):
+    """The entry range [0, N) split in two, as two devices holding halves of
+    one sequence's compressed keys would hold it: each range is selected on
+    its own (positions shifted so that a range sees the query's visible
+    entries inside it), and merging the two (score, index) lists gives the
+    selection of one call over the whole range, exactly (integer inputs make
+    every score exact, with many ties)."""
+    B, H_I, d_I, m = 1, 8, 64, 4
+    rng = np.random.default_rng(43 + N)
+    keys = rng.integers(-2, 3, (B, N, d_I)).astype(np.float64)
+    keys[:, :, 0] = 2.0
+    q = rng.integers(-1, 2, (B, H_I, d_I)).astype(np.float64)
+    q[:, :, 1] = 1.0
+    w = np.ones((B, 1, H_I), np.float32)
+    qst, _ = Hx.upload_store(q, "fp8")
+    for t in (m * N + 1, m * (split + 700) + 2):              # sees all N; sees 700 entries of the second range
+        whole, _ = Hx.upload_store(keys, "fp8")
+        sel, _ = _select(lib, qst, w, whole, N, [[t]], B, 1, H_I, m, k, False)
+        nt = int(O.n_visible(t, m, N))
+        parts = []
+        for r0, r1 in ((0, split), (split, N)):
+            part, _ = Hx.upload_store(keys[:, r0:r1], "fp8")
+            seen = max(0, min(nt, r1) - r0)
+            tp = m * seen - 1                                    # a position that sees exactly `seen` entries
+            s_r, sc_r = _select(lib, qst, w, part, r1 - r0, [[tp]], B, 1, H_I, m, k, True)
+            idx = s_r[0, 0].astype(np.int64)
+            parts.append((sc_r[0, 0], np.where(idx >= 0, idx + r0, -1)))
+        merged = _merge_pairs(parts, k)
+        want = sel[0, 0][sel[0, 0] >= 0]
+        assert np.array_equal(merged, want), t
