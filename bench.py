@@ -488,8 +488,8 @@ def main():
                     help="only run a plain 1 GiB device copy (the reference for scaling HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the path is built and timed on a single MI355X; "
-              "multi-GPU runs are not part of this build.", file=sys.stderr)
+        print("bench.py measures one GPU: the path runs and is timed on a single MI355X; "
+              "runs over several GPUs are not supported (--gpus 1 only).", file=sys.stderr)
         sys.exit(2)
     import torch
     if args.copy_calibration:
